@@ -1,0 +1,281 @@
+"""CPU oracle for the UFP4 quantization hot path -- TEST INFRASTRUCTURE.
+
+A plain, slow, single-threaded C implementation (``ufp4_oracle.c``) wrapped
+with ctypes and numpy.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the product path
+(``fp4_quantization_amd``) never does, and shares no code with it.
+
+Functions mirror the C-ABI semantics on host arrays.  See ``ufp4_oracle.h``
+for the definitions and the sources they follow.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libufp4_oracle.so")
+SOURCES = [os.path.join(_HERE, "ufp4_oracle.c")]
+
+GRID_E1M2, GRID_INT4, GRID_E2M1 = 0, 1, 2
+ROUND_RTNE, ROUND_SR = 0, 1
+SCALE_NV16, SCALE_MX32 = 0, 1
+LAYOUT_ROW, LAYOUT_COL = 0, 1
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc: binary32, round-to-nearest, no FMA contraction."""
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-Wall", "-Wextra", "-o", LIB_PATH + ".tmp"] + SOURCES + ["-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int32), ("rounding", ctypes.c_int32),
+                ("scaling", ctypes.c_int32), ("rht", ctypes.c_int32),
+                ("rht_seed", ctypes.c_uint64), ("sr_seed", ctypes.c_uint64)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("sqnr_db", ctypes.c_double), ("mean_signed_err", ctypes.c_double),
+                ("mean_signed_err_grid", ctypes.c_double), ("alpha", ctypes.c_double),
+                ("amax", ctypes.c_double), ("n", ctypes.c_uint64),
+                ("code_hist", ctypes.c_uint64 * 16), ("n_saturated", ctypes.c_uint64),
+                ("n_nonfinite", ctypes.c_uint64), ("n_zero_scale", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        d = {k: getattr(self, k) for k, _ in self._fields_ if k != "code_hist"}
+        d["code_hist"] = list(self.code_hist)
+        return d
+
+
+_lib = None
+
+
+def lib():
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i64, i32, u64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64
+        L.orc_bf16_to_f32.restype = ctypes.c_float
+        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_philox4x32_10.argtypes = [P, P, P]
+        L.orc_rht_signs.argtypes = [u64, P]
+        L.orc_sr_word.restype = ctypes.c_uint32
+        L.orc_sr_word.argtypes = [u64, u64, ctypes.c_uint32]
+        L.orc_fwht16_stages.argtypes = [P]
+        L.orc_rht16.argtypes = [P, P, P]
+        L.orc_inverse_rht16.argtypes = [P, P, P]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_e4m3_encode_n.argtypes = [P, i64, P]
+        L.orc_e4m3_decode.restype = ctypes.c_float
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_grid_qmax.restype = ctypes.c_float
+        L.orc_grid_qmax.argtypes = [i32]
+        L.orc_code_value.restype = ctypes.c_float
+        L.orc_code_value.argtypes = [ctypes.c_uint8, i32]
+        L.orc_round_to_code.restype = ctypes.c_uint8
+        L.orc_round_to_code.argtypes = [ctypes.c_float, i32, i32, ctypes.c_uint32]
+        L.orc_round_f32.restype = ctypes.c_int
+        L.orc_round_f32.argtypes = [P, i64, i32, i32, u64, P]
+        L.orc_quantize.restype = ctypes.c_int
+        L.orc_quantize.argtypes = [P, i64, i64, i64, ctypes.POINTER(Config), i32, P, P, P]
+        L.orc_grouped_col_offsets.restype = ctypes.c_int
+        L.orc_grouped_col_offsets.argtypes = [P, i32, i32, P]
+        L.orc_quantize_grouped.restype = ctypes.c_int
+        L.orc_quantize_grouped.argtypes = [P, i64, i64, P, i32, ctypes.POINTER(Config),
+                                           P, P, P, P, P, P]
+        L.orc_dequantize.restype = ctypes.c_int
+        L.orc_dequantize.argtypes = [P, P, P, i64, i64, ctypes.POINTER(Config), i32, P]
+        L.orc_compute_stats.restype = ctypes.c_int
+        L.orc_compute_stats.argtypes = [P, i64, i64, i64, i32, ctypes.POINTER(Config),
+                                        P, P, P, ctypes.POINTER(Stats)]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def config(grid=GRID_E1M2, rounding=ROUND_RTNE, scaling=SCALE_NV16, rht=1,
+           rht_seed=0, sr_seed=0) -> Config:
+    return Config(int(grid), int(rounding), int(scaling), int(rht), int(rht_seed), int(sr_seed))
+
+
+def block_len(scaling: int) -> int:
+    return 32 if scaling == SCALE_MX32 else 16
+
+
+# ---------------------------------------------------------------- primitives
+def bf16_to_f32(h: int) -> float:
+    return lib().orc_bf16_to_f32(h)
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def rht_signs(seed: int) -> np.ndarray:
+    s = np.zeros(16, dtype=np.int8)
+    lib().orc_rht_signs(int(seed), _ptr(s))
+    return s
+
+
+def sr_word(seed: int, index: int, stream: int) -> int:
+    return int(lib().orc_sr_word(int(seed), int(index), int(stream)))
+
+
+def fwht16_stages(v) -> np.ndarray:
+    a = np.array(v, dtype=np.float32).copy()
+    lib().orc_fwht16_stages(_ptr(a))
+    return a
+
+
+def rht16(x, signs) -> np.ndarray:
+    xa = np.ascontiguousarray(x, dtype=np.float32)
+    s = np.ascontiguousarray(signs, dtype=np.int8)
+    v = np.zeros(16, dtype=np.float32)
+    lib().orc_rht16(_ptr(xa), _ptr(s), _ptr(v))
+    return v
+
+
+def inverse_rht16(v, signs) -> np.ndarray:
+    va = np.ascontiguousarray(v, dtype=np.float32)
+    s = np.ascontiguousarray(signs, dtype=np.int8)
+    x = np.zeros(16, dtype=np.float32)
+    lib().orc_inverse_rht16(_ptr(va), _ptr(s), _ptr(x))
+    return x
+
+
+def e4m3_encode(q: float) -> int:
+    return int(lib().orc_e4m3_encode(float(q)))
+
+
+def e4m3_encode_n(q: np.ndarray) -> np.ndarray:
+    qa = np.ascontiguousarray(q, dtype=np.float32)
+    out = np.zeros(qa.size, dtype=np.uint8)
+    lib().orc_e4m3_encode_n(_ptr(qa), qa.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(c: int) -> float:
+    return float(lib().orc_e4m3_decode(int(c)))
+
+
+def grid_qmax(grid: int) -> float:
+    return float(lib().orc_grid_qmax(int(grid)))
+
+
+def code_value(code: int, grid: int) -> float:
+    return float(lib().orc_code_value(int(code), int(grid)))
+
+
+def round_f32(y: np.ndarray, grid: int, rounding: int = ROUND_RTNE, sr_seed: int = 0) -> np.ndarray:
+    ya = np.ascontiguousarray(y, dtype=np.float32)
+    codes = np.zeros(ya.size, dtype=np.uint8)
+    rc = lib().orc_round_f32(_ptr(ya), ya.size, int(grid), int(rounding), int(sr_seed), _ptr(codes))
+    if rc:
+        raise ValueError(f"orc_round_f32 failed ({rc})")
+    return codes
+
+
+# -------------------------------------------------------------- whole tensors
+def out_shapes(rows: int, cols: int, layout: int, scaling: int):
+    B = block_len(scaling)
+    if layout == LAYOUT_ROW:
+        return (rows, cols // 2), (rows, cols // B)
+    return (cols, rows // 2), (cols, rows // B)
+
+
+def quantize(x_bf16: np.ndarray, cfg: Config, layout: int):
+    """x_bf16: uint16 array [rows][ld>=cols] (bf16 bit patterns).
+    Returns (codes, scales, tensor_scale) for the layout."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    cshape, sshape = out_shapes(rows, cols, layout, cfg.scaling)
+    codes = np.zeros(cshape, dtype=np.uint8)
+    scales = np.zeros(sshape, dtype=np.uint8)
+    ts = np.zeros(1, dtype=np.float32)
+    rc = lib().orc_quantize(_ptr(x), rows, cols, cols, ctypes.byref(cfg), int(layout),
+                            _ptr(codes), _ptr(scales), _ptr(ts))
+    if rc:
+        raise ValueError(f"orc_quantize failed ({rc})")
+    return codes, scales, ts
+
+
+def grouped_col_offsets(offsets, block: int) -> np.ndarray:
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    E = off.size - 1
+    col = np.zeros(E + 1, dtype=np.int64)
+    rc = lib().orc_grouped_col_offsets(_ptr(off), E, int(block), _ptr(col))
+    if rc:
+        raise ValueError("bad offsets")
+    return col
+
+
+def quantize_grouped(x_bf16: np.ndarray, offsets, cfg: Config, row=True, col=True):
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    R, C = x.shape
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    E = off.size - 1
+    B = block_len(cfg.scaling)
+    coff = grouped_col_offsets(off, B)
+    R_pad = int(coff[-1])
+    rc_ = np.zeros((R, C // 2), np.uint8) if row else None
+    rs_ = np.zeros((R, C // B), np.uint8) if row else None
+    rts = np.zeros(E, np.float32)
+    cc_ = np.zeros((C, R_pad // 2), np.uint8) if col else None
+    cs_ = np.zeros((C, R_pad // B), np.uint8) if col else None
+    cts = np.zeros(E, np.float32)
+    nul = ctypes.c_void_p(0)
+    rc = lib().orc_quantize_grouped(
+        _ptr(x), R, C, _ptr(off), E, ctypes.byref(cfg),
+        _ptr(rc_) if row else nul, _ptr(rs_) if row else nul, _ptr(rts),
+        _ptr(cc_) if col else nul, _ptr(cs_) if col else nul, _ptr(cts))
+    if rc:
+        raise ValueError(f"orc_quantize_grouped failed ({rc})")
+    return (rc_, rs_, rts), (cc_, cs_, cts), coff
+
+
+def dequantize(codes, scales, tensor_scale, rows: int, cols: int, cfg: Config,
+               inverse_rht: bool = False) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint8)
+    t = np.ascontiguousarray(np.atleast_1d(tensor_scale), dtype=np.float32)
+    out = np.zeros((rows, cols), dtype=np.float32)
+    rc = lib().orc_dequantize(_ptr(c), _ptr(s), _ptr(t), rows, cols, ctypes.byref(cfg),
+                              int(bool(inverse_rht)), _ptr(out))
+    if rc:
+        raise ValueError(f"orc_dequantize failed ({rc})")
+    return out
+
+
+def stats(x_bf16, layout: int, cfg: Config, codes, scales, tensor_scale) -> dict:
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint8)
+    t = np.ascontiguousarray(np.atleast_1d(tensor_scale), dtype=np.float32)
+    st = Stats()
+    rc = lib().orc_compute_stats(_ptr(x), rows, cols, cols, int(layout), ctypes.byref(cfg),
+                                 _ptr(c), _ptr(s), _ptr(t), ctypes.byref(st))
+    if rc:
+        raise ValueError(f"orc_compute_stats failed ({rc})")
+    return st.as_dict()

@@ -1,0 +1,301 @@
+"""Pins of the oracle's whole-tensor drivers: scales, layouts, grouped segments,
+dequantization and statistics.  Expected values come from closed forms,
+brute-force searches or independent numpy computations, never from the
+oracle's own code path."""
+import numpy as np
+import pytest
+
+import synth
+
+E1M2, INT4, E2M1 = 0, 1, 2
+RTNE, SR = 0, 1
+NV16, MX32 = 0, 1
+ROW, COL = 0, 1
+
+
+def sylvester16():
+    i = np.arange(16)
+    pc = np.array([[bin(a & b).count("1") for b in i] for a in i])
+    return np.where(pc % 2 == 0, 1, -1)
+
+
+def unpack(codes):
+    c = np.asarray(codes, np.uint8)
+    out = np.empty(c.shape[:-1] + (c.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = c & 15
+    out[..., 1::2] = c >> 4
+    return out
+
+
+def value_table(orc, grid):
+    return np.array([orc.code_value(c, grid) for c in range(16)])
+
+
+# ------------------------------------------------------------------ scales
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+def test_one_hot_blocks_pin_signs_and_scales(orc, grid):
+    # x = c e_j in every block, same |c|: every |v| = |c|/4, so every block
+    # scale saturates at 448 and every code is +-Qmax with the sign pattern
+    # sign(c) d_j H[:, j].
+    H = sylvester16()
+    rows, cols = 16, 256
+    x = np.zeros((rows, cols), np.float32)
+    rng = np.random.default_rng(0)
+    js = rng.integers(0, 16, size=(rows, cols // 16))
+    cs = rng.choice([-2.0, 2.0], size=(rows, cols // 16))
+    for r in range(rows):
+        for b in range(cols // 16):
+            x[r, 16 * b + js[r, b]] = cs[r, b]
+    xb = synth.f32_to_bf16(x)
+    cfg = orc.config(grid=grid, rht=1, rht_seed=5)
+    codes, scales, ts = orc.quantize(xb, cfg, ROW)
+    assert np.all(scales == 0x7E)
+    s = orc.rht_signs(5)
+    vals = value_table(orc, grid)[unpack(codes)]
+    qmax = orc.grid_qmax(grid)
+    for r in range(rows):
+        for b in range(cols // 16):
+            want = np.sign(cs[r, b]) * s[js[r, b]] * H[:, js[r, b]] * qmax
+            np.testing.assert_array_equal(vals[r, 16 * b:16 * b + 16], want)
+
+
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+def test_grid_valued_inputs_reproduce_codes(orc, grid):
+    # RHT off; every block holds grid values times 2^k with its maximum at
+    # +-Qmax 2^k, so the scales are exact and the codes come back unchanged.
+    rng = np.random.default_rng(1)
+    mags = value_table(orc, grid)
+    rows, cols = 32, 128
+    codes_in = rng.integers(0, 16, size=(rows, cols)).astype(np.uint8)
+    if grid != INT4:
+        codes_in[codes_in == 8] = 0
+    else:
+        codes_in[codes_in == 8] = 9
+    codes_in[:, ::16] = 7  # +Qmax in each block
+    x = (mags[codes_in] * 4.0).astype(np.float32)
+    xb = synth.f32_to_bf16(x)
+    assert np.array_equal(synth.bf16_to_f32(xb), x)
+    codes, scales, ts = orc.quantize(xb, orc.config(grid=grid, rht=0), ROW)
+    np.testing.assert_array_equal(unpack(codes), codes_in)
+    deq = orc.dequantize(codes, scales, ts, rows, cols, orc.config(grid=grid, rht=0))
+    np.testing.assert_allclose(deq, x, rtol=2e-7)
+
+
+def test_zero_tensor(orc):
+    xb = np.zeros((32, 64), np.uint16)
+    for scaling in (NV16, MX32):
+        for layout in (ROW, COL):
+            codes, scales, ts = orc.quantize(xb, orc.config(scaling=scaling), layout)
+            assert ts[0] == 1.0 and np.all(codes == 0)
+            assert np.all(scales == (0 if scaling == NV16 else 0))
+
+
+def test_mx32_scale_is_power_of_two_of_block_max(orc):
+    rng = np.random.default_rng(2)
+    x = synth.f32_to_bf16(rng.standard_normal((8, 128)).astype(np.float32) * 3)
+    for grid, emax in ((E1M2, 1), (INT4, 2), (E2M1, 2)):
+        cfg = orc.config(grid=grid, scaling=MX32, rht=0)
+        codes, scales, ts = orc.quantize(x, cfg, ROW)
+        xf = synth.bf16_to_f32(x).reshape(8, 4, 32).astype(np.float64)
+        amax = np.abs(xf).max(axis=2)
+        want = np.floor(np.log2(amax)).astype(int) - emax + 127
+        np.testing.assert_array_equal(scales, want)
+        assert ts[0] == 1.0
+
+
+def test_nv16_scale_matches_definition_numpy(orc):
+    # Independent numpy evaluation of the two-level scale for RHT off:
+    # S_t = amax_t/(Qmax 448); s_b = E4M3(amax_b / fl(Qmax S_t)), evaluated
+    # with numpy float32 ops and a brute-force E4M3 nearest search.
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    xb = synth.activation(64, 256, 7)
+    xf = synth.bf16_to_f32(xb)
+    for grid, qmax in ((E1M2, 3.5), (INT4, 7.0), (E2M1, 6.0)):
+        codes, scales, ts = orc.quantize(xb, orc.config(grid=grid, rht=0), ROW)
+        amax_b = np.abs(xf.reshape(64, 16, 16)).max(axis=2)
+        amax_t = amax_b.max()
+        S_t = np.float32(amax_t) / np.float32(qmax * 448)
+        assert ts[0] == S_t
+        D = np.float32(qmax) * S_t
+        q = (amax_b.astype(np.float32) / D).astype(np.float32)
+        ref = torch.from_numpy(np.minimum(q, np.float32(448)).copy()).to(torch.float8_e4m3fn)
+        np.testing.assert_array_equal(scales, ref.view(torch.uint8).numpy())
+    del rng
+
+
+# ---------------------------------------------------------------- layouts
+@pytest.mark.parametrize("scaling", [NV16, MX32])
+@pytest.mark.parametrize("grid", [E1M2, E2M1])
+def test_column_layout_is_row_layout_of_transpose(orc, scaling, grid):
+    xb = synth.activation(96, 64, 4)
+    cfg = orc.config(grid=grid, scaling=scaling, rht=1, rht_seed=2)
+    c1, s1, t1 = orc.quantize(xb, cfg, COL)
+    c2, s2, t2 = orc.quantize(np.ascontiguousarray(xb.T), cfg, ROW)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s1, s2)
+    assert t1[0] == t2[0]
+
+
+def test_sr_streams_differ_between_layouts(orc):
+    xb = synth.output_grad(64, 64, 3)
+    cfg = orc.config(rounding=SR, sr_seed=3)
+    ccol, _, _ = orc.quantize(xb, cfg, COL)
+    crow, _, _ = orc.quantize(np.ascontiguousarray(xb.T), cfg, ROW)
+    assert not np.array_equal(ccol, crow)  # same values, different random streams
+
+
+def test_sr_index_mapping_row(orc):
+    # row output element (r, c) uses SR word index r*C + c of stream 0: check a
+    # single element against round_f32 of its scaled value at that index.
+    xb = synth.output_grad(32, 64, 5)
+    cfg = orc.config(rounding=SR, sr_seed=11, rht=0, scaling=MX32)
+    codes, scales, ts = orc.quantize(xb, cfg, ROW)
+    xf = synth.bf16_to_f32(xb)
+    u = unpack(codes)
+    for r, c in [(0, 0), (3, 17), (31, 63), (10, 33)]:
+        X = int(scales[r, c // 32]) - 127
+        y = np.float32(xf[r, c] * np.float32(2.0 ** -X))
+        seq = np.zeros(r * 64 + c + 1, np.float32)
+        seq[-1] = y
+        want = orc.round_f32(seq, E1M2, SR, sr_seed=11)[-1]
+        assert u[r, c] == want
+
+
+# ---------------------------------------------------------------- grouped
+def test_grouped_matches_dense_per_segment(orc):
+    rng = np.random.default_rng(8)
+    counts = np.array([0, 5, 16, 37, 1, 64, 0, 23])
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    R, C = int(offsets[-1]), 64
+    xb = synth.activation(R, C, 9)
+    for scaling in (NV16, MX32):
+        B = 16 if scaling == NV16 else 32
+        cfg = orc.config(rht=1, rht_seed=1, scaling=scaling)
+        (rc, rs, rts), (cc, cs, cts), coff = orc.quantize_grouped(xb, offsets, cfg)
+        want_off = np.concatenate([[0], np.cumsum((counts + B - 1) // B * B)])
+        np.testing.assert_array_equal(coff, want_off)
+        for e, m in enumerate(counts):
+            r0 = offsets[e]
+            if m == 0:
+                assert rts[e] == 1.0 and cts[e] == 1.0
+                continue
+            seg = xb[r0:r0 + m]
+            c_, s_, t_ = orc.quantize(seg, cfg, ROW)
+            np.testing.assert_array_equal(rc[r0:r0 + m], c_)
+            np.testing.assert_array_equal(rs[r0:r0 + m], s_)
+            assert rts[e] == t_[0]
+            P = int(want_off[e + 1] - want_off[e])
+            padded = np.zeros((P, C), np.uint16)
+            padded[:m] = seg
+            c_, s_, t_ = orc.quantize(padded, cfg, COL)
+            np.testing.assert_array_equal(cc[:, want_off[e] // 2:(want_off[e] + P) // 2], c_)
+            np.testing.assert_array_equal(cs[:, want_off[e] // B:(want_off[e] + P) // B], s_)
+            assert cts[e] == t_[0]
+    del rng
+
+
+# ----------------------------------------------------------- dequantize
+def test_dequantize_inverse_rht_preserves_error_norm(orc):
+    xb = synth.activation(64, 128, 12)
+    xf = synth.bf16_to_f32(xb).astype(np.float64)
+    cfg = orc.config(rht=1, rht_seed=4)
+    codes, scales, ts = orc.quantize(xb, cfg, ROW)
+    q_rht = orc.dequantize(codes, scales, ts, 64, 128, cfg, inverse_rht=False).astype(np.float64)
+    q_orig = orc.dequantize(codes, scales, ts, 64, 128, cfg, inverse_rht=True).astype(np.float64)
+    # error in the original domain equals error in the transformed domain
+    H = sylvester16() / 4.0
+    s = orc.rht_signs(4)
+    v = (xf.reshape(-1, 16) * s) @ H.T
+    e_rht = np.linalg.norm(v - q_rht.reshape(-1, 16))
+    e_orig = np.linalg.norm(xf - q_orig)
+    assert abs(e_rht - e_orig) <= 1e-5 * np.linalg.norm(xf)
+
+
+# ------------------------------------------------------------------ stats
+def test_stats_match_numpy_on_exact_scale_case(orc):
+    # RHT off, MX32 with every block max in [2, 4): X = 0, d_b = 1, so y = x
+    # and the dequantized value is the brute-force nearest E1M2/E2M1 value.
+    rng = np.random.default_rng(13)
+    rows, cols = 64, 256
+    for grid, mags in ((E1M2, np.arange(8) * 0.5), (E2M1, np.array([0, .5, 1, 1.5, 2, 3, 4, 6]))):
+        # block maxima in [2^emax, 2^(emax+1)) so the E8M0 exponent is 0
+        x = rng.uniform(-mags[-1], mags[-1], size=(rows, cols)).astype(np.float32)
+        x[:, ::32] = 3.0 if grid == E1M2 else 5.0
+        xb = synth.f32_to_bf16(x)
+        xf = synth.bf16_to_f32(xb).astype(np.float64)
+        cfg = orc.config(grid=grid, scaling=MX32, rht=0)
+        codes, scales, ts = orc.quantize(xb, cfg, ROW)
+        assert np.all(scales == 127)
+        a = np.abs(xf)
+        d = np.abs(a[..., None] - mags)
+        best = d.min(axis=-1, keepdims=True)
+        idx = np.arange(8)
+        tie_even = np.where((d == best) & (idx % 2 == 0), idx, 99).min(axis=-1)
+        k = np.where(tie_even < 99, tie_even, d.argmin(axis=-1))  # ties go to the even index
+        xh = np.sign(xf) * mags[k]
+        st = orc.stats(xb, ROW, cfg, codes, scales, ts)
+        e = xh - xf
+        assert st["n"] == rows * cols
+        np.testing.assert_allclose(st["sqnr_db"], 10 * np.log10((xf ** 2).sum() / (e ** 2).sum()), rtol=1e-12)
+        np.testing.assert_allclose(st["alpha"], (xf * xh).sum() / (xf ** 2).sum(), rtol=1e-12)
+        np.testing.assert_allclose(st["mean_signed_err"], (np.sign(xf) * e).mean(), rtol=1e-10, atol=1e-15)
+        np.testing.assert_allclose(st["mean_signed_err_grid"], (np.sign(xf) * e).mean(), rtol=1e-10, atol=1e-15)
+        assert st["amax"] == np.abs(xf).max()
+        assert st["n_saturated"] == 0 and st["n_nonfinite"] == 0
+        hist = np.bincount(unpack(codes).reshape(-1), minlength=16)
+        assert list(hist) == st["code_hist"]
+
+
+def test_stats_uniform_closed_form_and_shrinkage(orc):
+    # y ~ U(-Qmax, Qmax): E1M2 RTNE has MSE step^2/12 = 1/48 and no signed bias.
+    # Gaussian y scaled to each grid's range (4 sigma = Qmax): the projection
+    # gain alpha of E1M2 stays at 1 while E2M1 shrinks it (alpha < 1), the
+    # shrinkage the pages attribute to E2M1.  (The mean signed error of a
+    # Gaussian is negative on any grid, because the density falls off within
+    # each bucket; alpha isolates the grid's own asymmetry.)
+    rng = np.random.default_rng(14)
+    n = 1 << 20
+    y = rng.uniform(-3.5, 3.5, size=n).astype(np.float32)
+    e = value_table(orc, E1M2)[orc.round_f32(y, E1M2, RTNE)] - y.astype(np.float64)
+    assert abs(np.mean(e ** 2) - 1 / 48) < 1e-3
+    assert abs(np.mean(np.sign(y) * e)) < 1e-3
+    z = np.clip(rng.standard_normal(n), -4, 4)
+    res = {}
+    for grid, qmax in ((E1M2, 3.5), (E2M1, 6.0)):
+        y = (z * qmax / 4).astype(np.float32)
+        xh = value_table(orc, grid)[orc.round_f32(y, grid, RTNE)]
+        yd = y.astype(np.float64)
+        res[grid] = (yd * xh).sum() / (yd ** 2).sum()
+    assert abs(res[E1M2] - 1.0) < 1e-3
+    assert res[E2M1] < 0.995
+
+
+def test_stats_shrinkage_ranking_on_activation(orc):
+    # qualitative trend of the pages' RHT paradox on synthetic activations:
+    # with RHT, E1M2 beats E2M1 in SQNR; E2M1 shows a negative grid-unit bias.
+    xb = synth.activation(256, 256, 21)
+    res = {}
+    for grid in (E1M2, E2M1):
+        cfg = orc.config(grid=grid, rht=1, rht_seed=3)
+        codes, scales, ts = orc.quantize(xb, cfg, ROW)
+        res[grid] = orc.stats(xb, ROW, cfg, codes, scales, ts)
+    assert res[E1M2]["sqnr_db"] > res[E2M1]["sqnr_db"]
+    assert res[E2M1]["mean_signed_err_grid"] < 0
+    assert abs(res[E1M2]["mean_signed_err_grid"]) < abs(res[E2M1]["mean_signed_err_grid"])
+
+
+# --------------------------------------------------- INT4 == E1M2 (derived)
+@pytest.mark.parametrize("rounding", [RTNE, SR])
+@pytest.mark.parametrize("scaling", [NV16, MX32])
+def test_int4_dequantizes_identically_to_e1m2(orc, rounding, scaling):
+    xb = synth.activation(64, 128, 31)
+    out = {}
+    for grid in (E1M2, INT4):
+        cfg = orc.config(grid=grid, rounding=rounding, scaling=scaling, rht=1, rht_seed=7, sr_seed=8)
+        codes, scales, ts = orc.quantize(xb, cfg, ROW)
+        out[grid] = (codes, orc.dequantize(codes, scales, ts, 64, 128, cfg))
+    np.testing.assert_array_equal(out[E1M2][1].view(np.uint32), out[INT4][1].view(np.uint32))
+    e, i = unpack(out[E1M2][0]), unpack(out[INT4][0])
+    sm_to_tc = np.array([0, 1, 2, 3, 4, 5, 6, 7, 0, 15, 14, 13, 12, 11, 10, 9], np.uint8)
+    np.testing.assert_array_equal(sm_to_tc[e], i)
