@@ -1,0 +1,163 @@
+"""MI355X (gfx950) fused random-Hadamard transform + 4-bit block quantization.
+
+Thin Python layer over the C ABI of ``libufp4.so`` (include/ufp4.h): the
+functions below marshal torch device tensors into pointers and call the
+entry point of the same name.  PyTorch only provides device memory and
+streams; every step of the quantization runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._lib import (GRID_E1M2, GRID_E2M1, GRID_INT4, LIB_PATH, ROUND_RTNE, ROUND_STOCHASTIC,
+                   SCALE_MX32, SCALE_NV16, Ufp4Error, check, lib, ufp4_config, ufp4_qtensor,
+                   ufp4_stats_t)
+
+__all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "ROUND_RTNE", "ROUND_STOCHASTIC", "SCALE_NV16",
+           "SCALE_MX32", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
+           "ufp4_quantize", "ufp4_quantize_rowcol", "ufp4_quantize_grouped", "ufp4_dequantize",
+           "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets",
+           "block_len"]
+
+
+def config(grid: int = GRID_E1M2, rounding: int = ROUND_RTNE, scaling: int = SCALE_NV16,
+           rht: int = 1, rht_seed: int = 0, sr_seed: int = 0) -> ufp4_config:
+    return ufp4_config(int(grid), int(rounding), int(scaling), int(rht), int(rht_seed), int(sr_seed))
+
+
+def block_len(scaling: int) -> int:
+    return 32 if scaling == SCALE_MX32 else 16
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bf16_view(x: torch.Tensor):
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("x must hold bf16 values (bfloat16, or their 16-bit patterns)")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit column stride")
+    return x.shape[0], x.shape[1], x.stride(0)
+
+
+class QTensor:
+    """Device buffers of one quantized layout: packed codes, block scales and
+    per-tensor scale(s)."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, tensor_scale: torch.Tensor):
+        self.codes, self.scales, self.tensor_scale = codes, scales, tensor_scale
+
+    def c(self) -> ufp4_qtensor:
+        return ufp4_qtensor(self.codes.data_ptr(), self.scales.data_ptr(), self.tensor_scale.data_ptr())
+
+
+def alloc_layout(lines: int, length: int, scaling: int, n_tensor_scales: int = 1,
+                 device="cuda") -> QTensor:
+    """Output buffers for `lines` block lines of `length` elements each."""
+    B = block_len(scaling)
+    return QTensor(torch.empty((lines, length // 2), dtype=torch.uint8, device=device),
+                   torch.empty((lines, length // B), dtype=torch.uint8, device=device),
+                   torch.empty(n_tensor_scales, dtype=torch.float32, device=device))
+
+
+class Workspace:
+    """Caller-owned device workspace (zeroed once by ufp4_workspace_init)."""
+
+    def __init__(self, rows: int, cols: int, num_groups: int = 1, device="cuda", stream=None):
+        self.nbytes = int(lib.ufp4_workspace_size(rows, cols, num_groups))
+        if self.nbytes == 0:
+            raise ValueError("invalid workspace shape")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        check("ufp4_workspace_init", lib.ufp4_workspace_init(_ptr(self.buf), self.nbytes, _stream(stream)))
+
+    @property
+    def ptr(self):
+        return _ptr(self.buf)
+
+    def status(self, stream=None) -> int:
+        st = ctypes.c_int(0)
+        check("ufp4_workspace_status", lib.ufp4_workspace_status(self.ptr, self.nbytes, ctypes.byref(st),
+                                                                   _stream(stream)))
+        return st.value
+
+
+def ufp4_quantize(x: torch.Tensor, cfg: ufp4_config, row_out: QTensor, ws: Workspace | None,
+                  stream=None) -> None:
+    rows, cols, ld = _bf16_view(x)
+    check("ufp4_quantize", lib.ufp4_quantize(_ptr(x), rows, cols, ld, ctypes.byref(cfg), row_out.c(),
+                                             ws.ptr if ws else None, ws.nbytes if ws else 0,
+                                             _stream(stream)))
+
+
+def ufp4_quantize_rowcol(x: torch.Tensor, cfg: ufp4_config, row_out: QTensor, col_out: QTensor,
+                         ws: Workspace | None, stream=None) -> None:
+    rows, cols, ld = _bf16_view(x)
+    check("ufp4_quantize_rowcol",
+          lib.ufp4_quantize_rowcol(_ptr(x), rows, cols, ld, ctypes.byref(cfg), row_out.c(), col_out.c(),
+                                   ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)))
+
+
+def ufp4_quantize_grouped(x: torch.Tensor, offsets_dev: torch.Tensor, padded_rows: int,
+                          cfg: ufp4_config, row_out: QTensor | None, col_out: QTensor | None,
+                          ws: Workspace | None, stream=None) -> None:
+    rows, cols, ld = _bf16_view(x)
+    if ld != cols:
+        raise ValueError("grouped input must be contiguous")
+    if offsets_dev.dtype != torch.int64:
+        raise TypeError("offsets must be int64")
+    E = offsets_dev.numel() - 1
+    null = ufp4_qtensor(None, None, None)
+    check("ufp4_quantize_grouped",
+          lib.ufp4_quantize_grouped(_ptr(x), rows, cols, _ptr(offsets_dev), E, int(padded_rows),
+                                    ctypes.byref(cfg), row_out.c() if row_out else null,
+                                    col_out.c() if col_out else null, ws.ptr if ws else None,
+                                    ws.nbytes if ws else 0, _stream(stream)))
+
+
+def ufp4_dequantize(q: QTensor, rows: int, cols: int, cfg: ufp4_config, inverse_rht: bool,
+                    out: torch.Tensor, stream=None) -> None:
+    check("ufp4_dequantize",
+          lib.ufp4_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), rows, cols,
+                              ctypes.byref(cfg), int(bool(inverse_rht)), _ptr(out), _stream(stream)))
+
+
+def ufp4_stats(x: torch.Tensor, layout: int, cfg: ufp4_config, q: QTensor, ws: Workspace,
+               stream=None) -> dict:
+    rows, cols, ld = _bf16_view(x)
+    out = ufp4_stats_t()
+    check("ufp4_stats", lib.ufp4_stats(_ptr(x), rows, cols, ld, int(layout), ctypes.byref(cfg),
+                                       _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), ws.ptr,
+                                       ws.nbytes, ctypes.byref(out), _stream(stream)))
+    return out.as_dict()
+
+
+def ufp4_round_f32(y: torch.Tensor, grid: int, rounding: int, sr_seed: int, codes: torch.Tensor,
+                   stream=None) -> None:
+    if y.dtype != torch.float32 or codes.dtype != torch.uint8 or codes.numel() != y.numel():
+        raise TypeError("y must be float32 and codes uint8 of the same size")
+    check("ufp4_round_f32", lib.ufp4_round_f32(_ptr(y), y.numel(), int(grid), int(rounding),
+                                               int(sr_seed), _ptr(codes), _stream(stream)))
+
+
+def ufp4_rht_signs(rht_seed: int) -> np.ndarray:
+    s = np.zeros(16, dtype=np.int8)
+    check("ufp4_rht_signs", lib.ufp4_rht_signs(int(rht_seed), s.ctypes.data_as(ctypes.c_void_p)))
+    return s
+
+
+def ufp4_grouped_col_offsets(offsets, block: int) -> np.ndarray:
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    out = np.zeros(off.size, dtype=np.int64)
+    check("ufp4_grouped_col_offsets",
+          lib.ufp4_grouped_col_offsets(off.ctypes.data_as(ctypes.c_void_p), off.size - 1, int(block),
+                                       out.ctypes.data_as(ctypes.c_void_p)))
+    return out

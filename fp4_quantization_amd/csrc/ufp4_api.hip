@@ -1,0 +1,357 @@
+// ufp4_api.hip -- the C ABI (include/ufp4.h): argument checks, workspace
+// layout and launches.  Every check runs on the host before anything is
+// enqueued; nothing here allocates device memory.
+#include <string.h>
+
+#include "../../include/ufp4.h"
+#include "ufp4_internal.hpp"
+
+using namespace ufp4;
+
+namespace {
+
+constexpr int kStatsMaxWg = 1024;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_cfg(const ufp4_config* cfg) {
+  if (!cfg) return UFP4_ERR_INVALID_ARGUMENT;
+  if (cfg->grid < 0 || cfg->grid > 2) return UFP4_ERR_INVALID_ARGUMENT;
+  if (cfg->rounding < 0 || cfg->rounding > 1) return UFP4_ERR_INVALID_ARGUMENT;
+  if (cfg->scaling < 0 || cfg->scaling > 1) return UFP4_ERR_INVALID_ARGUMENT;
+  if (cfg->rht != 0 && cfg->rht != 1) return UFP4_ERR_INVALID_ARGUMENT;
+  return UFP4_OK;
+}
+
+int block_of(const ufp4_config* cfg) { return cfg->scaling == UFP4_SCALE_MX32 ? 32 : 16; }
+
+size_t quant_ws_bytes(int64_t rows, int64_t cols, int32_t groups) {
+  int32_t nb, nt;
+  const int64_t g16 = grid_size_quant(rows, cols, groups, 16, &nb, &nt);
+  const int64_t g32 = grid_size_quant(rows, cols, groups, 32, &nb, &nt);
+  const int64_t g = g16 > g32 ? g16 : g32;
+  return kWsHeader + ws_scale_bytes(groups) + (size_t)g * sizeof(float4);
+}
+
+size_t stats_ws_bytes() { return kWsHeader + (size_t)kStatsMaxWg * kStatsSlots * sizeof(double); }
+
+int check_qtensor(const ufp4_qtensor& q, int32_t n_ts) {
+  if (!q.codes || !q.scales || !q.tensor_scale) return UFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(q.codes, 16) || !aligned(q.tensor_scale, 4)) return UFP4_ERR_ALIGNMENT;
+  (void)n_ts;
+  return UFP4_OK;
+}
+
+// Common setup of the quantization parameters.
+void base_params(QuantParams& p, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                 const ufp4_config* cfg, void* ws) {
+  memset(&p, 0, sizeof p);
+  p.x = x;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld = ld;
+  p.num_groups = 1;
+  p.block = block_of(cfg);
+  p.padded_rows = rows;
+  p.rht = cfg->rht;
+  p.mx = cfg->scaling == UFP4_SCALE_MX32;
+  p.grid = cfg->grid;
+  p.sr = cfg->rounding == UFP4_ROUND_STOCHASTIC;
+  p.sr_k0 = (uint32_t)cfg->sr_seed;
+  p.sr_k1 = (uint32_t)(cfg->sr_seed >> 32);
+  fill_rht_signs(cfg->rht_seed, p);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  p.ws_counter = reinterpret_cast<uint32_t*>(w);
+  p.ws_status = reinterpret_cast<uint32_t*>(w + 4);
+}
+
+int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (p.rows == 0 || p.cols == 0) {
+    // nothing to quantize: every per-tensor scale is 1 (a zero tensor)
+    if (p.do_row && p.row_ts &&
+        launch_fill(reinterpret_cast<uint32_t*>(p.row_ts), p.num_groups, 0x3F800000u, stream) != hipSuccess)
+      return UFP4_ERR_HIP;
+    if (p.do_col && p.col_ts &&
+        launch_fill(reinterpret_cast<uint32_t*>(p.col_ts), p.num_groups, 0x3F800000u, stream) != hipSuccess)
+      return UFP4_ERR_HIP;
+    return UFP4_OK;
+  }
+  const int64_t grid = grid_size_quant(p.rows, p.cols, p.num_groups, p.block, &p.n_band, &p.n_tiles);
+  p.n_work = p.n_band * p.n_tiles;
+  if (grid > 0x7FFFFFFF) return UFP4_ERR_SHAPE;
+  if (!p.mx) {
+    const size_t need = quant_ws_bytes(p.rows, p.cols, p.num_groups);
+    if (!ws || ws_bytes < need || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    p.ws_scale = reinterpret_cast<float*>(w + kWsHeader);
+    p.ws_part = reinterpret_cast<float4*>(w + kWsHeader + ws_scale_bytes(p.num_groups));
+    if (launch_amax(p, grid, stream) != hipSuccess) return UFP4_ERR_HIP;
+  }
+  if (launch_quant(p, grid, stream) != hipSuccess) return UFP4_ERR_HIP;
+  return UFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ufp4_status_string(int status) {
+  switch (status) {
+    case UFP4_OK: return "ok";
+    case UFP4_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case UFP4_ERR_SHAPE: return "shape is not a multiple of the block";
+    case UFP4_ERR_ALIGNMENT: return "misaligned pointer or leading dimension";
+    case UFP4_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case UFP4_ERR_HIP: return "HIP runtime error";
+    case UFP4_ERR_OFFSETS: return "grouped offsets invalid";
+    default: return "unknown status";
+  }
+}
+
+size_t ufp4_workspace_size(int64_t rows, int64_t cols, int32_t num_groups) {
+  if (rows < 0 || cols < 0 || num_groups < 1) return 0;
+  const size_t a = quant_ws_bytes(rows, cols, num_groups), b = stats_ws_bytes();
+  return a > b ? a : b;
+}
+
+int ufp4_workspace_init(void* ws, size_t ws_bytes, ufp4_stream_t stream) {
+  if (!ws || ws_bytes < kWsHeader || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
+  if (launch_fill(static_cast<uint32_t*>(ws), (int64_t)(kWsHeader / 4), 0u, (hipStream_t)stream) != hipSuccess)
+    return UFP4_ERR_HIP;
+  return UFP4_OK;
+}
+
+int ufp4_workspace_status(const void* ws, size_t ws_bytes, int* status_out, ufp4_stream_t stream) {
+  if (!ws || ws_bytes < kWsHeader || !status_out) return UFP4_ERR_INVALID_ARGUMENT;
+  uint32_t st = 0;
+  if (hipMemcpyAsync(&st, static_cast<const uint8_t*>(ws) + 4, 4, hipMemcpyDeviceToHost,
+                     (hipStream_t)stream) != hipSuccess)
+    return UFP4_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return UFP4_ERR_HIP;
+  *status_out = st ? UFP4_ERR_OFFSETS : UFP4_OK;
+  return UFP4_OK;
+}
+
+int ufp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const ufp4_config* cfg,
+                  ufp4_qtensor row_out, void* ws, size_t ws_bytes, ufp4_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (rows < 0 || cols < 0 || ld < cols) return UFP4_ERR_INVALID_ARGUMENT;
+  if (cols % block_of(cfg)) return UFP4_ERR_SHAPE;
+  if ((rc = check_qtensor(row_out, 1))) return rc;
+  if (rows > 0 && cols > 0) {
+    if (!x) return UFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || ld % 8) return UFP4_ERR_ALIGNMENT;
+  }
+  QuantParams p;
+  base_params(p, x, rows, cols, ld, cfg, ws);
+  p.do_row = 1;
+  p.row_codes = row_out.codes;
+  p.row_scales = row_out.scales;
+  p.row_ts = row_out.tensor_scale;
+  if (rows == 0 || cols == 0) cols = rows = 0;
+  p.rows = rows;
+  p.cols = cols;
+  return run_quant(p, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                         const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws,
+                         size_t ws_bytes, ufp4_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (rows < 0 || cols < 0 || ld < cols) return UFP4_ERR_INVALID_ARGUMENT;
+  const int B = block_of(cfg);
+  if (cols % B || rows % B) return UFP4_ERR_SHAPE;
+  if ((rc = check_qtensor(row_out, 1))) return rc;
+  if ((rc = check_qtensor(col_out, 1))) return rc;
+  if (rows > 0 && cols > 0) {
+    if (!x) return UFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || ld % 8) return UFP4_ERR_ALIGNMENT;
+  }
+  QuantParams p;
+  base_params(p, x, rows, cols, ld, cfg, ws);
+  p.do_row = 1;
+  p.do_col = 1;
+  p.row_codes = row_out.codes;
+  p.row_scales = row_out.scales;
+  p.row_ts = row_out.tensor_scale;
+  p.col_codes = col_out.codes;
+  p.col_scales = col_out.scales;
+  p.col_ts = col_out.tensor_scale;
+  if (rows == 0 || cols == 0) p.rows = p.cols = 0;
+  p.padded_rows = p.rows;
+  return run_quant(p, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int ufp4_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
+                          const int64_t* offsets_dev, int32_t num_groups, int64_t padded_rows,
+                          const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws,
+                          size_t ws_bytes, ufp4_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (total_rows < 0 || cols < 0 || num_groups < 1 || num_groups > kMaxGroups) return UFP4_ERR_INVALID_ARGUMENT;
+  if (!offsets_dev) return UFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(offsets_dev, 8)) return UFP4_ERR_ALIGNMENT;
+  const int B = block_of(cfg);
+  if (cols % B) return UFP4_ERR_SHAPE;
+  const bool do_row = row_out.codes != nullptr, do_col = col_out.codes != nullptr;
+  if (!do_row && !do_col) return UFP4_ERR_INVALID_ARGUMENT;
+  if (do_row && (rc = check_qtensor(row_out, num_groups))) return rc;
+  if (do_col) {
+    if ((rc = check_qtensor(col_out, num_groups))) return rc;
+    if (padded_rows < total_rows || padded_rows % B ||
+        padded_rows > total_rows + (int64_t)(B - 1) * num_groups)
+      return UFP4_ERR_SHAPE;
+  }
+  if (total_rows > 0 && cols > 0) {
+    if (!x) return UFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || cols % 8) return UFP4_ERR_ALIGNMENT;
+  }
+  QuantParams p;
+  base_params(p, x, total_rows, cols, cols, cfg, ws);
+  p.offsets = offsets_dev;
+  p.num_groups = num_groups;
+  p.padded_rows = do_col ? padded_rows : 0;
+  p.do_row = do_row;
+  p.do_col = do_col;
+  p.row_codes = row_out.codes;
+  p.row_scales = row_out.scales;
+  p.row_ts = row_out.tensor_scale;
+  p.col_codes = col_out.codes;
+  p.col_scales = col_out.scales;
+  p.col_ts = col_out.tensor_scale;
+  return run_quant(p, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int ufp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t rows,
+                    int64_t cols, const ufp4_config* cfg, int32_t inverse_rht, float* out,
+                    ufp4_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (rows < 0 || cols < 0) return UFP4_ERR_INVALID_ARGUMENT;
+  if (cols % block_of(cfg)) return UFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return UFP4_OK;
+  if (!codes || !scales || !out || (!tensor_scale && cfg->scaling == UFP4_SCALE_NV16))
+    return UFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(codes, 8) || !aligned(out, 16)) return UFP4_ERR_ALIGNMENT;
+  DequantParams p;
+  memset(&p, 0, sizeof p);
+  p.codes = codes;
+  p.scales = scales;
+  p.ts = tensor_scale;
+  p.rows = rows;
+  p.cols = cols;
+  p.grid = cfg->grid;
+  p.mx = cfg->scaling == UFP4_SCALE_MX32;
+  p.inverse = inverse_rht ? 1 : 0;
+  const uint32_t mask = rht_sign_mask(cfg->rht_seed);
+  for (int j = 0; j < 16; ++j) p.d[j] = ((mask >> j) & 1u) ? -1.0f : 1.0f;
+  p.out = out;
+  return launch_dequant(p, (hipStream_t)stream) == hipSuccess ? UFP4_OK : UFP4_ERR_HIP;
+}
+
+int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_t layout,
+               const ufp4_config* cfg, const uint8_t* codes, const uint8_t* scales,
+               const float* tensor_scale, void* ws, size_t ws_bytes, ufp4_stats_t* host_out,
+               ufp4_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!host_out || rows < 0 || cols < 0 || ld < cols || (layout != 0 && layout != 1))
+    return UFP4_ERR_INVALID_ARGUMENT;
+  const int B = block_of(cfg);
+  if ((layout == 0 ? cols : rows) % B) return UFP4_ERR_SHAPE;
+  if (!ws || ws_bytes < stats_ws_bytes() || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
+  memset(host_out, 0, sizeof *host_out);
+  const int64_t nblk = rows * cols / B;
+  if (nblk == 0) {
+    host_out->sqnr_db = __builtin_inf();
+    host_out->alpha = 1.0;
+    return UFP4_OK;
+  }
+  if (!x || !codes || !scales || (!tensor_scale && cfg->scaling == UFP4_SCALE_NV16))
+    return UFP4_ERR_INVALID_ARGUMENT;
+  StatsParams p;
+  memset(&p, 0, sizeof p);
+  p.x = x;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld = ld;
+  p.layout = layout;
+  p.grid = cfg->grid;
+  p.mx = cfg->scaling == UFP4_SCALE_MX32;
+  p.rht = cfg->rht;
+  QuantParams tmp;
+  memset(&tmp, 0, sizeof tmp);
+  fill_rht_signs(cfg->rht_seed, tmp);
+  p.sg = tmp.sg;
+  p.codes = codes;
+  p.scales = scales;
+  p.ts = tensor_scale;
+  int64_t wg = (nblk + 255) / 256;
+  if (wg > kStatsMaxWg) wg = kStatsMaxWg;
+  p.n_wg = (int32_t)wg;
+  p.part = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + kWsHeader);
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_stats(p, s) != hipSuccess) return UFP4_ERR_HIP;
+  static thread_local double host[kStatsMaxWg * kStatsSlots];
+  if (hipMemcpyAsync(host, p.part, (size_t)wg * kStatsSlots * sizeof(double), hipMemcpyDeviceToHost, s) !=
+      hipSuccess)
+    return UFP4_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return UFP4_ERR_HIP;
+  double v2 = 0, e2 = 0, vx = 0, se = 0, seg = 0, amax = 0;
+  double n = 0, n_grid = 0, n_zero = 0, n_sat = 0, n_nf = 0;
+  double hist[16] = {0};
+  for (int64_t i = 0; i < wg; ++i) {
+    const double* q = host + i * kStatsSlots;
+    v2 += q[0]; e2 += q[1]; vx += q[2]; se += q[3]; seg += q[4];
+    amax = q[5] > amax ? q[5] : amax;
+    n += q[6]; n_grid += q[7]; n_zero += q[8]; n_sat += q[9]; n_nf += q[10];
+    for (int c = 0; c < 16; ++c) hist[c] += q[11 + c];
+  }
+  host_out->n = (uint64_t)n;
+  for (int c = 0; c < 16; ++c) host_out->code_hist[c] = (uint64_t)hist[c];
+  host_out->n_saturated = (uint64_t)n_sat;
+  host_out->n_nonfinite = (uint64_t)n_nf;
+  host_out->n_zero_scale = (uint64_t)n_zero;
+  host_out->amax = amax;
+  host_out->sqnr_db = e2 > 0 ? 10.0 * __builtin_log10(v2 / e2) : __builtin_inf();
+  host_out->mean_signed_err = n > 0 ? se / n : 0.0;
+  host_out->mean_signed_err_grid = n_grid > 0 ? seg / n_grid : 0.0;
+  host_out->alpha = v2 > 0 ? vx / v2 : 1.0;
+  return UFP4_OK;
+}
+
+int ufp4_round_f32(const float* y_dev, int64_t n, int32_t grid, int32_t rounding, uint64_t sr_seed,
+                   uint8_t* codes_dev, ufp4_stream_t stream) {
+  if (n < 0 || grid < 0 || grid > 2 || rounding < 0 || rounding > 1) return UFP4_ERR_INVALID_ARGUMENT;
+  if (n == 0) return UFP4_OK;
+  if (!y_dev || !codes_dev) return UFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(y_dev, 4)) return UFP4_ERR_ALIGNMENT;
+  return launch_round(y_dev, n, grid, rounding, sr_seed, codes_dev, (hipStream_t)stream) == hipSuccess
+             ? UFP4_OK
+             : UFP4_ERR_HIP;
+}
+
+int ufp4_rht_signs(uint64_t rht_seed, int8_t signs_host[16]) {
+  if (!signs_host) return UFP4_ERR_INVALID_ARGUMENT;
+  const uint32_t mask = rht_sign_mask(rht_seed);
+  for (int j = 0; j < 16; ++j) signs_host[j] = ((mask >> j) & 1u) ? (int8_t)-1 : (int8_t)1;
+  return UFP4_OK;
+}
+
+int ufp4_grouped_col_offsets(const int64_t* offsets_host, int32_t num_groups, int32_t block,
+                             int64_t* col_offsets_host) {
+  if (!offsets_host || !col_offsets_host || num_groups < 1 || (block != 16 && block != 32))
+    return UFP4_ERR_INVALID_ARGUMENT;
+  if (offsets_host[0] != 0) return UFP4_ERR_INVALID_ARGUMENT;
+  col_offsets_host[0] = 0;
+  for (int32_t e = 0; e < num_groups; ++e) {
+    const int64_t m = offsets_host[e + 1] - offsets_host[e];
+    if (m < 0) return UFP4_ERR_INVALID_ARGUMENT;
+    col_offsets_host[e + 1] = col_offsets_host[e] + (m + block - 1) / block * block;
+  }
+  return UFP4_OK;
+}
+
+}  // extern "C"

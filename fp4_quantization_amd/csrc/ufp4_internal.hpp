@@ -1,0 +1,93 @@
+// ufp4_internal.hpp -- host/device shared parameter blocks and launchers of
+// the gfx950 kernels (internal to the library; the public ABI is ufp4.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ufp4_device.hpp"
+
+namespace ufp4 {
+
+// Geometry of the quantization kernels.  A workgroup of 4 wavefronts covers a
+// tile of kTileRows x kBandCols elements: each wavefront a 32-row strip (two
+// 16-row halves, one per 32-lane half of the wavefront), each lane 16 rows x 8
+// columns (one 16-byte load per row).
+constexpr int kThreads = 256;
+constexpr int kBandCols = 256;
+constexpr int kTileRows = 128;
+constexpr int kMaxGroups = 256;
+constexpr int kNumXcd = 8;
+
+struct QuantParams {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  const int64_t* offsets;  // grouped: device offsets[E+1]; dense: null
+  int32_t num_groups;      // E (1 for a dense tensor)
+  int32_t block;           // 16 (NV16) or 32 (MX32)
+  int64_t padded_rows;     // length of a column-wise output line
+  uint8_t* row_codes;
+  uint8_t* row_scales;
+  float* row_ts;
+  uint8_t* col_codes;
+  uint8_t* col_scales;
+  float* col_ts;
+  int32_t do_row, do_col, rht, mx, grid, sr;
+  uint32_t sr_k0, sr_k1;
+  RhtSigns sg;        // folded signs for in-lane (column-wise) blocks
+  HalfSigns hs[2];    // folded signs for the two 8-column halves of a row block
+  float s4[2];        // stage-4 multiplier of the partner value, per lane parity
+  float fin_lane[2];  // output multiplier per lane parity (row-wise blocks)
+  int32_t n_band;     // column bands of kBandCols
+  int32_t n_tiles;    // row tiles per band (upper bound for grouped)
+  int32_t n_work;     // n_band * n_tiles (workgroups beyond this are idle)
+  // workspace
+  uint32_t* ws_counter;
+  uint32_t* ws_status;
+  float* ws_scale;    // [E][2]: per-tensor scale S_t (row, col) after phase A
+  float4* ws_part;    // [gridDim.x]: (segment, max|w| row, max|w| col, -)
+};
+
+// Workspace layout (bytes).
+constexpr size_t kWsHeader = 256;                 // counter, status
+inline size_t ws_scale_bytes(int32_t groups) { return ((size_t)groups * 2 * sizeof(float) + 255) / 256 * 256; }
+
+void fill_rht_signs(uint64_t seed, QuantParams& p);
+uint32_t rht_sign_mask(uint64_t seed);
+
+int64_t grid_size_quant(int64_t rows, int64_t cols, int32_t groups, int32_t block, int32_t* n_band,
+                        int32_t* n_tiles);
+
+hipError_t launch_amax(const QuantParams& p, int64_t grid, hipStream_t s);
+hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s);
+hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
+
+struct DequantParams {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* ts;
+  int64_t rows, cols;
+  int32_t grid, mx, inverse;
+  float d[16];  // signs of the inverse transform
+  float* out;
+};
+hipError_t launch_dequant(const DequantParams& p, hipStream_t s);
+
+struct StatsParams {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  int32_t layout, grid, mx, rht;
+  RhtSigns sg;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* ts;
+  double* part;  // per workgroup: 5 doubles + 20 counters (as double-size slots)
+  int32_t n_wg;
+};
+constexpr int kStatsSlots = 32;  // 8-byte slots per workgroup partial
+hipError_t launch_stats(const StatsParams& p, hipStream_t s);
+
+hipError_t launch_round(const float* y, int64_t n, int32_t grid, int32_t rounding, uint64_t seed,
+                        uint8_t* codes, hipStream_t s);
+
+}  // namespace ufp4

@@ -1,0 +1,208 @@
+/*
+ * ufp4.h -- C ABI of the MI355X (gfx950) library for fused random-Hadamard
+ * transform + 4-bit block quantization, the operand-quantization step of the
+ * UFP4 FP4-pretraining recipe.
+ *
+ * The method (sources cited by title and section):
+ *   [Z] "Shrinkage Bias: The Hidden Geometric Trap in FP4 Training ... and the
+ *       UFP4 Fix" (zhichai.net) -- "Key points": the E2M1 and E1M2 grids, the
+ *       RHT paradox, the fix (uniform grid, RHT on all three GEMM paths,
+ *       stochastic rounding, fused RHT+quantization kernels).
+ *   [A] "UFP4 Eliminates Shrinkage Bias in FP4 LLM Pretraining, Ant Group
+ *       Research Finds" (autonainews.com) -- "The UFP4 Recipe": uniform E1M2 or
+ *       INT4 grids, RHT on the three training GEMMs, stochastic rounding only
+ *       on the output gradient dY.
+ *   [H] "Rethinking Shrinkage Bias in LLM FP4 Pretraining: Geometric Origin,
+ *       Systemic Impact, and UFP4 Recipe" (hotpaper.ai) -- technical approach:
+ *       RHT on FPROP/DGRAD/WGRAD, SR on dY, NVFP4 and MXFP4 as comparison
+ *       formats; RTNE named as the rounding that exposes E2M1's bias.
+ *
+ * Per 16-element block along the GEMM reduction dimension the library
+ *   1. multiplies by 16 seeded random signs, runs a 16-point fast
+ *      Walsh-Hadamard butterfly (stages of half-width 1, 2, 4, 8) and scales
+ *      by 1/4 (an orthonormal random Hadamard transform);
+ *   2. scales the block by an FP8-E4M3 block scale under an FP32 per-tensor
+ *      scale (NVFP4-style), or by a power-of-two E8M0 scale per 32 elements
+ *      (MXFP4-style);
+ *   3. rounds onto the uniform E1M2 grid {0, .5, ..., 3.5}, symmetric INT4
+ *      {-7..7} or the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}, with
+ *      round-to-nearest-even or Philox-driven stochastic rounding;
+ *   4. packs two 4-bit codes per byte.
+ * Outputs come in the row-wise layout (blocks along a row; the fwd_y and
+ * bwd_dx operands) and the column-wise layout (blocks down a column, stored
+ * transposed; the bwd_dw operands), for dense tensors and for ragged
+ * per-expert (MoE) row segments.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Scratch memory is a caller-owned
+ *     device workspace of ufp4_workspace_size() bytes.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns before it completes.  ufp4_stats and ufp4_workspace_status
+ *     synchronize the stream.
+ *   - Return value: UFP4_OK, or a UFP4_ERR_* code.  Argument errors are found
+ *     on the host before anything is enqueued, and leave outputs untouched.
+ *     Nothing throws across the ABI.
+ *   - Results are deterministic for fixed inputs and configuration.
+ *   - Calls that share one workspace must not run concurrently.
+ */
+#ifndef UFP4_H
+#define UFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* ufp4_stream_t; /* hipStream_t */
+
+enum ufp4_status {
+  UFP4_OK = 0,
+  UFP4_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad enum value, negative size */
+  UFP4_ERR_SHAPE = 2,            /* a dimension is not a multiple of the block */
+  UFP4_ERR_ALIGNMENT = 3,        /* a pointer or leading dimension is misaligned */
+  UFP4_ERR_WORKSPACE = 4,        /* workspace null or smaller than required */
+  UFP4_ERR_HIP = 5,              /* a HIP runtime call failed */
+  UFP4_ERR_OFFSETS = 6           /* grouped offsets were found invalid on the device */
+};
+
+enum ufp4_grid { UFP4_GRID_E1M2 = 0, UFP4_GRID_INT4 = 1, UFP4_GRID_E2M1 = 2 };
+enum ufp4_rounding { UFP4_ROUND_RTNE = 0, UFP4_ROUND_STOCHASTIC = 1 };
+/* NV16: E4M3 scale per 16 elements + FP32 per-tensor scale.
+ * MX32: E8M0 (power-of-two) scale per 32 elements, no tensor scale (1.0). */
+enum ufp4_scaling { UFP4_SCALE_NV16 = 0, UFP4_SCALE_MX32 = 1 };
+
+/* Quantization configuration ("tensor, grid, RHT on/off, rounding mode and seed").
+ * rht_seed selects the 16 random signs (bit j of word 0 of
+ * Philox4x32-10(key = rht_seed, counter = (0,0,2,0)) set => sign j is -1); both
+ * operands of one GEMM must use the same rht_seed.  sr_seed keys the random
+ * words of stochastic rounding: output element i of a layout uses word i%4 of
+ * Philox4x32-10(key = sr_seed, counter = (lo32(i/4), hi32(i/4), stream, 0)),
+ * stream 0 for the row-wise output and 1 for the column-wise output, with i the
+ * element's flat index in that output. */
+typedef struct {
+  int32_t grid;     /* enum ufp4_grid */
+  int32_t rounding; /* enum ufp4_rounding */
+  int32_t scaling;  /* enum ufp4_scaling */
+  int32_t rht;      /* 0 = off, 1 = random Hadamard transform on */
+  uint64_t rht_seed;
+  uint64_t sr_seed;
+} ufp4_config;
+
+/* One quantized layout.  All three pointers are device pointers. */
+typedef struct {
+  uint8_t* codes;      /* packed codes, element 2k in the low nibble of byte k */
+  uint8_t* scales;     /* one byte per scale block (E4M3 or E8M0) */
+  float* tensor_scale; /* one float (E floats for grouped calls) */
+} ufp4_qtensor;
+
+/* Quantization diagnostics, computed over the quantizer's own domain (v = the
+ * post-RHT input, xhat = the dequantized value before any inverse RHT), with
+ * binary64 sums:
+ *   sqnr_db = 10 log10(sum v^2 / sum (v - xhat)^2)
+ *   mean_signed_err = mean of sign(v) (xhat - v); negative = shrinkage toward
+ *     zero, the bias the pages measure per rounding bucket ([Z] "Key points").
+ *   mean_signed_err_grid = the same in grid units (divided by the block's
+ *     dequantization factor), over elements of blocks with a nonzero scale.
+ *   alpha = <v, xhat> / <v, v>, the gain of the scaled-copy-plus-orthogonal-
+ *     residual decomposition of a quantized operand ([Z] "Key points").
+ *   code_hist = occurrences of each 4-bit code (bucket utilisation, [H]).
+ *   n_saturated = elements with |v / d_b| > Qmax; n_nonfinite = non-finite
+ *     inputs; n_zero_scale = elements in blocks whose scale is zero. */
+typedef struct {
+  double sqnr_db, mean_signed_err, mean_signed_err_grid, alpha, amax;
+  uint64_t n, code_hist[16], n_saturated, n_nonfinite, n_zero_scale;
+} ufp4_stats_t;
+
+/* Static text for a status code. */
+const char* ufp4_status_string(int status);
+
+/* Bytes of device workspace needed by any call on a tensor of `rows` x `cols`
+ * with `num_groups` segments (1 for dense tensors). */
+size_t ufp4_workspace_size(int64_t rows, int64_t cols, int32_t num_groups);
+
+/* Prepare a workspace before its first use (zeroes its synchronization words
+ * with a fill kernel).  Every later call leaves it ready for the next one. */
+int ufp4_workspace_init(void* ws, size_t ws_bytes, ufp4_stream_t stream);
+
+/* After a grouped call: writes UFP4_OK or UFP4_ERR_OFFSETS (the device found
+ * the offsets invalid and wrote no output).  Synchronizes the stream. */
+int ufp4_workspace_status(const void* ws, size_t ws_bytes, int* status_out, ufp4_stream_t stream);
+
+/* Row-wise quantization of x[rows][ld] (bf16 bit patterns), blocks along each
+ * row.  cols must be a multiple of 16 (NV16) or 32 (MX32); rows may be any
+ * size >= 0.  x must be 16-byte aligned with ld a multiple of 8 elements and
+ * ld >= cols; output pointers 16-byte aligned.
+ * Output: codes[rows][cols/2], scales[rows][cols/B] (B = 16 or 32),
+ * tensor_scale[1] (S_t = amax/(Qmax*448) for NV16, 1.0 for MX32). */
+int ufp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                  const ufp4_config* cfg, ufp4_qtensor row_out, void* ws, size_t ws_bytes,
+                  ufp4_stream_t stream);
+
+/* Row-wise and column-wise quantization of the same tensor in one call.
+ * rows and cols must both be multiples of B.  Column-wise output is stored
+ * transposed: codes[cols][rows/2], scales[cols][rows/B], tensor_scale[1]
+ * (its own per-tensor scale, from the column-wise transformed values). */
+int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                         const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out,
+                         void* ws, size_t ws_bytes, ufp4_stream_t stream);
+
+/* Grouped (MoE) quantization of x[total_rows][cols] whose rows are split into
+ * num_groups ragged segments: segment e is rows [offsets[e], offsets[e+1]).
+ * offsets_dev: device array of num_groups+1 int64, offsets[0] = 0, non-
+ * decreasing, offsets[E] = total_rows.  Each segment gets its own tensor scale
+ * per layout.  Column-wise blocks restart at each segment start; a segment's
+ * last block is zero-padded to B rows and all of its outputs are stored.
+ * padded_rows = sum over segments of roundup(M_e, B) (ufp4_grouped_col_offsets
+ * computes it); the column output is codes[cols][padded_rows/2],
+ * scales[cols][padded_rows/B], segment e occupying positions
+ * [col_offsets[e], col_offsets[e+1]).  Row output as ufp4_quantize.
+ * row_out.tensor_scale / col_out.tensor_scale hold num_groups floats.  Either
+ * output may be skipped by passing a null codes pointer.  If the device finds
+ * the offsets inconsistent it writes nothing and ufp4_workspace_status
+ * reports UFP4_ERR_OFFSETS. */
+int ufp4_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
+                          const int64_t* offsets_dev, int32_t num_groups, int64_t padded_rows,
+                          const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out,
+                          void* ws, size_t ws_bytes, ufp4_stream_t stream);
+
+/* Dequantize one layout in its own orientation: `rows` lines of `cols`
+ * elements (for a column-wise output: rows = tensor cols, cols = tensor rows).
+ * out[rows][cols] = value(code) * d_b, one rounding, d_b = decode(scale) * S_t
+ * (NV16) or 2^(scale-127) (MX32); with inverse_rht != 0 each 16-block is then
+ * mapped back through the inverse transform (butterfly, x1/4, signs). */
+int ufp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                    int64_t rows, int64_t cols, const ufp4_config* cfg, int32_t inverse_rht,
+                    float* out, ufp4_stream_t stream);
+
+/* Diagnostics (ufp4_stats_t) of one dense layout of x (layout 0 row-wise,
+ * 1 column-wise) against its quantization (codes/scales/tensor_scale as
+ * written by ufp4_quantize / _rowcol).  Uses the workspace; synchronizes the
+ * stream and fills *host_out. */
+int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_t layout,
+               const ufp4_config* cfg, const uint8_t* codes, const uint8_t* scales,
+               const float* tensor_scale, void* ws, size_t ws_bytes, ufp4_stats_t* host_out,
+               ufp4_stream_t stream);
+
+/* --- diagnostic hooks (not on the hot path) ------------------------------ */
+
+/* codes_dev[i] = 4-bit code (one per byte) of y_dev[i] rounded at unit scale
+ * onto `grid`, with the stochastic-rounding word of index i in stream 0.
+ * +-inf saturates to +-Qmax; NaN gives code 0. */
+int ufp4_round_f32(const float* y_dev, int64_t n, int32_t grid, int32_t rounding,
+                   uint64_t sr_seed, uint8_t* codes_dev, ufp4_stream_t stream);
+
+/* The 16 signs (+1/-1) selected by rht_seed (host memory). */
+int ufp4_rht_signs(uint64_t rht_seed, int8_t signs_host[16]);
+
+/* Host helper: col_offsets[e] = sum over e' < e of roundup(offsets[e+1]-offsets[e], block),
+ * for e = 0..num_groups (col_offsets[num_groups] = padded_rows). */
+int ufp4_grouped_col_offsets(const int64_t* offsets_host, int32_t num_groups, int32_t block,
+                             int64_t* col_offsets_host);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UFP4_H */

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/ufp4.h, rejects bad arguments on the host before any
+launch, and its host helpers agree with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "ufp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ufp4_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def F():
+    import fp4_quantization_amd as F
+    return F
+
+
+def test_exports_every_declared_symbol(F):
+    names = declared_functions()
+    assert len(names) >= 12
+    raw = ctypes.CDLL(F.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(F._lib.EXPORTED)
+
+
+def test_status_strings(F):
+    for s in range(7):
+        assert F.lib.ufp4_status_string(s)
+    assert F.lib.ufp4_status_string(99) == b"unknown status"
+
+
+def test_host_signs_and_offsets_match_oracle(F, orc):
+    for seed in (0, 1, 2, 3, 4, 77, 2**63 + 5):
+        np.testing.assert_array_equal(F.ufp4_rht_signs(seed), orc.rht_signs(seed))
+    rng = np.random.default_rng(0)
+    for block in (16, 32):
+        counts = rng.integers(0, 100, size=40)
+        off = np.concatenate([[0], np.cumsum(counts)])
+        np.testing.assert_array_equal(F.ufp4_grouped_col_offsets(off, block),
+                                      orc.grouped_col_offsets(off, block))
+
+
+def test_workspace_size(F):
+    assert F.lib.ufp4_workspace_size(8192, 2048, 1) > 0
+    assert F.lib.ufp4_workspace_size(-1, 16, 1) == 0
+    assert F.lib.ufp4_workspace_size(16, 16, 0) == 0
+    assert F.lib.ufp4_workspace_size(65536, 4096, 64) >= F.lib.ufp4_workspace_size(65536, 4096, 1)
+
+
+# Argument errors are detected on the host before anything is enqueued, so
+# these calls are safe with fake (never dereferenced) pointers and no GPU.
+FAKE = 1 << 40  # 16-byte aligned, never touched
+
+
+def q(F, codes=FAKE, scales=FAKE, ts=FAKE):
+    return F.ufp4_qtensor(codes, scales, ts)
+
+
+def call_quant(F, rows=64, cols=64, ld=64, cfg=None, out=None, ws=FAKE, ws_bytes=1 << 30, x=FAKE):
+    cfg = cfg or F.config()
+    return F.lib.ufp4_quantize(ctypes.c_void_p(x), rows, cols, ld, ctypes.byref(cfg), out or q(F),
+                               ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_quantize_argument_errors(F):
+    assert call_quant(F, cfg=F.config(grid=3)) == 1
+    assert call_quant(F, cfg=F.config(rounding=2)) == 1
+    assert call_quant(F, cfg=F.config(scaling=5)) == 1
+    assert call_quant(F, cfg=F.config(rht=2)) == 1
+    assert F.lib.ufp4_quantize(ctypes.c_void_p(FAKE), 64, 64, 64, None, q(F), None, 0, None) == 1
+    assert call_quant(F, rows=-1) == 1
+    assert call_quant(F, ld=32) == 1
+    assert call_quant(F, cols=24) == 2                      # not a multiple of 16
+    assert call_quant(F, cols=48, ld=48, cfg=F.config(scaling=1)) == 2  # MX32 needs 32
+    assert call_quant(F, x=FAKE + 2) == 3
+    assert call_quant(F, ld=68) == 3
+    assert call_quant(F, out=q(F, codes=FAKE + 4)) == 3
+    assert call_quant(F, out=q(F, codes=0)) == 1
+    assert call_quant(F, x=0) == 1
+    assert call_quant(F, ws=0) == 4
+    assert call_quant(F, ws_bytes=16) == 4
+    assert call_quant(F, ws=FAKE + 16) == 4
+
+
+def test_rowcol_and_grouped_argument_errors(F):
+    cfg = F.config()
+    rc = F.lib.ufp4_quantize_rowcol(ctypes.c_void_p(FAKE), 40, 64, 64, ctypes.byref(cfg), q(F), q(F),
+                                    ctypes.c_void_p(FAKE), 1 << 30, None)
+    assert rc == 2  # rows not a multiple of 16
+    rc = F.lib.ufp4_quantize_rowcol(ctypes.c_void_p(FAKE), 64, 64, 64, ctypes.byref(cfg), q(F),
+                                    q(F, scales=0), ctypes.c_void_p(FAKE), 1 << 30, None)
+    assert rc == 1
+
+    def grouped(E=4, padded=None, offsets=FAKE, row=None, col=None, cols=64, rows=100):
+        return F.lib.ufp4_quantize_grouped(ctypes.c_void_p(FAKE), rows, cols, ctypes.c_void_p(offsets), E,
+                                           padded if padded is not None else 128, ctypes.byref(cfg),
+                                           row or q(F), col or q(F), ctypes.c_void_p(FAKE), 1 << 30, None)
+    assert grouped(E=0) == 1
+    assert grouped(E=257) == 1
+    assert grouped(offsets=0) == 1
+    assert grouped(offsets=FAKE + 4) == 3
+    assert grouped(padded=96) == 2          # fewer than total rows
+    assert grouped(padded=120) == 2         # not a multiple of 16
+    assert grouped(padded=100 + 15 * 4 + 16) == 2  # more than any segmentation allows
+    assert grouped(row=q(F, codes=0), col=q(F, codes=0)) == 1
+    assert grouped(cols=40) == 2
+
+
+def test_other_entry_point_errors(F):
+    cfg = F.config()
+    assert F.lib.ufp4_dequantize(None, None, None, 16, 24, ctypes.byref(cfg), 0, None, None) == 2
+    assert F.lib.ufp4_dequantize(None, None, None, 16, 32, ctypes.byref(cfg), 0, None, None) == 1
+    assert F.lib.ufp4_dequantize(None, None, None, 0, 32, ctypes.byref(cfg), 0, None, None) == 0
+    st = F.ufp4_stats_t()
+    assert F.lib.ufp4_stats(None, 16, 16, 16, 2, ctypes.byref(cfg), None, None, None, None, 0,
+                            ctypes.byref(st), None) == 1
+    assert F.lib.ufp4_stats(None, 16, 16, 16, 0, ctypes.byref(cfg), None, None, None, None, 0,
+                            ctypes.byref(st), None) == 4
+    assert F.lib.ufp4_round_f32(None, 10, 0, 0, 0, None, None) == 1
+    assert F.lib.ufp4_round_f32(None, 10, 3, 0, 0, None, None) == 1
+    assert F.lib.ufp4_round_f32(None, 0, 0, 0, 0, None, None) == 0
+    assert F.lib.ufp4_rht_signs(0, None) == 1
+    assert F.lib.ufp4_workspace_init(None, 0, None) == 4
+    assert F.lib.ufp4_grouped_col_offsets(None, 1, 16, None) == 1

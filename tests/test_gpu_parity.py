@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Codes, block scales, tensor scales and dequantized values must be
+bit-identical; statistics agree within 1e-6 relative with an absolute floor
+of 1e-6 * mean|v| (binary64 sums in a different order).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+E1M2, INT4, E2M1 = 0, 1, 2
+RTNE, SR = 0, 1
+NV16, MX32 = 0, 1
+ROW, COL = 0, 1
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp4_quantization_amd as F
+    import oracle
+    oracle.lib()
+    return torch, F, oracle
+
+
+def to_dev(torch, xb):
+    return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).cuda()
+
+
+def cfgs(F, orc, grid=E1M2, rounding=RTNE, scaling=NV16, rht=1, rht_seed=0, sr_seed=0):
+    return (F.config(grid, rounding, scaling, rht, rht_seed, sr_seed),
+            orc.config(grid, rounding, scaling, rht, rht_seed, sr_seed))
+
+
+def gpu_rowcol(env, xb, fc):
+    torch, F, _ = env
+    R, C = xb.shape
+    x = to_dev(torch, xb)
+    row = F.alloc_layout(R, C, fc.scaling)
+    col = F.alloc_layout(C, R, fc.scaling)
+    ws = F.Workspace(R, C)
+    F.ufp4_quantize_rowcol(x, fc, row, col, ws)
+    torch.cuda.synchronize()
+    return row, col
+
+
+def gpu_row(env, xb, fc, ld=None):
+    torch, F, _ = env
+    R, C = xb.shape
+    if ld is not None and ld != C:
+        buf = np.zeros((R, ld), np.uint16)
+        buf[:, :C] = xb
+        x = to_dev(torch, buf)[:, :C]
+    else:
+        x = to_dev(torch, xb)
+    row = F.alloc_layout(R, C, fc.scaling)
+    ws = F.Workspace(R, C)
+    F.ufp4_quantize(x, fc, row, ws)
+    torch.cuda.synchronize()
+    return row
+
+
+def assert_layout_equal(q, ref, what):
+    c, s, t = ref
+    gc, gs, gt = q.codes.cpu().numpy(), q.scales.cpu().numpy(), q.tensor_scale.cpu().numpy()
+    if not np.array_equal(gc, c):
+        bad = np.argwhere(gc != c)
+        raise AssertionError(f"{what}: {len(bad)} code bytes differ, first at {bad[:5].tolist()}")
+    if not np.array_equal(gs, s):
+        bad = np.argwhere(gs != s)
+        raise AssertionError(f"{what}: {len(bad)} scale bytes differ, first at {bad[:5].tolist()}")
+    assert gt.view(np.uint32)[: t.size].tolist() == t.view(np.uint32).tolist(), f"{what}: tensor scale"
+
+
+# ------------------------------------------------------------- rounding hook
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+@pytest.mark.parametrize("rounding", [RTNE, SR])
+def test_round_f32_all_bf16_patterns(env, grid, rounding):
+    torch, F, orc = env
+    say(f"[round_f32] grid={grid} rounding={rounding}")
+    y = synth.all_bf16_patterns()
+    want = orc.round_f32(y, grid, rounding, sr_seed=5)
+    yd = torch.from_numpy(y).cuda()
+    codes = torch.empty(y.size, dtype=torch.uint8, device="cuda")
+    F.ufp4_round_f32(yd, grid, rounding, 5, codes)
+    np.testing.assert_array_equal(codes.cpu().numpy(), want)
+
+
+def test_round_f32_dense_fp32_sweep(env):
+    # every fp32 bit pattern in [0, 8) with a stride, both signs, all grids,
+    # both roundings: catches ties and bucket edges beyond bf16 precision
+    torch, F, orc = env
+    say("[round_f32] fp32 sweep")
+    bits = np.arange(0, 0x41000000, 257, dtype=np.uint32)
+    y = np.concatenate([bits.view(np.float32), -bits.view(np.float32)])
+    yd = torch.from_numpy(y).cuda()
+    codes = torch.empty(y.size, dtype=torch.uint8, device="cuda")
+    for grid in (E1M2, INT4, E2M1):
+        for rounding in (RTNE, SR):
+            F.ufp4_round_f32(yd, grid, rounding, 9, codes)
+            np.testing.assert_array_equal(codes.cpu().numpy(), orc.round_f32(y, grid, rounding, sr_seed=9))
+
+
+# -------------------------------------------------------------- tiny config
+def test_tiny_config_row(env):
+    torch, F, orc = env
+    say("[tiny] 256x256 RHT E1M2 RTNE row-wise")
+    xb = synth.tiny(0)
+    fc, oc = cfgs(F, orc, rht_seed=0)
+    assert_layout_equal(gpu_row(env, xb, fc), orc.quantize(xb, oc, ROW), "tiny row")
+
+
+# ------------------------------------------------ small shapes, all variants
+SHAPES = [(384, 320), (160, 512), (32, 2048)]
+
+
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+@pytest.mark.parametrize("rounding", [RTNE, SR])
+@pytest.mark.parametrize("scaling", [NV16, MX32])
+@pytest.mark.parametrize("rht", [1, 0])
+def test_rowcol_variants(env, grid, rounding, scaling, rht):
+    torch, F, orc = env
+    for shape in SHAPES:
+        R, C = shape
+        say(f"[rowcol] {R}x{C} grid={grid} rnd={rounding} scl={scaling} rht={rht}")
+        xb = synth.activation(R, C, seed=R + C + grid)
+        fc, oc = cfgs(F, orc, grid, rounding, scaling, rht, rht_seed=3, sr_seed=11)
+        row, col = gpu_rowcol(env, xb, fc)
+        assert_layout_equal(row, orc.quantize(xb, oc, ROW), f"row {shape}")
+        assert_layout_equal(col, orc.quantize(xb, oc, COL), f"col {shape}")
+
+
+@pytest.mark.parametrize("scaling", [NV16, MX32])
+def test_row_ragged_rows_and_padded_ld(env, scaling):
+    torch, F, orc = env
+    for R, C, ld in [(1, 32, 32), (100, 64, 72), (129, 96, 96), (300, 256, 264)]:
+        say(f"[row ragged] {R}x{C} ld={ld} scl={scaling}")
+        xb = synth.output_grad(R, C, seed=R)
+        fc, oc = cfgs(F, orc, E1M2, SR, scaling, 1, rht_seed=1, sr_seed=2)
+        assert_layout_equal(gpu_row(env, xb, fc, ld=ld), orc.quantize(xb, oc, ROW), f"row {R}x{C}")
+
+
+def test_edge_values(env):
+    torch, F, orc = env
+    R, C = 64, 64
+    cases = {
+        "zeros": np.zeros((R, C), np.uint16),
+        "one_nonzero": np.where(np.arange(R * C).reshape(R, C) == 777, 0x3F80, 0).astype(np.uint16),
+        "tiny": synth.f32_to_bf16(np.random.default_rng(1).standard_normal((R, C)).astype(np.float32) * 1e-38),
+        "subnormal_bf16": (np.random.default_rng(2).integers(0, 0x80, (R, C)) |
+                           (np.random.default_rng(3).integers(0, 2, (R, C)) << 15)).astype(np.uint16),
+        "huge": synth.f32_to_bf16(np.random.default_rng(4).standard_normal((R, C)).astype(np.float32) * 1e36),
+        "mixed_scale": synth.f32_to_bf16(np.random.default_rng(5).standard_normal((R, C)).astype(np.float32) *
+                                         (10.0 ** np.random.default_rng(6).integers(-30, 30, (R, C))).astype(np.float32)),
+    }
+    for name, xb in cases.items():
+        for grid in (E1M2, INT4, E2M1):
+            for scaling in (NV16, MX32):
+                for rounding in (RTNE, SR):
+                    say(f"[edge] {name} grid={grid} scl={scaling} rnd={rounding}")
+                    fc, oc = cfgs(F, orc, grid, rounding, scaling, 1, rht_seed=4, sr_seed=4)
+                    row, col = gpu_rowcol(env, xb, fc)
+                    assert_layout_equal(row, orc.quantize(xb, oc, ROW), f"{name} row")
+                    assert_layout_equal(col, orc.quantize(xb, oc, COL), f"{name} col")
+
+
+def test_empty_tensor(env):
+    torch, F, orc = env
+    fc, _ = cfgs(F, orc)
+    x = torch.zeros((0, 64), dtype=torch.int16, device="cuda")
+    row = F.alloc_layout(0, 64, NV16)
+    F.ufp4_quantize(x, fc, row, F.Workspace(16, 64))
+    torch.cuda.synchronize()
+    assert row.tensor_scale.item() == 1.0
+
+
+def test_deterministic_repeat(env):
+    torch, F, orc = env
+    xb = synth.output_grad(256, 512, seed=8)
+    fc, _ = cfgs(F, orc, E1M2, SR, NV16, 1, 1, 1)
+    a = gpu_rowcol(env, xb, fc)
+    b = gpu_rowcol(env, xb, fc)
+    for qa, qb in zip(a, b):
+        assert torch.equal(qa.codes, qb.codes) and torch.equal(qa.scales, qb.scales)
+
+
+# ------------------------------------------------------------------ grouped
+def gpu_grouped(env, xb, offsets, fc, row=True, col=True):
+    torch, F, _ = env
+    R, C = xb.shape
+    E = len(offsets) - 1
+    B = 32 if fc.scaling == MX32 else 16
+    coff = F.ufp4_grouped_col_offsets(offsets, B)
+    Rp = int(coff[-1])
+    x = to_dev(torch, xb)
+    off = torch.from_numpy(np.asarray(offsets, np.int64)).cuda()
+    rq = F.alloc_layout(R, C, fc.scaling, E) if row else None
+    cq = F.alloc_layout(C, Rp, fc.scaling, E) if col else None
+    ws = F.Workspace(R, C, E)
+    F.ufp4_quantize_grouped(x, off, Rp, fc, rq, cq, ws)
+    assert ws.status() == 0
+    return rq, cq, coff
+
+
+@pytest.mark.parametrize("scaling", [NV16, MX32])
+@pytest.mark.parametrize("rounding", [RTNE, SR])
+def test_grouped_small(env, scaling, rounding):
+    torch, F, orc = env
+    counts = np.array([0, 5, 16, 37, 1, 130, 0, 23, 64, 200, 3])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    xb = synth.activation(int(offsets[-1]), 320, seed=12)
+    say(f"[grouped] E={len(counts)} rows={offsets[-1]} scl={scaling} rnd={rounding}")
+    fc, oc = cfgs(F, orc, E1M2, rounding, scaling, 1, rht_seed=6, sr_seed=7)
+    rq, cq, coff = gpu_grouped(env, xb, offsets, fc)
+    (rc, rs, rts), (cc, cs, cts), ocoff = orc.quantize_grouped(xb, offsets, oc)
+    np.testing.assert_array_equal(coff, ocoff)
+    assert_layout_equal(rq, (rc, rs, rts), "grouped row")
+    assert_layout_equal(cq, (cc, cs, cts), "grouped col")
+
+
+def test_grouped_single_outputs_and_bad_offsets(env):
+    torch, F, orc = env
+    counts = np.array([17, 0, 48])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    xb = synth.activation(int(offsets[-1]), 64, seed=13)
+    fc, oc = cfgs(F, orc)
+    (rc, rs, rts), (cc, cs, cts), _ = orc.quantize_grouped(xb, offsets, oc)
+    rq, _, _ = gpu_grouped(env, xb, offsets, fc, row=True, col=False)
+    assert_layout_equal(rq, (rc, rs, rts), "row only")
+    _, cq, _ = gpu_grouped(env, xb, offsets, fc, row=False, col=True)
+    assert_layout_equal(cq, (cc, cs, cts), "col only")
+    # non-monotone offsets: the device detects it and writes nothing
+    bad = np.array([0, 40, 20, 65], np.int64)
+    R, C = xb.shape
+    x = to_dev(torch, xb)
+    rqb = F.alloc_layout(R, C, NV16, 3)
+    rqb.codes.fill_(0xAB)
+    ws = F.Workspace(R, C, 3)
+    F.ufp4_quantize_grouped(x, torch.from_numpy(bad).cuda(), 96, fc, rqb, None, ws)
+    assert ws.status() == 6
+    assert bool((rqb.codes == 0xAB).all())
+
+
+# ------------------------------------------------------- dequantize / stats
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+@pytest.mark.parametrize("scaling", [NV16, MX32])
+def test_dequantize_bit_exact(env, grid, scaling):
+    torch, F, orc = env
+    R, C = 128, 256
+    xb = synth.activation(R, C, seed=21)
+    fc, oc = cfgs(F, orc, grid, RTNE, scaling, 1, rht_seed=2)
+    row, col = gpu_rowcol(env, xb, fc)
+    for q, rows, cols in ((row, R, C), (col, C, R)):
+        for inv in (False, True):
+            out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+            F.ufp4_dequantize(q, rows, cols, fc, inv, out)
+            want = orc.dequantize(q.codes.cpu().numpy(), q.scales.cpu().numpy(),
+                                  q.tensor_scale.cpu().numpy(), rows, cols, oc, inverse_rht=inv)
+            np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def assert_stats_close(g, o, floor):
+    for k in ("n", "n_saturated", "n_nonfinite", "n_zero_scale"):
+        assert g[k] == o[k], k
+    assert g["code_hist"] == o["code_hist"]
+    assert g["amax"] == o["amax"]
+    for k in ("sqnr_db", "mean_signed_err", "mean_signed_err_grid", "alpha"):
+        a, b = g[k], o[k]
+        assert abs(a - b) <= 1e-6 * max(abs(a), abs(b)) + floor, (k, a, b)
+
+
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+@pytest.mark.parametrize("layout", [ROW, COL])
+def test_stats_match_oracle(env, grid, layout):
+    torch, F, orc = env
+    R, C = 256, 512
+    xb = synth.weight(R, C, seed=2)
+    fc, oc = cfgs(F, orc, grid, RTNE, NV16, 1, rht_seed=2)
+    row, col = gpu_rowcol(env, xb, fc)
+    q = row if layout == ROW else col
+    g = F.ufp4_stats(to_dev(torch, xb), layout, fc, q, F.Workspace(R, C))
+    o = orc.stats(xb, layout, oc, q.codes.cpu().numpy(), q.scales.cpu().numpy(), q.tensor_scale.cpu().numpy())
+    floor = 1e-6 * float(np.mean(np.abs(synth.bf16_to_f32(xb))))
+    assert_stats_close(g, o, floor)
