@@ -1,0 +1,250 @@
+"""Benchmark: fused RHT + E1M2 row+column quantization of an 8192x2048 bf16
+activation on one MI355X, reported as HBM GB/s (algorithmic bytes / time).
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one ufp4_quantize_rowcol call (every stage of the hot path: load,
+random signs, 16-point Walsh-Hadamard transform, tensor and block maxima,
+E4M3 block scales, E1M2 round-to-nearest-even, nibble packing, row-wise and
+column-wise stores) on one synthetic activation tensor already resident in
+HBM.  Steps rotate over enough input/output buffer sets (>= 600 MB) that the
+256 MB Infinity Cache cannot hold the next step's input.
+
+Algorithmic bytes per call: 2 B/element read (bf16) + 2 x 0.5 B/element codes
++ 2 x 1/16 B/element E4M3 scales + 2 x 4 B tensor scales.
+
+The oracle leg (cpu_baseline) times the single-threaded CPU oracle on the same
+tensor (row-wise and column-wise), a reported baseline only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HBM GB/s (% of peak) fused RHT+E1M2 quant, row+col, 8192×2048 bf16"
+PEAK_GBPS = 8000.0  # MI355X HBM3E
+ROWS, COLS = 8192, 2048
+COUNTERS = os.path.join(ROOT, "profiles", "counters_activation_8192x2048.json")
+CSRC = os.path.join(ROOT, "fp4_quantization_amd", "csrc")
+
+
+def algorithmic_bytes(rows: int, cols: int) -> int:
+    n = rows * cols
+    return 2 * n + 2 * (n // 2) + 2 * (n // 16) + 2 * 4
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return c.get("hbm_bytes_per_call")
+
+
+def time_eager(torch, fns, steps, warmup, stream):
+    """Back-to-back launches from the host (prebuilt ctypes arguments)."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fns[i % len(fns)]()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def time_graph(torch, fns, steps, warmup, stream):
+    """The same K calls captured once in a HIP graph and replayed, so host
+    launch overhead cannot starve the GPU."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    g.replay()  # untimed replay
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, g
+
+
+def cpu_baseline(xb, min_seconds: float = 10.0):
+    import oracle
+
+    cfg = oracle.config(grid=0, rounding=0, scaling=0, rht=1, rht_seed=1)
+    n_calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.quantize(xb, cfg, oracle.LAYOUT_ROW)
+        oracle.quantize(xb, cfg, oracle.LAYOUT_COL)
+        n_calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    per_call = dt / n_calls
+    return {"value": round(algorithmic_bytes(*xb.shape) / per_call / 1e9, 6), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{n_calls} full row+col oracle calls on the same 8192x2048 tensor, "
+                      f"{per_call:.2f} s each, single thread"}
+
+
+def copy_bench(torch, args):
+    """Plain device-to-device copy of 512 MiB (read 512 MiB + write 512 MiB per
+    step): a reference bandwidth, and the known-size kernel that calibrates
+    the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 512 * 1024 * 1024 // 4
+    bufs = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(4)]
+    for b in bufs:
+        b.fill_(1.0)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        bufs[(2 * i + 1) % 4].copy_(bufs[(2 * i) % 4])
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(args.steps):
+        bufs[(2 * i + 1) % 4].copy_(bufs[(2 * i) % 4])
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    print(json.dumps({"copy_bytes_per_step": 2 * n * 4, "ms_per_step": round(ms, 6),
+                      "copy_gbps": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy", action="store_true",
+                    help="time a plain device copy of 512 MiB instead (bandwidth and counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the per-tensor amax exchange a multi-GPU run would need is not built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp4_quantization_amd as F
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import ctypes
+
+    if args.copy:
+        copy_bench(torch, args)
+        return
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)  # default priority
+    torch.cuda.set_stream(stream)
+    xb = synth.activation(ROWS, COLS, seed=1)
+    x0 = torch.from_numpy(xb.view(np.int16)).to(dev)
+    cfg = F.config(F.GRID_E1M2, F.ROUND_RTNE, F.SCALE_NV16, rht=1, rht_seed=1)
+    cfg_off = F.config(F.GRID_E1M2, F.ROUND_RTNE, F.SCALE_NV16, rht=0, rht_seed=1)
+    set_bytes = ROWS * COLS * 2 + algorithmic_bytes(ROWS, COLS)
+    n_sets = max(12, -(-600_000_000 // set_bytes))
+    sets = []
+    for _ in range(n_sets):
+        sets.append((x0.clone(), F.alloc_layout(ROWS, COLS, F.SCALE_NV16, device=dev),
+                     F.alloc_layout(COLS, ROWS, F.SCALE_NV16, device=dev), F.Workspace(ROWS, COLS, device=dev)))
+    torch.cuda.synchronize()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def prebuilt(c):
+        fns = []
+        for x, row, col, ws in sets:
+            a = (ctypes.c_void_p(x.data_ptr()), ROWS, COLS, COLS, ctypes.byref(c), row.c(), col.c(),
+                 ws.ptr, ws.nbytes, sptr)
+
+            def fn(a=a):
+                rc = F.lib.ufp4_quantize_rowcol(*a)
+                if rc:
+                    raise F.Ufp4Error("ufp4_quantize_rowcol", rc)
+            fns.append(fn)
+        return fns
+
+    on, off = prebuilt(cfg), prebuilt(cfg_off)
+    ms, graph = time_graph(torch, on, args.steps, args.warmup, stream)
+    ms_off, _ = time_graph(torch, off, args.steps, args.warmup, stream)
+    ms_eager = time_eager(torch, on, args.steps, args.warmup, stream)
+    ms_warm, _ = time_graph(torch, on[:1], args.steps, args.warmup, stream)
+    # the graph's outputs equal an eager call's
+    x, row, col, ws = sets[0]
+    ref_row, ref_col = row.codes.clone(), col.codes.clone()
+    row.codes.zero_()
+    col.codes.zero_()
+    on[0]()
+    torch.cuda.synchronize()
+    assert torch.equal(ref_row, row.codes) and torch.equal(ref_col, col.codes), "graph replay != eager call"
+
+    nbytes = algorithmic_bytes(ROWS, COLS)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    traffic = counter_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "activation 8192x2048 bf16, N(0,1) + channel bias N(0,0.5), 2 channels x50; "
+                               "RHT (seed 1) + E1M2 RTNE, E4M3 per-16 + FP32 per-tensor scales, row+col",
+                   "rows": ROWS, "cols": COLS, "buffer_sets": n_sets,
+                   "algorithmic_bytes_per_call": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "ufp4_quantize_rowcol call (ufp4_amax_kernel + ufp4_quant_kernel<E1M2,RTNE>)"},
+        "extra": {"elements_per_s": round(ROWS * COLS / (ms * 1e-3), 1),
+                  "rht_off_ms": round(ms_off, 6),
+                  "rht_overhead": round(ms / ms_off - 1.0, 4),
+                  "warm_same_buffer_ms": round(ms_warm, 6),
+                  "warm_same_buffer_gbps": round(nbytes / (ms_warm * 1e-3) / 1e9, 2),
+                  "eager_launch_ms": round(ms_eager, 6),
+                  "timing": "HIP graph of the K calls, one replay, hipEvents on the launch stream"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(xb)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,10 +35,12 @@ size_t quant_ws_bytes(int64_t rows, int64_t cols, int32_t groups) {
 
 size_t stats_ws_bytes() { return kWsHeader + (size_t)kStatsMaxWg * kStatsSlots * sizeof(double); }
 
-int check_qtensor(const ufp4_qtensor& q, int32_t n_ts) {
-  if (!q.codes || !q.scales || !q.tensor_scale) return UFP4_ERR_INVALID_ARGUMENT;
+// An empty output (no elements) may pass null codes/scales; the tensor
+// scale is always written.
+int check_qtensor(const ufp4_qtensor& q, bool empty) {
+  if (!q.tensor_scale) return UFP4_ERR_INVALID_ARGUMENT;
+  if (!empty && (!q.codes || !q.scales)) return UFP4_ERR_INVALID_ARGUMENT;
   if (!aligned(q.codes, 16) || !aligned(q.tensor_scale, 4)) return UFP4_ERR_ALIGNMENT;
-  (void)n_ts;
   return UFP4_OK;
 }
 
@@ -138,7 +140,7 @@ int ufp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, con
   if (rc) return rc;
   if (rows < 0 || cols < 0 || ld < cols) return UFP4_ERR_INVALID_ARGUMENT;
   if (cols % block_of(cfg)) return UFP4_ERR_SHAPE;
-  if ((rc = check_qtensor(row_out, 1))) return rc;
+  if ((rc = check_qtensor(row_out, rows == 0 || cols == 0))) return rc;
   if (rows > 0 && cols > 0) {
     if (!x) return UFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(x, 16) || ld % 8) return UFP4_ERR_ALIGNMENT;
@@ -163,8 +165,8 @@ int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
   if (rows < 0 || cols < 0 || ld < cols) return UFP4_ERR_INVALID_ARGUMENT;
   const int B = block_of(cfg);
   if (cols % B || rows % B) return UFP4_ERR_SHAPE;
-  if ((rc = check_qtensor(row_out, 1))) return rc;
-  if ((rc = check_qtensor(col_out, 1))) return rc;
+  if ((rc = check_qtensor(row_out, rows == 0 || cols == 0))) return rc;
+  if ((rc = check_qtensor(col_out, rows == 0 || cols == 0))) return rc;
   if (rows > 0 && cols > 0) {
     if (!x) return UFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(x, 16) || ld % 8) return UFP4_ERR_ALIGNMENT;
@@ -195,11 +197,12 @@ int ufp4_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
   if (!aligned(offsets_dev, 8)) return UFP4_ERR_ALIGNMENT;
   const int B = block_of(cfg);
   if (cols % B) return UFP4_ERR_SHAPE;
-  const bool do_row = row_out.codes != nullptr, do_col = col_out.codes != nullptr;
+  const bool do_row = row_out.tensor_scale != nullptr, do_col = col_out.tensor_scale != nullptr;
   if (!do_row && !do_col) return UFP4_ERR_INVALID_ARGUMENT;
-  if (do_row && (rc = check_qtensor(row_out, num_groups))) return rc;
+  const bool empty = total_rows == 0 || cols == 0;
+  if (do_row && (rc = check_qtensor(row_out, empty))) return rc;
   if (do_col) {
-    if ((rc = check_qtensor(col_out, num_groups))) return rc;
+    if ((rc = check_qtensor(col_out, empty))) return rc;
     if (padded_rows < total_rows || padded_rows % B ||
         padded_rows > total_rows + (int64_t)(B - 1) * num_groups)
       return UFP4_ERR_SHAPE;

@@ -91,7 +91,8 @@ typedef struct {
   uint64_t sr_seed;
 } ufp4_config;
 
-/* One quantized layout.  All three pointers are device pointers. */
+/* One quantized layout.  All three pointers are device pointers; codes and
+ * scales may be null when the output has no elements. */
 typedef struct {
   uint8_t* codes;      /* packed codes, element 2k in the low nibble of byte k */
   uint8_t* scales;     /* one byte per scale block (E4M3 or E8M0) */
@@ -160,7 +161,7 @@ int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
  * scales[cols][padded_rows/B], segment e occupying positions
  * [col_offsets[e], col_offsets[e+1]).  Row output as ufp4_quantize.
  * row_out.tensor_scale / col_out.tensor_scale hold num_groups floats.  Either
- * output may be skipped by passing a null codes pointer.  If the device finds
+ * output may be skipped by passing a qtensor whose pointers are all null.  If the device finds
  * the offsets inconsistent it writes nothing and ufp4_workspace_status
  * reports UFP4_ERR_OFFSETS. */
 int ufp4_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,

@@ -38,10 +38,11 @@ def f32_to_bf16(f: np.ndarray) -> np.ndarray:
     flat_o = out.reshape(-1)
     step = 1 << 22
     for s in range(0, flat_u.size, step):
-        v = flat_u[s:s + step].astype(np.uint64)
-        r = (v + 0x7FFF + ((v >> 16) & 1)) >> 16
-        nan = (v & 0x7FFFFFFF) > 0x7F800000
-        r = np.where(nan, (v >> 16) | 0x40, r)
+        v = flat_u[s:s + step]
+        nan = (v & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+        # finite patterns stay below 2^32 after adding the rounding bias
+        r = (np.where(nan, np.uint32(0), v) + np.uint32(0x7FFF) + ((v >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+        r = np.where(nan, (v >> np.uint32(16)) | np.uint32(0x40), r)
         flat_o[s:s + step] = r.astype(np.uint16)
     return out
 

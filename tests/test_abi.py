@@ -111,7 +111,8 @@ def test_rowcol_and_grouped_argument_errors(F):
     assert grouped(padded=96) == 2          # fewer than total rows
     assert grouped(padded=120) == 2         # not a multiple of 16
     assert grouped(padded=100 + 15 * 4 + 16) == 2  # more than any segmentation allows
-    assert grouped(row=q(F, codes=0), col=q(F, codes=0)) == 1
+    assert grouped(row=q(F, codes=0, scales=0, ts=0), col=q(F, codes=0, scales=0, ts=0)) == 1
+    assert grouped(row=q(F, codes=0)) == 1
     assert grouped(cols=40) == 2
 
 
