@@ -30,7 +30,7 @@ size_t quant_ws_bytes(int64_t rows, int64_t cols, int32_t groups) {
   const int64_t g16 = grid_size_quant(rows, cols, groups, 16, &nb, &nt);
   const int64_t g32 = grid_size_quant(rows, cols, groups, 32, &nb, &nt);
   const int64_t g = g16 > g32 ? g16 : g32;
-  return kWsHeader + ws_scale_bytes(groups) + (size_t)g * sizeof(float4);
+  return kWsHeader + (size_t)g * sizeof(float2);
 }
 
 size_t stats_ws_bytes() { return kWsHeader + (size_t)kStatsMaxWg * kStatsSlots * sizeof(double); }
@@ -62,9 +62,7 @@ void base_params(QuantParams& p, const uint16_t* x, int64_t rows, int64_t cols, 
   p.sr_k0 = (uint32_t)cfg->sr_seed;
   p.sr_k1 = (uint32_t)(cfg->sr_seed >> 32);
   fill_rht_signs(cfg->rht_seed, p);
-  uint8_t* w = static_cast<uint8_t*>(ws);
-  p.ws_counter = reinterpret_cast<uint32_t*>(w);
-  p.ws_status = reinterpret_cast<uint32_t*>(w + 4);
+  p.ws_status = ws ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + 4) : nullptr;
 }
 
 int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -84,10 +82,10 @@ int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!p.mx) {
     const size_t need = quant_ws_bytes(p.rows, p.cols, p.num_groups);
     if (!ws || ws_bytes < need || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
-    uint8_t* w = static_cast<uint8_t*>(ws);
-    p.ws_scale = reinterpret_cast<float*>(w + kWsHeader);
-    p.ws_part = reinterpret_cast<float4*>(w + kWsHeader + ws_scale_bytes(p.num_groups));
+    p.ws_part = reinterpret_cast<float2*>(static_cast<uint8_t*>(ws) + kWsHeader);
     if (launch_amax(p, grid, stream) != hipSuccess) return UFP4_ERR_HIP;
+  } else if (p.offsets) {
+    if (!ws || ws_bytes < kWsHeader || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
   }
   if (launch_quant(p, grid, stream) != hipSuccess) return UFP4_ERR_HIP;
   return UFP4_OK;

@@ -42,15 +42,13 @@ struct QuantParams {
   int32_t n_tiles;    // row tiles per band (upper bound for grouped)
   int32_t n_work;     // n_band * n_tiles (workgroups beyond this are idle)
   // workspace
-  uint32_t* ws_counter;
-  uint32_t* ws_status;
-  float* ws_scale;    // [E][2]: per-tensor scale S_t (row, col) after phase A
-  float4* ws_part;    // [gridDim.x]: (segment, max|w| row, max|w| col, -)
+  uint32_t* ws_status;  // grouped calls: 0, or UFP4_ERR_OFFSETS
+  float2* ws_part;      // [n_work]: per tile, max |transform| (row-wise, column-wise)
 };
 
-// Workspace layout (bytes).
-constexpr size_t kWsHeader = 256;                 // counter, status
-inline size_t ws_scale_bytes(int32_t groups) { return ((size_t)groups * 2 * sizeof(float) + 255) / 256 * 256; }
+// Workspace layout (bytes): a 256-byte header (status word), then one
+// float2 partial per tile.
+constexpr size_t kWsHeader = 256;
 
 void fill_rht_signs(uint64_t seed, QuantParams& p);
 uint32_t rht_sign_mask(uint64_t seed);

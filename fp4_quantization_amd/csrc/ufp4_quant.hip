@@ -2,16 +2,16 @@
 //
 // Two phases per call (the per-tensor scale makes every code depend on the
 // absolute maximum of the whole transformed tensor):
-//   phase A (ufp4_amax_kernel): load tiles, transform row-wise and
-//     column-wise blocks, keep the largest magnitude; every workgroup writes
-//     a partial, and the last workgroup to finish reduces them per segment
-//     into the per-tensor scales S_t = amax / (Qmax * 448)
-//     ([Z] "Key points": fused RHT+quantization; the two-level NVFP4-style
-//     scale is named there and in [H] technical approach);
-//   phase B (ufp4_quant_kernel): reload the tile, transform again, compute
-//     the block scales, round ([Z] fix / [A] "The UFP4 Recipe": E1M2 or INT4,
-//     SR only where requested) and store packed codes and scales for both
-//     layouts from the same registers.
+//   phase A (ufp4_amax_kernel): load each tile, transform its row-wise and
+//     column-wise blocks and write the tile's largest magnitudes to the
+//     workspace (no atomics, no fences);
+//   phase B (ufp4_quant_kernel): reduce the partials of its segment into the
+//     per-tensor scales S_t = amax / (Qmax * 448), reload the tile, transform
+//     again, compute the block scales, round and store packed codes and
+//     scales for both layouts from the same registers
+//     ([Z] "Key points": fused RHT+quantization, uniform E1M2 grid;
+//     [A] "The UFP4 Recipe": E1M2 or INT4, SR only where requested; the
+//     two-level NVFP4-style scale is named in [H] technical approach).
 //
 // Mapping.  A lane holds a 16-row x 8-column sub-tile (one 16-byte load per
 // row).  Row-wise blocks (16 consecutive columns) span a lane pair: stages of
@@ -28,6 +28,7 @@ namespace ufp4 {
 struct TileInfo {
   bool active;
   bool bad;
+  int32_t work;  // band * n_tiles + row tile: the tile's partial slot
   int32_t band;
   int32_t seg;
   int64_t m0;        // first local row of the tile inside its segment
@@ -58,6 +59,7 @@ __device__ TileInfo tile_info(const QuantParams& p, GroupLds& g) {
   T.bad = false;
   const int32_t w = remap_xcd((int32_t)blockIdx.x, (int32_t)gridDim.x);
   T.active = w < p.n_work;
+  T.work = w;
   T.band = T.active ? w / p.n_tiles : 0;
   const int32_t t = T.active ? w % p.n_tiles : 0;
   if (p.offsets == nullptr) {
@@ -215,33 +217,84 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Max over the 16 outputs of a block from the values before its last
+// butterfly stage: max(|a + q b|, |a - q b|) = fl(|a| + |b|) exactly, since
+// one of the two is a sum of like-signed terms and rounding is monotone.
+__device__ __forceinline__ float lastpair_max(float m, float a, float b) {
+  return fmaxf(m, fabsf(a) + fabsf(b));
+}
+
+// Two's-complement nibbles -> sign-magnitude nibbles, eight at a time: for a
+// negative nibble n (bit 3 set, |n| <= 7) the sign-magnitude code is
+// (n ^ 7) + 1; nonnegative nibbles (and zero) are unchanged.
+__device__ __forceinline__ uint32_t tc_to_signmag8(uint32_t P) {
+  const uint32_t A = P & 0x88888888u;
+  const uint32_t S = A >> 3;
+  return (P ^ (A - S)) + S;
+}
+
+// Shift the low nibble of m in at the top of acc (acc >> 4 | m << 28).
+__device__ __forceinline__ uint32_t push_nibble(uint32_t m, uint32_t acc) {
+  return __builtin_amdgcn_alignbit(m, acc, 4u);
+}
+
+// fl(t + 1.5*2^23) has t rounded to the nearest integer (ties to even) in
+// its low mantissa bits, as a two's-complement value, for |t| < 2^22.
+constexpr float kMagic = 12582912.0f;
+
 // ---------------------------------------------------------------- phase A
 __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
   __shared__ GroupLds g;
   __shared__ float red[2][kThreads / 64];
-  __shared__ uint32_t seg_max[2][kMaxGroups];
-  __shared__ int32_t is_last;
   const TileInfo T = tile_info(p, g);
+  if (!T.active) return;  // uniform per workgroup; its partial slot is never read
+  const LaneGeom L = lane_geom(p, T);
+  uint32_t w[16][4];
+  load_tile(p, T, L, w);
   float acc_r = 0.0f, acc_c = 0.0f;
-  if (T.active) {
-    const LaneGeom L = lane_geom(p, T);
-    uint32_t w[16][4];
-    load_tile(p, T, L, w);
-    if (p.do_row) {
-      const RowLaneSigns rs = row_lane_signs(p, L.lc & 1);
+  if (p.do_row) {
+    const RowLaneSigns rs = row_lane_signs(p, L.lc & 1);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v[8];
-        row_transform(p, w[i], rs, v);
+    for (int i = 0; i < 16; ++i) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = bf_lo(w[i][k]);
+        v[2 * k + 1] = bf_hi(w[i][k]);
+      }
+      if (p.rht) {
+        fwht8_half(v, rs.h);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc_r = lastpair_max(acc_r, v[j], dpp_xor1(v[j]));
+      } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc_r = fmaxf(acc_r, fabsf(v[j]));
       }
     }
-    if (p.do_col) {
+  }
+  if (p.do_col) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        float v[16];
-        col_transform(p, w, k, v);
+    for (int k = 0; k < 8; ++k) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (k & 1) ? bf_hi(w[i][k >> 1]) : bf_lo(w[i][k >> 1]);
+      if (p.rht) {
+        // stages of half-width 1, 2, 4; the last stage folds into the max
+#pragma unroll
+        for (int q = 0; q < 8; ++q) bfly(v[2 * q], v[2 * q + 1], p.sg.q1[q]);
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          bfly(v[4 * gi + 0], v[4 * gi + 2], p.sg.q2[gi]);
+          bfly(v[4 * gi + 1], v[4 * gi + 3], p.sg.q2[gi]);
+        }
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bfly(v[8 * gi + j], v[8 * gi + j + 4], p.sg.q3[gi]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc_c = lastpair_max(acc_c, v[j], v[j + 8]);
+      } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc_c = fmaxf(acc_c, fabsf(v[j]));
       }
@@ -249,134 +302,212 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
   }
   acc_r = wave_max(acc_r);
   acc_c = wave_max(acc_c);
-  const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    red[0][wave] = acc_r;
-    red[1][wave] = acc_c;
+    red[0][threadIdx.x >> 6] = acc_r;
+    red[1][threadIdx.x >> 6] = acc_c;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     float r = red[0][0], c = red[1][0];
+#pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) {
       r = fmaxf(r, red[0][i]);
       c = fmaxf(c, red[1][i]);
     }
-    p.ws_part[blockIdx.x] = make_float4(T.active ? (float)T.seg : -1.0f, r, c, 0.0f);
-    const uint32_t prev =
-        __hip_atomic_fetch_add(p.ws_counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == gridDim.x - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  // Last workgroup: reduce the partials per segment and publish the scales.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int E = p.num_groups;
-  for (int i = threadIdx.x; i < E; i += kThreads) {
-    seg_max[0][i] = 0u;
-    seg_max[1][i] = 0u;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads) {
-    const float4 q = p.ws_part[i];
-    const int e = (int)q.x;
-    if (e >= 0 && e < E) {
-      atomicMax(&seg_max[0][e], __float_as_uint(q.y));  // non-negative: bit order = value order
-      atomicMax(&seg_max[1][e], __float_as_uint(q.z));
-    }
-  }
-  __syncthreads();
-  const float qmax448 = qmax_of(p.grid) * 448.0f;
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-#pragma unroll
-    for (int l = 0; l < 2; ++l) {
-      float a = __uint_as_float(seg_max[l][e]);
-      if (p.rht) a = a * 0.25f;  // max of the scaled values (monotone rounding)
-      const float S = (a > 0.0f) ? a / qmax448 : 1.0f;
-      p.ws_scale[2 * e + l] = S;
-      if (l == 0 && p.do_row && p.row_ts && !T.bad) p.row_ts[e] = S;
-      if (l == 1 && p.do_col && p.col_ts && !T.bad) p.col_ts[e] = S;
-    }
-  }
-  if (threadIdx.x == 0) {
-    *p.ws_status = T.bad ? 6u : 0u;
-    __hip_atomic_store(p.ws_counter, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    p.ws_part[T.work] = make_float2(r, c);
   }
 }
 
 // ---------------------------------------------------------------- phase B
-template <int GRID, bool SR>
+// Per-tensor quantities of one layout of the workgroup's segment.
+struct TensorScale {
+  float S;      // S_t
+  float D;      // fl(Qmax * S_t)
+  float R;      // fl(1 / D), for the bracketed block-scale estimate
+  bool fast;    // D normal and finite, amax small enough that 0.25*inv_b is exact
+};
+
+// raw = max |transform before the 1/4| over the tensor (or max |x| without
+// the transform).  S_t = amax / (Qmax * 448), 1 for an all-zero tensor.
+__device__ __forceinline__ TensorScale make_tensor_scale(float raw, bool rht, float qmax) {
+  TensorScale ts;
+  const float a = rht ? raw * 0.25f : raw;  // max of the scaled values (rounding is monotone)
+  ts.S = (a > 0.0f) ? a / (qmax * 448.0f) : 1.0f;
+  ts.D = qmax * ts.S;
+  ts.R = 1.0f / ts.D;
+  ts.fast = ts.D >= 0x1p-126f && ts.D <= 0x1p+127f && a < 0x1p+119f;
+  return ts;
+}
+
+// Block scale (NV16): s_b = E4M3(fl(amax_b / D)), saturated.  fl(amax_b * R)
+// is within 3 ulp of amax_b / D, so when both ends of a +-2^-21 bracket around
+// it encode to the same E4M3 code, that code is exact (E4M3 rounding is
+// monotone); otherwise, or when the per-tensor quantities are extreme, the
+// correctly rounded division decides.
+__device__ __forceinline__ uint32_t nv_block_code(float amax_b, const TensorScale& ts) {
+  if (ts.fast) {
+    const float q = amax_b * ts.R;
+    const float lo = fminf(q * 0x1.fffffp-1f, 448.0f);   // q (1 - 2^-21)
+    const float hi = fminf(q * 0x1.000004p+0f, 448.0f);  // q (1 + 2^-21)
+    const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false);
+    if ((pk & 0xFFu) == ((pk >> 8) & 0xFFu)) return pk & 0xFFu;
+  }
+  return e4m3_encode_sat(amax_b / ts.D);
+}
+
+template <int GRID, bool SR, bool MX>
 __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
   __shared__ GroupLds g;
   __shared__ float lut[2][128];
+  __shared__ float red[2][kThreads / 64];
   const TileInfo T = tile_info(p, g);
-  if (p.mx && blockIdx.x == 0 && (p.offsets == nullptr || !T.bad)) {
-    for (int e = threadIdx.x; e < p.num_groups; e += kThreads) {
-      if (p.do_row && p.row_ts) p.row_ts[e] = 1.0f;
-      if (p.do_col && p.col_ts) p.col_ts[e] = 1.0f;
+  if (blockIdx.x == 0) {
+    // tensor scales nobody else writes: MX32 (always 1) and empty segments
+    if (p.offsets && p.ws_status && threadIdx.x == 0) *p.ws_status = T.bad ? 6u : 0u;
+    if (p.offsets == nullptr || !T.bad) {
+      for (int e = threadIdx.x; e < p.num_groups; e += kThreads) {
+        const bool empty = p.offsets != nullptr && g.off[e + 1] == g.off[e];
+        if (MX || empty) {
+          if (p.do_row && p.row_ts) p.row_ts[e] = 1.0f;
+          if (p.do_col && p.col_ts) p.col_ts[e] = 1.0f;
+        }
+      }
     }
   }
   if (!T.active) return;  // uniform per workgroup
-  const float qmax = grid_qmax<GRID>();
-  float D[2] = {0.0f, 0.0f};
-  if (!p.mx) {
-    const float S0 = p.ws_scale[2 * T.seg + 0], S1 = p.ws_scale[2 * T.seg + 1];
-    D[0] = qmax * S0;
-    D[1] = qmax * S1;
-    const int t = threadIdx.x;
-    const int l = t >> 7, c = t & 127;
-    const float S = l ? S1 : S0;
-    // inverse dequantization factor of every E4M3 block-scale code
-    const float d = (c == 127) ? 0.0f : e4m3_decode_pos((uint32_t)c) * S;
-    lut[l][c] = (d == 0.0f) ? 0.0f : 1.0f / d;
-    __syncthreads();
-  }
   const LaneGeom L = lane_geom(p, T);
   uint32_t w[16][4];
   load_tile(p, T, L, w);
+  constexpr float qmax = GRID == kGridE1M2 ? 3.5f : (GRID == kGridINT4 ? 7.0f : 6.0f);
+  TensorScale tsr{1.0f, qmax, 1.0f / qmax, false}, tsc = tsr;
+  if (!MX) {
+    // per-tensor maximum of the segment from the phase-A partials
+    float r = 0.0f, c = 0.0f;
+    const int64_t t0 = p.offsets ? g.tpre[T.seg] : 0;
+    const int64_t nt = p.offsets ? g.tpre[T.seg + 1] - g.tpre[T.seg] : p.n_tiles;
+    const int64_t cnt = nt * p.n_band;
+    for (int64_t i = threadIdx.x; i < cnt; i += kThreads) {
+      const int64_t b = i / nt, t = t0 + i % nt;
+      const float2 q = p.ws_part[b * p.n_tiles + t];
+      r = fmaxf(r, q.x);
+      c = fmaxf(c, q.y);
+    }
+    r = wave_max(r);
+    c = wave_max(c);
+    if ((threadIdx.x & 63) == 0) {
+      red[0][threadIdx.x >> 6] = r;
+      red[1][threadIdx.x >> 6] = c;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) {
+      r = fmaxf(r, red[0][i]);
+      c = fmaxf(c, red[1][i]);
+    }
+    tsr = make_tensor_scale(r, p.rht != 0, qmax);
+    tsc = make_tensor_scale(c, p.rht != 0, qmax);
+    {
+      const int t = threadIdx.x, l = t >> 7, cc = t & 127;
+      const float S = l ? tsc.S : tsr.S;
+      const float d = (cc == 127) ? 0.0f : e4m3_decode_pos((uint32_t)cc) * S;
+      lut[l][cc] = (d == 0.0f) ? 0.0f : 1.0f / d;  // inverse dequantization factor per code
+    }
+    if (threadIdx.x == 0 && T.band == 0 && T.m0 == 0) {
+      if (p.do_row && p.row_ts) p.row_ts[T.seg] = tsr.S;
+      if (p.do_col && p.col_ts) p.col_ts[T.seg] = tsc.S;
+    }
+    __syncthreads();
+  }
+
+  // unpack the sub-tile once; both layouts read it
+  float xf[16][8];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      xf[i][2 * k] = bf_lo(w[i][k]);
+      xf[i][2 * k + 1] = bf_hi(w[i][k]);
+    }
+  }
   const int parity = L.lc & 1;
   const RowLaneSigns rs = row_lane_signs(p, parity);
-  const float fin_r = rs.fin;
-  const float fin_c = p.rht ? p.sg.fin : 1.0f;
   const int64_t C = p.cols;
+  // RTNE onto E1M2/INT4 has an exact fast form (see fast_codes8); it needs no
+  // clamp when the block scale is a normal E4M3 value (|y| <= 1.0625 Qmax).
+  constexpr bool kFastGrid = !SR && (GRID == kGridE1M2 || GRID == kGridINT4);
+  constexpr float kGridMul = GRID == kGridE1M2 ? 2.0f : 1.0f;  // grid step -> integer
 
   if (p.do_row) {
 #pragma clang loop unroll(full)
     for (int i = 0; i < 16; ++i) {
       float v[8];
-      row_transform(p, w[i], rs, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = xf[i][j];
+      if (p.rht) {
+        fwht8_half(v, rs.h);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = fmaf(dpp_xor1(v[j]), rs.s4, v[j]);
+      }
+      // v = transform / fin (fin = the lane's sign and the 1/4)
       float m = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v[j] = v[j] * fin_r;
-        m = fmaxf(m, fabsf(v[j]));
-      }
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
       m = fmaxf(m, dpp_xor1(m));
-      if (p.mx) m = fmaxf(m, dpp_xor2(m));
+      if (MX) m = fmaxf(m, dpp_xor2(m));
+      const float amax_b = p.rht ? m * 0.25f : m;
       uint32_t sbyte;
       float inv;
-      if (p.mx) {
-        mx_scale<GRID>(m, sbyte, inv);
+      if (MX) {
+        mx_scale<GRID>(amax_b, sbyte, inv);
       } else {
-        sbyte = e4m3_encode_sat(m / D[0]);
+        sbyte = nv_block_code(amax_b, tsr);
         inv = lut[0][sbyte];
       }
       const int64_t grow = T.seg_row0 + L.m_h0 + i;
+      const bool real = L.lane_ok && L.m_h0 + i < T.M;
       uint32_t packed = 0u;
-      if (SR) {
-        const uint64_t base = (uint64_t)grow * (uint64_t)C + (uint64_t)L.c0;
-        const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
-        const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
-        packed = quantize_code<GRID, true>(v[0] * inv, r0.x) | (quantize_code<GRID, true>(v[1] * inv, r0.y) << 4) |
-                 (quantize_code<GRID, true>(v[2] * inv, r0.z) << 8) | (quantize_code<GRID, true>(v[3] * inv, r0.w) << 12) |
-                 (quantize_code<GRID, true>(v[4] * inv, r1.x) << 16) | (quantize_code<GRID, true>(v[5] * inv, r1.y) << 20) |
-                 (quantize_code<GRID, true>(v[6] * inv, r1.z) << 24) | (quantize_code<GRID, true>(v[7] * inv, r1.w) << 28);
-      } else {
+      bool done = false;
+      if (kFastGrid) {
+        const bool ok = !real || amax_b == 0.0f ||
+                        (amax_b >= 0x1p-100f && (MX || sbyte >= 8u) && (MX || tsr.fast));
+        if (__all(ok)) {
+          // t = y * (grid step)^-1 computed as one product: exact scalings by
+          // powers of two of the two-step fl(fl(v * 1/4) * inv_b) for every
+          // element whose code can be nonzero (see the design notes)
+          const float mult = inv * (rs.fin * kGridMul);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) packed |= quantize_code<GRID, false>(v[j] * inv, 0u) << (4 * j);
+          for (int j = 0; j < 8; ++j) {
+            float t = v[j] * mult;
+            if (MX) t = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
+            packed = push_nibble(__float_as_uint(t + kMagic), packed);
+          }
+          if (GRID == kGridE1M2) packed = tc_to_signmag8(packed);
+          done = true;
+        }
       }
-      if (L.lane_ok && L.m_h0 + i < T.M) {
+      if (!done) {
+        if (SR) {
+          const uint64_t base = (uint64_t)grow * (uint64_t)C + (uint64_t)L.c0;
+          const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
+          const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
+          const float f = rs.fin;
+          packed = quantize_code<GRID, SR>((v[0] * f) * inv, r0.x) |
+                   (quantize_code<GRID, SR>((v[1] * f) * inv, r0.y) << 4) |
+                   (quantize_code<GRID, SR>((v[2] * f) * inv, r0.z) << 8) |
+                   (quantize_code<GRID, SR>((v[3] * f) * inv, r0.w) << 12) |
+                   (quantize_code<GRID, SR>((v[4] * f) * inv, r1.x) << 16) |
+                   (quantize_code<GRID, SR>((v[5] * f) * inv, r1.y) << 20) |
+                   (quantize_code<GRID, SR>((v[6] * f) * inv, r1.z) << 24) |
+                   (quantize_code<GRID, SR>((v[7] * f) * inv, r1.w) << 28);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            packed |= quantize_code<GRID, false>((v[j] * rs.fin) * inv, 0u) << (4 * j);
+        }
+      }
+      if (real) {
         *reinterpret_cast<uint32_t*>(p.row_codes + grow * (C / 2) + L.c0 / 2) = packed;
-        if (p.mx) {
+        if (MX) {
           if ((L.lc & 3) == 0) p.row_scales[grow * (C / 32) + L.c0 / 32] = (uint8_t)sbyte;
         } else if (parity == 0) {
           p.row_scales[grow * (C / 16) + L.c0 / 16] = (uint8_t)sbyte;
@@ -389,49 +520,77 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     const bool blk_ok = L.m_h0 < T.P;  // this half's 16-row block exists
     const int64_t Rp = p.padded_rows;
     const int64_t pos0 = T.coff + L.m_h0;  // column-wise position of the block start
+    const float fin = p.rht ? p.sg.fin : 1.0f;
 #pragma clang loop unroll(full)
     for (int k = 0; k < 8; ++k) {
       float v[16];
-      col_transform(p, w, k, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = xf[i][k];
+      if (p.rht) fwht16_inlane(v, p.sg);
       float m = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        v[j] = v[j] * fin_c;
-        m = fmaxf(m, fabsf(v[j]));
-      }
-      if (p.mx) m = fmaxf(m, __shfl_xor(m, 32));
+      for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
+      if (MX) m = fmaxf(m, __shfl_xor(m, 32));
+      const float amax_b = p.rht ? m * 0.25f : m;
       uint32_t sbyte;
       float inv;
-      if (p.mx) {
-        mx_scale<GRID>(m, sbyte, inv);
+      if (MX) {
+        mx_scale<GRID>(amax_b, sbyte, inv);
       } else {
-        sbyte = e4m3_encode_sat(m / D[1]);
+        sbyte = nv_block_code(amax_b, tsc);
         inv = lut[1][sbyte];
       }
       const int64_t c = L.c0 + k;
       uint32_t lo = 0u, hi = 0u;
-      if (SR) {
-        const uint64_t base = (uint64_t)c * (uint64_t)Rp + (uint64_t)pos0;
-        uint32_t word[4];
+      bool done = false;
+      if (kFastGrid) {
+        const bool ok = !(L.lane_ok && blk_ok) || amax_b == 0.0f ||
+                        (amax_b >= 0x1p-100f && (MX || sbyte >= 8u) && (MX || tsc.fast));
+        if (__all(ok)) {
+          const float mult = inv * (fin * kGridMul);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const Ctr4 r = sr_words4((base >> 2) + q, 1u, p.sr_k0, p.sr_k1);
-          word[q] = quantize_code<GRID, true>(v[4 * q + 0] * inv, r.x) |
-                    (quantize_code<GRID, true>(v[4 * q + 1] * inv, r.y) << 4) |
-                    (quantize_code<GRID, true>(v[4 * q + 2] * inv, r.z) << 8) |
-                    (quantize_code<GRID, true>(v[4 * q + 3] * inv, r.w) << 12);
+          for (int j = 0; j < 8; ++j) {
+            float t = v[j] * mult;
+            if (MX) t = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
+            lo = push_nibble(__float_as_uint(t + kMagic), lo);
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float t = v[8 + j] * mult;
+            if (MX) t = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
+            hi = push_nibble(__float_as_uint(t + kMagic), hi);
+          }
+          if (GRID == kGridE1M2) {
+            lo = tc_to_signmag8(lo);
+            hi = tc_to_signmag8(hi);
+          }
+          done = true;
         }
-        lo = word[0] | (word[1] << 16);
-        hi = word[2] | (word[3] << 16);
-      } else {
+      }
+      if (!done) {
+        if (SR) {
+          const uint64_t base = (uint64_t)c * (uint64_t)Rp + (uint64_t)pos0;
+          uint32_t word[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) lo |= quantize_code<GRID, false>(v[j] * inv, 0u) << (4 * j);
+          for (int q = 0; q < 4; ++q) {
+            const Ctr4 r = sr_words4((base >> 2) + q, 1u, p.sr_k0, p.sr_k1);
+            word[q] = quantize_code<GRID, SR>((v[4 * q + 0] * fin) * inv, r.x) |
+                      (quantize_code<GRID, SR>((v[4 * q + 1] * fin) * inv, r.y) << 4) |
+                      (quantize_code<GRID, SR>((v[4 * q + 2] * fin) * inv, r.z) << 8) |
+                      (quantize_code<GRID, SR>((v[4 * q + 3] * fin) * inv, r.w) << 12);
+          }
+          lo = word[0] | (word[1] << 16);
+          hi = word[2] | (word[3] << 16);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) hi |= quantize_code<GRID, false>(v[8 + j] * inv, 0u) << (4 * j);
+          for (int j = 0; j < 8; ++j) lo |= quantize_code<GRID, false>((v[j] * fin) * inv, 0u) << (4 * j);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) hi |= quantize_code<GRID, false>((v[8 + j] * fin) * inv, 0u) << (4 * j);
+        }
       }
       if (L.lane_ok && blk_ok) {
         *reinterpret_cast<uint2*>(p.col_codes + c * (Rp / 2) + pos0 / 2) = make_uint2(lo, hi);
-        if (p.mx) {
+        if (MX) {
           if (L.half == 0) p.col_scales[c * (Rp / 32) + pos0 / 32] = (uint8_t)sbyte;
         } else {
           p.col_scales[c * (Rp / 16) + pos0 / 16] = (uint8_t)sbyte;
@@ -508,21 +667,26 @@ hipError_t launch_amax(const QuantParams& p, int64_t grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int GRID>
+template <int GRID, bool MX>
 static hipError_t launch_quant_grid(const QuantParams& p, int64_t grid, bool sr, hipStream_t s) {
   if (sr)
-    hipLaunchKernelGGL((ufp4_quant_kernel<GRID, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((ufp4_quant_kernel<GRID, true, MX>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((ufp4_quant_kernel<GRID, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((ufp4_quant_kernel<GRID, false, MX>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
+}
+
+template <int GRID>
+static hipError_t launch_quant_mx(const QuantParams& p, int64_t grid, bool sr, hipStream_t s) {
+  return p.mx ? launch_quant_grid<GRID, true>(p, grid, sr, s) : launch_quant_grid<GRID, false>(p, grid, sr, s);
 }
 
 hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s) {
   const bool sr = p.sr != 0;
   switch (p.grid) {
-    case kGridE1M2: return launch_quant_grid<kGridE1M2>(p, grid, sr, s);
-    case kGridINT4: return launch_quant_grid<kGridINT4>(p, grid, sr, s);
-    case kGridE2M1: return launch_quant_grid<kGridE2M1>(p, grid, sr, s);
+    case kGridE1M2: return launch_quant_mx<kGridE1M2>(p, grid, sr, s);
+    case kGridINT4: return launch_quant_mx<kGridINT4>(p, grid, sr, s);
+    case kGridE2M1: return launch_quant_mx<kGridE2M1>(p, grid, sr, s);
     default: return hipErrorInvalidValue;
   }
 }
