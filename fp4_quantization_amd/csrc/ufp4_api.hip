@@ -11,6 +11,7 @@ using namespace ufp4;
 namespace {
 
 constexpr int kStatsMaxWg = 1024;
+constexpr int64_t kMaxDim = (int64_t)1 << 25;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -66,6 +67,8 @@ void base_params(QuantParams& p, const uint16_t* x, int64_t rows, int64_t cols, 
 }
 
 int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  // per-lane output offsets inside a tile are 32-bit
+  if (p.cols >= kMaxDim || p.padded_rows >= kMaxDim) return UFP4_ERR_SHAPE;
   if (p.rows == 0 || p.cols == 0) {
     // nothing to quantize: every per-tensor scale is 1 (a zero tensor)
     if (p.do_row && p.row_ts &&

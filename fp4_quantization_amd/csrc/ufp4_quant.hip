@@ -149,20 +149,35 @@ __device__ __forceinline__ LaneGeom lane_geom(const QuantParams& p, const TileIn
   return L;
 }
 
-// Load the lane's 16 x 8 sub-tile (zeros outside the segment / tensor).
+// Load the lane's 16 x 8 sub-tile (zeros outside the segment / tensor).  The
+// loads are unconditional and in row order, so consumers that walk the rows
+// in order start before the last row arrives; lanes or rows outside the data
+// read an in-bounds address and are zeroed.
 __device__ __forceinline__ void load_tile(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
                                           uint32_t w[16][4]) {
+  const int64_t rows_left = T.M - L.m_h0;
+  const bool full = L.lane_ok && rows_left >= 16;
+  if (__all(full)) {
+    const uint16_t* ptr = p.x + (T.seg_row0 + L.m_h0) * p.ld + L.c0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t m = L.m_h0 + i;
-    if (L.lane_ok && m < T.M) {
-      const uint4 v = *reinterpret_cast<const uint4*>(p.x + (T.seg_row0 + m) * p.ld + L.c0);
+    for (int i = 0; i < 16; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(ptr + (int64_t)i * p.ld);
       w[i][0] = v.x;
       w[i][1] = v.y;
       w[i][2] = v.z;
       w[i][3] = v.w;
-    } else {
-      w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
+    }
+  } else {
+    const int64_t c = L.lane_ok ? L.c0 : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = L.lane_ok && i < rows_left;
+      const int64_t m = ok ? L.m_h0 + i : 0;  // row 0 of an active segment exists
+      const uint4 v = *reinterpret_cast<const uint4*>(p.x + (T.seg_row0 + m) * p.ld + c);
+      w[i][0] = ok ? v.x : 0u;
+      w[i][1] = ok ? v.y : 0u;
+      w[i][2] = ok ? v.z : 0u;
+      w[i][3] = ok ? v.w : 0u;
     }
   }
 }
@@ -175,16 +190,23 @@ struct RowLaneSigns {
   float fin;  // output multiplier (0.25 d0, and -q4 on odd lanes)
 };
 
+__device__ __forceinline__ float lane_select(float even, float odd, float oddf) {
+  // even + (odd - even) * oddf with oddf in {0, 1}: exact for the +-1 / +-0.25
+  // values involved, and computed from uniform (scalar) operands, so no
+  // per-lane address into the kernel arguments is ever formed
+  return fmaf(odd - even, oddf, even);
+}
+
 __device__ __forceinline__ RowLaneSigns row_lane_signs(const QuantParams& p, int parity) {
   RowLaneSigns r;
-  const bool odd = parity != 0;
+  const float oddf = (float)parity;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) r.h.q1[k] = odd ? p.hs[1].q1[k] : p.hs[0].q1[k];
+  for (int k = 0; k < 4; ++k) r.h.q1[k] = lane_select(p.hs[0].q1[k], p.hs[1].q1[k], oddf);
 #pragma unroll
-  for (int k = 0; k < 2; ++k) r.h.q2[k] = odd ? p.hs[1].q2[k] : p.hs[0].q2[k];
-  r.h.q3 = odd ? p.hs[1].q3 : p.hs[0].q3;
-  r.s4 = odd ? p.s4[1] : p.s4[0];
-  r.fin = p.rht ? (odd ? p.fin_lane[1] : p.fin_lane[0]) : 1.0f;
+  for (int k = 0; k < 2; ++k) r.h.q2[k] = lane_select(p.hs[0].q2[k], p.hs[1].q2[k], oddf);
+  r.h.q3 = lane_select(p.hs[0].q3, p.hs[1].q3, oddf);
+  r.s4 = lane_select(p.s4[0], p.s4[1], oddf);
+  r.fin = p.rht ? lane_select(p.fin_lane[0], p.fin_lane[1], oddf) : 1.0f;
   return r;
 }
 
@@ -254,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
   float acc_r = 0.0f, acc_c = 0.0f;
   if (p.do_row) {
     const RowLaneSigns rs = row_lane_signs(p, L.lc & 1);
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int i = 0; i < 16; ++i) {
       float v[8];
 #pragma unroll
@@ -273,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
     }
   }
   if (p.do_col) {
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int k = 0; k < 8; ++k) {
       float v[16];
 #pragma unroll
@@ -355,11 +377,20 @@ __device__ __forceinline__ uint32_t nv_block_code(float amax_b, const TensorScal
   return e4m3_encode_sat(amax_b / ts.D);
 }
 
+// Staging of a tile's column-wise output: [chunk][column] with chunk = the
+// 16-row block of one half-wavefront (8 per 128-row tile).  One padding
+// entry per chunk row spreads the write-out reads over the LDS banks.
+struct ColStage {
+  uint2 codes[8][kBandCols + 1];
+  uint8_t scales[8][kBandCols + 4];
+};
+
 template <int GRID, bool SR, bool MX>
 __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
   __shared__ GroupLds g;
   __shared__ float lut[2][128];
   __shared__ float red[2][kThreads / 64];
+  __shared__ ColStage cst;
   const TileInfo T = tile_info(p, g);
   if (blockIdx.x == 0) {
     // tensor scales nobody else writes: MX32 (always 1) and empty segments
@@ -376,17 +407,32 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
   }
   if (!T.active) return;  // uniform per workgroup
   const LaneGeom L = lane_geom(p, T);
-  uint32_t w[16][4];
-  load_tile(p, T, L, w);
   constexpr float qmax = GRID == kGridE1M2 ? 3.5f : (GRID == kGridINT4 ? 7.0f : 6.0f);
   TensorScale tsr{1.0f, qmax, 1.0f / qmax, false}, tsc = tsr;
+  // Phase-A partials of the segment: the first 4 per thread are requested
+  // before the tile, so their latency overlaps the tile loads.
+  const int64_t t0 = p.offsets ? g.tpre[T.seg] : 0;
+  const int64_t nt = p.offsets ? g.tpre[T.seg + 1] - g.tpre[T.seg] : p.n_tiles;
+  const int64_t cnt = MX ? 0 : nt * p.n_band;
+  float2 pre[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t i = threadIdx.x + q * kThreads;
+    const int64_t j = i < cnt ? i : 0;
+    const int64_t b = j / nt, t = t0 + j % nt;
+    pre[q] = (i < cnt) ? p.ws_part[b * p.n_tiles + t] : make_float2(0.0f, 0.0f);
+  }
+  uint32_t w[16][4];
+  load_tile(p, T, L, w);
   if (!MX) {
     // per-tensor maximum of the segment from the phase-A partials
     float r = 0.0f, c = 0.0f;
-    const int64_t t0 = p.offsets ? g.tpre[T.seg] : 0;
-    const int64_t nt = p.offsets ? g.tpre[T.seg + 1] - g.tpre[T.seg] : p.n_tiles;
-    const int64_t cnt = nt * p.n_band;
-    for (int64_t i = threadIdx.x; i < cnt; i += kThreads) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      r = fmaxf(r, pre[q].x);
+      c = fmaxf(c, pre[q].y);
+    }
+    for (int64_t i = threadIdx.x + 4 * kThreads; i < cnt; i += kThreads) {
       const int64_t b = i / nt, t = t0 + i % nt;
       const float2 q = p.ws_part[b * p.n_tiles + t];
       r = fmaxf(r, q.x);
@@ -419,183 +465,242 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     __syncthreads();
   }
 
-  // unpack the sub-tile once; both layouts read it
+  // The sub-tile is unpacked once (row by row, in load order, inside the
+  // row-wise pass) and kept for the column-wise pass.
   float xf[16][8];
+  if (!p.do_row) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 16; ++i) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      xf[i][2 * k] = bf_lo(w[i][k]);
-      xf[i][2 * k + 1] = bf_hi(w[i][k]);
+      for (int k = 0; k < 4; ++k) {
+        xf[i][2 * k] = bf_lo(w[i][k]);
+        xf[i][2 * k + 1] = bf_hi(w[i][k]);
+      }
     }
   }
   const int parity = L.lc & 1;
   const RowLaneSigns rs = row_lane_signs(p, parity);
   const int64_t C = p.cols;
-  // RTNE onto E1M2/INT4 has an exact fast form (see fast_codes8); it needs no
-  // clamp when the block scale is a normal E4M3 value (|y| <= 1.0625 Qmax).
+  // RTNE onto E1M2/INT4 has an exact fast form; it needs no clamp when the
+  // block scale is a normal E4M3 value (then |y| <= 1.0625 Qmax).
   constexpr bool kFastGrid = !SR && (GRID == kGridE1M2 || GRID == kGridINT4);
   constexpr float kGridMul = GRID == kGridE1M2 ? 2.0f : 1.0f;  // grid step -> integer
+  // Addresses: a uniform tile base plus a 32-bit per-lane offset.
+  const int64_t tile_row0 = T.seg_row0 + T.m0;
+  const uint32_t lrow = (uint32_t)(32 * L.wave + 16 * L.half);  // lane's first row in the tile
 
   if (p.do_row) {
+    const int B = MX ? 32 : 16;
+    uint8_t* rc_base = p.row_codes + tile_row0 * (C / 2) + (int64_t)T.band * (kBandCols / 2);
+    uint8_t* rsc_base = p.row_scales + tile_row0 * (C / B) + (int64_t)T.band * (kBandCols / B);
+    const uint32_t rc_stride = (uint32_t)(C / 2), rsc_stride = (uint32_t)(C / B);
 #pragma clang loop unroll(full)
-    for (int i = 0; i < 16; ++i) {
-      float v[8];
+    for (int g4 = 0; g4 < 4; ++g4) {
+      // four independent row blocks per step: transform, scale, vote, round
+      float v[4][8];
+      float amax_b[4], inv[4];
+      uint32_t sbyte[4];
+      bool ok = true;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = xf[i][j];
-      if (p.rht) {
-        fwht8_half(v, rs.h);
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g4 + r;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = fmaf(dpp_xor1(v[j]), rs.s4, v[j]);
+        for (int k = 0; k < 4; ++k) {
+          xf[i][2 * k] = bf_lo(w[i][k]);
+          xf[i][2 * k + 1] = bf_hi(w[i][k]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[r][j] = xf[i][j];
+        if (p.rht) {
+          fwht8_half(v[r], rs.h);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[r][j] = fmaf(dpp_xor1(v[r][j]), rs.s4, v[r][j]);
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[r][j]));
+        m = fmaxf(m, dpp_xor1(m));
+        if (MX) m = fmaxf(m, dpp_xor2(m));
+        amax_b[r] = p.rht ? m * 0.25f : m;
+        if (MX) {
+          mx_scale<GRID>(amax_b[r], sbyte[r], inv[r]);
+        } else {
+          sbyte[r] = nv_block_code(amax_b[r], tsr);
+          inv[r] = lut[0][sbyte[r]];
+        }
+        const bool real = L.lane_ok && L.m_h0 + i < T.M;
+        ok = ok && (!real || amax_b[r] == 0.0f ||
+                    (amax_b[r] >= 0x1p-100f && (MX || (sbyte[r] >= 8u && tsr.fast))));
       }
-      // v = transform / fin (fin = the lane's sign and the 1/4)
-      float m = 0.0f;
+      uint32_t packed[4] = {0u, 0u, 0u, 0u};
+      if (kFastGrid && __all(ok)) {
+        // t = y / (grid step) as one product: an exact power-of-two rescaling
+        // of fl(fl(v/4) * inv_b) for every element whose code can be nonzero
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-      m = fmaxf(m, dpp_xor1(m));
-      if (MX) m = fmaxf(m, dpp_xor2(m));
-      const float amax_b = p.rht ? m * 0.25f : m;
-      uint32_t sbyte;
-      float inv;
-      if (MX) {
-        mx_scale<GRID>(amax_b, sbyte, inv);
-      } else {
-        sbyte = nv_block_code(amax_b, tsr);
-        inv = lut[0][sbyte];
-      }
-      const int64_t grow = T.seg_row0 + L.m_h0 + i;
-      const bool real = L.lane_ok && L.m_h0 + i < T.M;
-      uint32_t packed = 0u;
-      bool done = false;
-      if (kFastGrid) {
-        const bool ok = !real || amax_b == 0.0f ||
-                        (amax_b >= 0x1p-100f && (MX || sbyte >= 8u) && (MX || tsr.fast));
-        if (__all(ok)) {
-          // t = y * (grid step)^-1 computed as one product: exact scalings by
-          // powers of two of the two-step fl(fl(v * 1/4) * inv_b) for every
-          // element whose code can be nonzero (see the design notes)
-          const float mult = inv * (rs.fin * kGridMul);
+        for (int r = 0; r < 4; ++r) {
+          const float mult = inv[r] * (rs.fin * kGridMul);
+          uint32_t acc = 0u;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            float t = v[j] * mult;
+            float t = v[r][j] * mult;
             if (MX) t = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
-            packed = push_nibble(__float_as_uint(t + kMagic), packed);
+            acc = push_nibble(__float_as_uint(t + kMagic), acc);
           }
-          if (GRID == kGridE1M2) packed = tc_to_signmag8(packed);
-          done = true;
+          packed[r] = GRID == kGridE1M2 ? tc_to_signmag8(acc) : acc;
         }
-      }
-      if (!done) {
-        if (SR) {
-          const uint64_t base = (uint64_t)grow * (uint64_t)C + (uint64_t)L.c0;
-          const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
-          const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
-          const float f = rs.fin;
-          packed = quantize_code<GRID, SR>((v[0] * f) * inv, r0.x) |
-                   (quantize_code<GRID, SR>((v[1] * f) * inv, r0.y) << 4) |
-                   (quantize_code<GRID, SR>((v[2] * f) * inv, r0.z) << 8) |
-                   (quantize_code<GRID, SR>((v[3] * f) * inv, r0.w) << 12) |
-                   (quantize_code<GRID, SR>((v[4] * f) * inv, r1.x) << 16) |
-                   (quantize_code<GRID, SR>((v[5] * f) * inv, r1.y) << 20) |
-                   (quantize_code<GRID, SR>((v[6] * f) * inv, r1.z) << 24) |
-                   (quantize_code<GRID, SR>((v[7] * f) * inv, r1.w) << 28);
-        } else {
+      } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            packed |= quantize_code<GRID, false>((v[j] * rs.fin) * inv, 0u) << (4 * j);
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * g4 + r;
+          const float f = rs.fin;
+          if (SR) {
+            const uint64_t base = (uint64_t)(T.seg_row0 + L.m_h0 + i) * (uint64_t)C + (uint64_t)L.c0;
+            const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
+            const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
+            packed[r] = quantize_code<GRID, SR>((v[r][0] * f) * inv[r], r0.x) |
+                        (quantize_code<GRID, SR>((v[r][1] * f) * inv[r], r0.y) << 4) |
+                        (quantize_code<GRID, SR>((v[r][2] * f) * inv[r], r0.z) << 8) |
+                        (quantize_code<GRID, SR>((v[r][3] * f) * inv[r], r0.w) << 12) |
+                        (quantize_code<GRID, SR>((v[r][4] * f) * inv[r], r1.x) << 16) |
+                        (quantize_code<GRID, SR>((v[r][5] * f) * inv[r], r1.y) << 20) |
+                        (quantize_code<GRID, SR>((v[r][6] * f) * inv[r], r1.z) << 24) |
+                        (quantize_code<GRID, SR>((v[r][7] * f) * inv[r], r1.w) << 28);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              packed[r] |= quantize_code<GRID, false>((v[r][j] * f) * inv[r], 0u) << (4 * j);
+          }
         }
       }
-      if (real) {
-        *reinterpret_cast<uint32_t*>(p.row_codes + grow * (C / 2) + L.c0 / 2) = packed;
-        if (MX) {
-          if ((L.lc & 3) == 0) p.row_scales[grow * (C / 32) + L.c0 / 32] = (uint8_t)sbyte;
-        } else if (parity == 0) {
-          p.row_scales[grow * (C / 16) + L.c0 / 16] = (uint8_t)sbyte;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g4 + r;
+        if (L.lane_ok && L.m_h0 + i < T.M) {
+          const uint32_t li = lrow + (uint32_t)i;
+          *reinterpret_cast<uint32_t*>(rc_base + (li * rc_stride + 4u * (uint32_t)L.lc)) = packed[r];
+          if (MX) {
+            if ((L.lc & 3) == 0) rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 2)] = (uint8_t)sbyte[r];
+          } else if (parity == 0) {
+            rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 1)] = (uint8_t)sbyte[r];
+          }
         }
       }
     }
   }
 
   if (p.do_col) {
+    // Column-wise blocks: codes and scales go to LDS first (chunk = one
+    // half-wavefront's 16 rows), then leave as contiguous 8-byte code runs
+    // and byte runs per output line, instead of one scattered store per
+    // lane and column.
     const bool blk_ok = L.m_h0 < T.P;  // this half's 16-row block exists
-    const int64_t Rp = p.padded_rows;
-    const int64_t pos0 = T.coff + L.m_h0;  // column-wise position of the block start
     const float fin = p.rht ? p.sg.fin : 1.0f;
+    const int ch = 2 * L.wave + L.half;  // chunk of this half-wavefront
 #pragma clang loop unroll(full)
-    for (int k = 0; k < 8; ++k) {
-      float v[16];
+    for (int g2 = 0; g2 < 4; ++g2) {
+      // two independent column blocks per step
+      float v[2][16];
+      float amax_b[2], inv[2];
+      uint32_t sbyte[2];
+      bool ok = true;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = xf[i][k];
-      if (p.rht) fwht16_inlane(v, p.sg);
-      float m = 0.0f;
+      for (int r = 0; r < 2; ++r) {
+        const int k = 2 * g2 + r;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
-      if (MX) m = fmaxf(m, __shfl_xor(m, 32));
-      const float amax_b = p.rht ? m * 0.25f : m;
-      uint32_t sbyte;
-      float inv;
-      if (MX) {
-        mx_scale<GRID>(amax_b, sbyte, inv);
-      } else {
-        sbyte = nv_block_code(amax_b, tsc);
-        inv = lut[1][sbyte];
-      }
-      const int64_t c = L.c0 + k;
-      uint32_t lo = 0u, hi = 0u;
-      bool done = false;
-      if (kFastGrid) {
-        const bool ok = !(L.lane_ok && blk_ok) || amax_b == 0.0f ||
-                        (amax_b >= 0x1p-100f && (MX || sbyte >= 8u) && (MX || tsc.fast));
-        if (__all(ok)) {
-          const float mult = inv * (fin * kGridMul);
+        for (int i = 0; i < 16; ++i) v[r][i] = xf[i][k];
+        if (p.rht) fwht16_inlane(v[r], p.sg);
+        float m = 0.0f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float t = v[j] * mult;
-            if (MX) t = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
-            lo = push_nibble(__float_as_uint(t + kMagic), lo);
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float t = v[8 + j] * mult;
-            if (MX) t = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
-            hi = push_nibble(__float_as_uint(t + kMagic), hi);
-          }
-          if (GRID == kGridE1M2) {
-            lo = tc_to_signmag8(lo);
-            hi = tc_to_signmag8(hi);
-          }
-          done = true;
-        }
-      }
-      if (!done) {
-        if (SR) {
-          const uint64_t base = (uint64_t)c * (uint64_t)Rp + (uint64_t)pos0;
-          uint32_t word[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const Ctr4 r = sr_words4((base >> 2) + q, 1u, p.sr_k0, p.sr_k1);
-            word[q] = quantize_code<GRID, SR>((v[4 * q + 0] * fin) * inv, r.x) |
-                      (quantize_code<GRID, SR>((v[4 * q + 1] * fin) * inv, r.y) << 4) |
-                      (quantize_code<GRID, SR>((v[4 * q + 2] * fin) * inv, r.z) << 8) |
-                      (quantize_code<GRID, SR>((v[4 * q + 3] * fin) * inv, r.w) << 12);
-          }
-          lo = word[0] | (word[1] << 16);
-          hi = word[2] | (word[3] << 16);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) lo |= quantize_code<GRID, false>((v[j] * fin) * inv, 0u) << (4 * j);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) hi |= quantize_code<GRID, false>((v[8 + j] * fin) * inv, 0u) << (4 * j);
-        }
-      }
-      if (L.lane_ok && blk_ok) {
-        *reinterpret_cast<uint2*>(p.col_codes + c * (Rp / 2) + pos0 / 2) = make_uint2(lo, hi);
+        for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[r][j]));
+        if (MX) m = fmaxf(m, __shfl_xor(m, 32));
+        amax_b[r] = p.rht ? m * 0.25f : m;
         if (MX) {
-          if (L.half == 0) p.col_scales[c * (Rp / 32) + pos0 / 32] = (uint8_t)sbyte;
+          mx_scale<GRID>(amax_b[r], sbyte[r], inv[r]);
         } else {
-          p.col_scales[c * (Rp / 16) + pos0 / 16] = (uint8_t)sbyte;
+          sbyte[r] = nv_block_code(amax_b[r], tsc);
+          inv[r] = lut[1][sbyte[r]];
+        }
+        ok = ok && (!(L.lane_ok && blk_ok) || amax_b[r] == 0.0f ||
+                    (amax_b[r] >= 0x1p-100f && (MX || (sbyte[r] >= 8u && tsc.fast))));
+      }
+      uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+      if (kFastGrid && __all(ok)) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const float mult = inv[r] * (fin * kGridMul);
+          uint32_t a0 = 0u, a1 = 0u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float t0 = v[r][j] * mult, t1 = v[r][8 + j] * mult;
+            if (MX) {
+              t0 = __builtin_amdgcn_fmed3f(t0, -7.0f, 7.0f);
+              t1 = __builtin_amdgcn_fmed3f(t1, -7.0f, 7.0f);
+            }
+            a0 = push_nibble(__float_as_uint(t0 + kMagic), a0);
+            a1 = push_nibble(__float_as_uint(t1 + kMagic), a1);
+          }
+          lo[r] = GRID == kGridE1M2 ? tc_to_signmag8(a0) : a0;
+          hi[r] = GRID == kGridE1M2 ? tc_to_signmag8(a1) : a1;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          if (SR) {
+            const int64_t cglob = L.c0 + 2 * g2 + r;
+            const uint64_t base =
+                (uint64_t)cglob * (uint64_t)p.padded_rows + (uint64_t)(T.coff + L.m_h0);
+            uint32_t word[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const Ctr4 rr = sr_words4((base >> 2) + q, 1u, p.sr_k0, p.sr_k1);
+              word[q] = quantize_code<GRID, SR>((v[r][4 * q + 0] * fin) * inv[r], rr.x) |
+                        (quantize_code<GRID, SR>((v[r][4 * q + 1] * fin) * inv[r], rr.y) << 4) |
+                        (quantize_code<GRID, SR>((v[r][4 * q + 2] * fin) * inv[r], rr.z) << 8) |
+                        (quantize_code<GRID, SR>((v[r][4 * q + 3] * fin) * inv[r], rr.w) << 12);
+            }
+            lo[r] = word[0] | (word[1] << 16);
+            hi[r] = word[2] | (word[3] << 16);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              lo[r] |= quantize_code<GRID, false>((v[r][j] * fin) * inv[r], 0u) << (4 * j);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              hi[r] |= quantize_code<GRID, false>((v[r][8 + j] * fin) * inv[r], 0u) << (4 * j);
+          }
         }
       }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int col = 8 * L.lc + 2 * g2 + r;  // column within the band
+        cst.codes[ch][col] = make_uint2(lo[r], hi[r]);
+        cst.scales[ch][col] = (uint8_t)sbyte[r];
+      }
+    }
+    __syncthreads();
+    // write-out: 8 threads per output line (column), one 8-byte code run each
+    const int64_t Rp = p.padded_rows;
+    const int B = MX ? 32 : 16;
+    const int64_t band_c0 = (int64_t)T.band * kBandCols;
+    const int64_t ncols = p.cols - band_c0 < kBandCols ? p.cols - band_c0 : kBandCols;
+    const int64_t rows_here = T.P - T.m0;
+    const int nch = rows_here >= kTileRows ? 8 : (int)(rows_here / 16);  // chunks that exist
+    uint8_t* cc = p.col_codes + band_c0 * (Rp / 2) + (T.coff + T.m0) / 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = threadIdx.x + j * kThreads;
+      const int col = q >> 3, chq = q & 7;
+      if (col < ncols && chq < nch)
+        *reinterpret_cast<uint2*>(cc + (int64_t)col * (Rp / 2) + 8 * chq) = cst.codes[chq][col];
+    }
+    uint8_t* cs = p.col_scales + band_c0 * (Rp / B) + (T.coff + T.m0) / B;
+    const int nsc = MX ? nch / 2 : nch;  // scale bytes per line in this tile
+    const int per = MX ? 4 : 8;
+#pragma unroll
+    for (int j = 0; j < (MX ? 4 : 8); ++j) {
+      const int q = threadIdx.x + j * kThreads;
+      const int col = q / per, b = q % per;
+      if (col < ncols && b < nsc) cs[(int64_t)col * (Rp / B) + b] = cst.scales[MX ? 2 * b : b][col];
     }
   }
 }

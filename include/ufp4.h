@@ -45,6 +45,8 @@
  *     Nothing throws across the ABI.
  *   - Results are deterministic for fixed inputs and configuration.
  *   - Calls that share one workspace must not run concurrently.
+ *   - Quantization calls accept cols < 2^25 and rows < 2^25 (UFP4_ERR_SHAPE
+ *     otherwise).
  */
 #ifndef UFP4_H
 #define UFP4_H
