@@ -1,7 +1,7 @@
 """Benchmark: fused RHT + E1M2 row+column quantization of an 8192x2048 bf16
 activation on one MI355X, reported as HBM GB/s (algorithmic bytes / time).
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--warm] [--copy]
 
 A step is one ufp4_quantize_rowcol call (every stage of the hot path: load,
 random signs, 16-point Walsh-Hadamard transform, tensor and block maxima,
@@ -12,6 +12,13 @@ HBM.  Steps rotate over enough input/output buffer sets (>= 600 MB) that the
 
 Algorithmic bytes per call: 2 B/element read (bf16) + 2 x 0.5 B/element codes
 + 2 x 1/16 B/element E4M3 scales + 2 x 4 B tensor scales.
+
+A call runs two kernels: the tensor-maximum pass (reads the input) and the
+quantization pass (reads the input again and writes every output).  The
+roofline object describes the quantization kernel, the dominant one: its
+algorithmic bytes per launch are the call's (input once, all outputs), and its
+duration is the mean of hipEvent intervals recorded on the launch stream
+around that kernel alone, over calls that rotate through the buffer sets.
 
 The oracle leg (cpu_baseline) times the single-threaded CPU oracle on the same
 tensor (row-wise and column-wise), a reported baseline only.
@@ -49,16 +56,86 @@ def kernel_source_sha() -> str:
 
 
 def counter_traffic():
-    """HBM bytes per call from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    """HBM bytes per launch of the quantization kernel and per call, from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel
+    sources; else (None, None)."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if c.get("kernel_source_sha256") != kernel_source_sha():
-        return None
-    return c.get("hbm_bytes_per_call")
+        return None, None
+    return c.get("hbm_bytes_quant_kernel"), c.get("hbm_bytes_per_call")
+
+
+AMAX_KERNEL = "ufp4_amax_kernel<true>"
+QUANT_KERNEL = "ufp4_quant_kernel<0, false, false, true>"
+
+
+def _counter_means(csv_dir, counter):
+    """Mean counter value (KiB) per dispatch, by kernel name, from a rocprofv3
+    --pmc CSV directory; also the largest-grid copyBuffer dispatches'."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {csv_dir}")
+    sums, copies = {}, {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name, v = r["Kernel_Name"], float(r["Counter_Value"])
+                if "copyBuffer" in name:
+                    copies.setdefault(int(r["Grid_Size"]), []).append(v)
+                else:
+                    sums.setdefault(name, []).append(v)
+    means = {k: sum(v) / len(v) for k, v in sums.items()}
+    copy_mean = None
+    if copies:
+        big = copies[max(copies)]
+        copy_mean = sum(big) / len(big)
+    return means, copy_mean
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+    """Write the counter summary bench.py reads: HBM bytes per launch of the
+    quantization kernel and per call, each counter scaled by what it reads
+    for a plain 512 MiB device copy."""
+    fetch, _ = _counter_means(fetch_dir, "FETCH_SIZE")
+    write, _ = _counter_means(write_dir, "WRITE_SIZE")
+    _, copy_fetch = _counter_means(copy_fetch_dir, "FETCH_SIZE")
+    _, copy_write = _counter_means(copy_write_dir, "WRITE_SIZE")
+    copy_kib = 512 * 1024
+    ff, wf = copy_kib / copy_fetch, copy_kib / copy_write
+
+    def pick(d, key):
+        hits = [k for k in d if key in k]
+        if len(hits) != 1:
+            raise SystemExit(f"kernel {key!r}: found {hits}")
+        return hits[0], d[hits[0]]
+
+    ka, fa = pick(fetch, AMAX_KERNEL)
+    kq, fq = pick(fetch, QUANT_KERNEL)
+    _, wa = pick(write, AMAX_KERNEL)
+    _, wq = pick(write, QUANT_KERNEL)
+    quant = (fq * ff + wq * wf) * 1024
+    call = quant + (fa * ff + wa * wf) * 1024
+    out = {"fetch_kib_raw": {ka: fa, kq: fq}, "write_kib_raw": {ka: wa, kq: wq},
+           "copy_calibration": {"copy_bytes": copy_kib * 1024, "fetch_kib_raw": copy_fetch,
+                                "write_kib_raw": copy_write, "fetch_factor": ff, "write_factor": wf},
+           "hbm_bytes_quant_kernel": round(quant), "hbm_bytes_per_call": round(call),
+           "algorithmic_bytes_per_call": algorithmic_bytes(ROWS, COLS),
+           "kernel_source_sha256": kernel_source_sha(), "commands": commands,
+           "note": "KiB per dispatch, mean over dispatches; bytes = (fetch * fetch_factor + "
+                   "write * write_factor) * 1024; FETCH_SIZE counts traffic beyond L2 (HBM and "
+                   "Infinity Cache)"}
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def time_eager(torch, fns, steps, warmup, stream):
@@ -99,22 +176,32 @@ def time_graph(torch, fns, steps, warmup, stream):
 
 
 def cpu_baseline(xb, min_seconds: float = 10.0):
+    """The oracle (single-threaded C) on the whole tensor, row-wise then
+    column-wise, repeated for at least min_seconds, on one host core."""
     import oracle
 
-    cfg = oracle.config(grid=0, rounding=0, scaling=0, rht=1, rht_seed=1)
-    n_calls, t0 = 0, time.perf_counter()
-    while True:
-        oracle.quantize(xb, cfg, oracle.LAYOUT_ROW)
-        oracle.quantize(xb, cfg, oracle.LAYOUT_COL)
-        n_calls += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
+    oracle.lib()  # build/load before timing
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        cfg = oracle.config(grid=0, rounding=0, scaling=0, rht=1, rht_seed=1)
+        n_calls, t0 = 0, time.perf_counter()
+        while True:
+            oracle.quantize(xb, cfg, oracle.LAYOUT_ROW)
+            oracle.quantize(xb, cfg, oracle.LAYOUT_COL)
+            n_calls += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    finally:
+        os.sched_setaffinity(0, allowed)
     per_call = dt / n_calls
     return {"value": round(algorithmic_bytes(*xb.shape) / per_call / 1e9, 6), "unit": "GB/s",
             "cores": 1, "kind": "oracle",
             "sample": f"{n_calls} full row+col oracle calls on the same 8192x2048 tensor, "
-                      f"{per_call:.2f} s each, single thread"}
+                      f"{per_call:.3f} s each, one thread pinned to host core {core} "
+                      f"of {os.cpu_count()}"}
 
 
 def copy_bench(torch, args):
@@ -146,9 +233,28 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time repeated calls on one buffer set (input cache-resident)")
     ap.add_argument("--copy", action="store_true",
                     help="time a plain device copy of 512 MiB instead (bandwidth and counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                              "COPY_WRITE_DIR"),
+                    help="write the counter summary from four rocprofv3 --pmc output directories "
+                         "(this run, FETCH_SIZE then WRITE_SIZE; --copy run, the same) and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        d = args.summarize_counters
+        summarize_counters(*d, commands=[
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[0]} -o run -- "
+            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[1]} -o run -- "
+            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[2]} -o run -- "
+            "python3 bench.py --copy --steps 5 --warmup 2",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[3]} -o run -- "
+            "python3 bench.py --copy --steps 5 --warmup 2",
+            f"python3 bench.py --summarize-counters {' '.join(d)}"])
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the per-tensor amax exchange a multi-GPU run would need is not built", file=sys.stderr)
@@ -200,7 +306,15 @@ def main():
     ms, graph = time_graph(torch, on, args.steps, args.warmup, stream)
     ms_off, _ = time_graph(torch, off, args.steps, args.warmup, stream)
     ms_eager = time_eager(torch, on, args.steps, args.warmup, stream)
-    ms_warm, _ = time_graph(torch, on[:1], args.steps, args.warmup, stream)
+    ms_warm = time_graph(torch, on[:1], args.steps, args.warmup, stream)[0] if args.warm else None
+    # per-kernel durations: hipEvents around each kernel of one call, on the
+    # launch stream, over calls that rotate through the buffer sets
+    per_kernel = []
+    for i in range(args.steps):
+        x, row, col, ws = sets[i % len(sets)]
+        per_kernel.append(F.ufp4_time_rowcol(x, cfg, row, col, ws, stream))
+    k_amax = np.array([a for a, _ in per_kernel])
+    k_quant = np.array([b for _, b in per_kernel])
     # the graph's outputs equal an eager call's
     x, row, col, ws = sets[0]
     ref_row, ref_col = row.codes.clone(), col.codes.clone()
@@ -212,7 +326,8 @@ def main():
 
     nbytes = algorithmic_bytes(ROWS, COLS)
     gbps = nbytes / (ms * 1e-3) / 1e9
-    traffic = counter_traffic()
+    traffic_quant, traffic_call = counter_traffic()
+    quant_gbps = nbytes / (float(k_quant.mean()) * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -230,17 +345,26 @@ def main():
                                "RHT (seed 1) + E1M2 RTNE, E4M3 per-16 + FP32 per-tensor scales, row+col",
                    "rows": ROWS, "cols": COLS, "buffer_sets": n_sets,
                    "algorithmic_bytes_per_call": nbytes},
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "ufp4_quantize_rowcol call (ufp4_amax_kernel + ufp4_quant_kernel<E1M2,RTNE>)"},
+        "roofline": {"bound": "hbm", "achieved": round(quant_gbps, 2), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(quant_gbps / PEAK_GBPS, 4), "traffic": traffic_quant,
+                     "kernel": "ufp4_quant_kernel<E1M2, RTNE, NV16, RHT>",
+                     "bytes_per_launch": nbytes,
+                     "kernel_ms_mean": round(float(k_quant.mean()), 6)},
         "extra": {"elements_per_s": round(ROWS * COLS / (ms * 1e-3), 1),
+                  "call_frac_of_peak": round(gbps / PEAK_GBPS, 4),
+                  "call_hbm_bytes_counted": traffic_call,
+                  "amax_kernel_ms_mean": round(float(k_amax.mean()), 6),
+                  "amax_kernel_ms_median": round(float(np.median(k_amax)), 6),
+                  "quant_kernel_ms_median": round(float(np.median(k_quant)), 6),
+                  "event_call_ms_median": round(float(np.median(k_amax + k_quant)), 6),
                   "rht_off_ms": round(ms_off, 6),
                   "rht_overhead": round(ms / ms_off - 1.0, 4),
-                  "warm_same_buffer_ms": round(ms_warm, 6),
-                  "warm_same_buffer_gbps": round(nbytes / (ms_warm * 1e-3) / 1e9, 2),
                   "eager_launch_ms": round(ms_eager, 6),
                   "timing": "HIP graph of the K calls, one replay, hipEvents on the launch stream"},
     }
+    if ms_warm is not None:
+        line["extra"]["warm_same_buffer_ms"] = round(ms_warm, 6)
+        line["extra"]["warm_same_buffer_gbps"] = round(nbytes / (ms_warm * 1e-3) / 1e9, 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(xb)
     print(json.dumps(line), flush=True)

@@ -19,7 +19,7 @@ from ._lib import (GRID_E1M2, GRID_E2M1, GRID_INT4, LIB_PATH, ROUND_RTNE, ROUND_
 __all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "ROUND_RTNE", "ROUND_STOCHASTIC", "SCALE_NV16",
            "SCALE_MX32", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
            "ufp4_quantize", "ufp4_quantize_rowcol", "ufp4_quantize_grouped", "ufp4_dequantize",
-           "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets",
+           "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol",
            "block_len"]
 
 
@@ -121,6 +121,19 @@ def ufp4_quantize_grouped(x: torch.Tensor, offsets_dev: torch.Tensor, padded_row
                                     ctypes.byref(cfg), row_out.c() if row_out else null,
                                     col_out.c() if col_out else null, ws.ptr if ws else None,
                                     ws.nbytes if ws else 0, _stream(stream)))
+
+
+def ufp4_time_rowcol(x: torch.Tensor, cfg: ufp4_config, row_out: QTensor, col_out: QTensor,
+                     ws: Workspace, stream=None) -> tuple[float, float]:
+    """One ufp4_quantize_rowcol call with hipEvents around each of its two
+    kernels; returns (ms of the tensor-maximum kernel, ms of the quantization
+    kernel).  Synchronizes."""
+    rows, cols, ld = _bf16_view(x)
+    a, b = ctypes.c_float(0), ctypes.c_float(0)
+    check("ufp4_time_rowcol", lib.ufp4_time_rowcol(_ptr(x), rows, cols, ld, ctypes.byref(cfg), row_out.c(),
+                                                   col_out.c(), ws.ptr, ws.nbytes, _stream(stream),
+                                                   ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
 
 
 def ufp4_dequantize(q: QTensor, rows: int, cols: int, cfg: ufp4_config, inverse_rht: bool,

@@ -24,7 +24,7 @@ SCALE_NV16, SCALE_MX32 = 0, 1
 EXPORTED = ["ufp4_status_string", "ufp4_workspace_size", "ufp4_workspace_init",
             "ufp4_workspace_status", "ufp4_quantize", "ufp4_quantize_rowcol",
             "ufp4_quantize_grouped", "ufp4_dequantize", "ufp4_stats", "ufp4_round_f32",
-            "ufp4_rht_signs", "ufp4_grouped_col_offsets"]
+            "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol"]
 
 
 class Ufp4Error(RuntimeError):
@@ -85,6 +85,9 @@ def _load():
                              ctypes.POINTER(ufp4_stats_t), P]
     L.ufp4_round_f32.restype = ctypes.c_int
     L.ufp4_round_f32.argtypes = [P, i64, i32, i32, u64, P, P]
+    L.ufp4_time_rowcol.restype = ctypes.c_int
+    L.ufp4_time_rowcol.argtypes = [P, i64, i64, i64, cfgp, ufp4_qtensor, ufp4_qtensor, P, sz, P,
+                                   ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]
     L.ufp4_rht_signs.restype = ctypes.c_int
     L.ufp4_rht_signs.argtypes = [u64, P]
     L.ufp4_grouped_col_offsets.restype = ctypes.c_int

@@ -66,7 +66,12 @@ void base_params(QuantParams& p, const uint16_t* x, int64_t rows, int64_t cols, 
   p.ws_status = ws ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + 4) : nullptr;
 }
 
-int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream) {
+// Start and end events of the two kernels of one call.
+struct KernelTimer {
+  hipEvent_t ev[4];
+};
+
+int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream, KernelTimer* tm = nullptr) {
   // per-lane output offsets inside a tile are 32-bit
   if (p.cols >= kMaxDim || p.padded_rows >= kMaxDim) return UFP4_ERR_SHAPE;
   if (p.rows == 0 || p.cols == 0) {
@@ -86,11 +91,13 @@ int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream) {
     const size_t need = quant_ws_bytes(p.rows, p.cols, p.num_groups);
     if (!ws || ws_bytes < need || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
     p.ws_part = reinterpret_cast<float2*>(static_cast<uint8_t*>(ws) + kWsHeader);
-    if (launch_amax(p, grid, stream) != hipSuccess) return UFP4_ERR_HIP;
+    if (launch_amax(p, grid, stream, tm ? tm->ev[0] : nullptr, tm ? tm->ev[1] : nullptr) != hipSuccess)
+      return UFP4_ERR_HIP;
   } else if (p.offsets) {
     if (!ws || ws_bytes < kWsHeader || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
   }
-  if (launch_quant(p, grid, stream) != hipSuccess) return UFP4_ERR_HIP;
+  if (launch_quant(p, grid, stream, tm ? tm->ev[2] : nullptr, tm ? tm->ev[3] : nullptr) != hipSuccess)
+    return UFP4_ERR_HIP;
   return UFP4_OK;
 }
 
@@ -158,9 +165,9 @@ int ufp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, con
   return run_quant(p, ws, ws_bytes, (hipStream_t)stream);
 }
 
-int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
-                         const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws,
-                         size_t ws_bytes, ufp4_stream_t stream) {
+static int rowcol_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const ufp4_config* cfg,
+                       ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws, size_t ws_bytes,
+                       ufp4_stream_t stream, KernelTimer* tm) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (rows < 0 || cols < 0 || ld < cols) return UFP4_ERR_INVALID_ARGUMENT;
@@ -184,7 +191,36 @@ int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
   p.col_ts = col_out.tensor_scale;
   if (rows == 0 || cols == 0) p.rows = p.cols = 0;
   p.padded_rows = p.rows;
-  return run_quant(p, ws, ws_bytes, (hipStream_t)stream);
+  return run_quant(p, ws, ws_bytes, (hipStream_t)stream, tm);
+}
+
+int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                         const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws,
+                         size_t ws_bytes, ufp4_stream_t stream) {
+  return rowcol_impl(x, rows, cols, ld, cfg, row_out, col_out, ws, ws_bytes, stream, nullptr);
+}
+
+int ufp4_time_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const ufp4_config* cfg,
+                     ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws, size_t ws_bytes,
+                     ufp4_stream_t stream, float* ms_amax_host, float* ms_quant_host) {
+  if (!ms_amax_host || !ms_quant_host || !cfg || cfg->scaling != UFP4_SCALE_NV16 || rows <= 0 || cols <= 0)
+    return UFP4_ERR_INVALID_ARGUMENT;
+  KernelTimer tm;
+  int made = 0, rc = UFP4_OK;
+  for (; made < 4; ++made)
+    if (hipEventCreate(&tm.ev[made]) != hipSuccess) {
+      rc = UFP4_ERR_HIP;
+      break;
+    }
+  if (rc == UFP4_OK) rc = rowcol_impl(x, rows, cols, ld, cfg, row_out, col_out, ws, ws_bytes, stream, &tm);
+  if (rc == UFP4_OK) {
+    if (hipEventSynchronize(tm.ev[3]) != hipSuccess ||
+        hipEventElapsedTime(ms_amax_host, tm.ev[0], tm.ev[1]) != hipSuccess ||
+        hipEventElapsedTime(ms_quant_host, tm.ev[2], tm.ev[3]) != hipSuccess)
+      rc = UFP4_ERR_HIP;
+  }
+  for (int i = 0; i < made; ++i) (void)hipEventDestroy(tm.ev[i]);
+  return rc;
 }
 
 int ufp4_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,

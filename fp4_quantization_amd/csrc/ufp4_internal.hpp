@@ -56,8 +56,11 @@ uint32_t rht_sign_mask(uint64_t seed);
 int64_t grid_size_quant(int64_t rows, int64_t cols, int32_t groups, int32_t block, int32_t* n_band,
                         int32_t* n_tiles);
 
-hipError_t launch_amax(const QuantParams& p, int64_t grid, hipStream_t s);
-hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s);
+// With non-null events the kernel's start and end are recorded in them.
+hipError_t launch_amax(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0 = nullptr,
+                       hipEvent_t t1 = nullptr);
+hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0 = nullptr,
+                        hipEvent_t t1 = nullptr);
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
 
 struct DequantParams {

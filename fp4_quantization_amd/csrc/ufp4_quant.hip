@@ -21,6 +21,8 @@
 // registers feed both layouts.  Workgroups are remapped so that the ones
 // dispatched to one XCD (round-robin over 8) walk down one column band, so
 // the transposed outputs they write share L2 lines.
+#include <hip/hip_ext.h>
+
 #include "ufp4_internal.hpp"
 
 namespace ufp4 {
@@ -197,6 +199,7 @@ __device__ __forceinline__ float lane_select(float even, float odd, float oddf) 
   return fmaf(odd - even, oddf, even);
 }
 
+template <bool RHT>
 __device__ __forceinline__ RowLaneSigns row_lane_signs(const QuantParams& p, int parity) {
   RowLaneSigns r;
   const float oddf = (float)parity;
@@ -206,31 +209,8 @@ __device__ __forceinline__ RowLaneSigns row_lane_signs(const QuantParams& p, int
   for (int k = 0; k < 2; ++k) r.h.q2[k] = lane_select(p.hs[0].q2[k], p.hs[1].q2[k], oddf);
   r.h.q3 = lane_select(p.hs[0].q3, p.hs[1].q3, oddf);
   r.s4 = lane_select(p.s4[0], p.s4[1], oddf);
-  r.fin = p.rht ? lane_select(p.fin_lane[0], p.fin_lane[1], oddf) : 1.0f;
+  r.fin = RHT ? lane_select(p.fin_lane[0], p.fin_lane[1], oddf) : 1.0f;
   return r;
-}
-
-// Row-wise transform of one row of the sub-tile: the lane's 8 values of the
-// block's transform, before the lane's output multiplier.
-__device__ __forceinline__ void row_transform(const QuantParams& p, const uint32_t wi[4],
-                                              const RowLaneSigns& rs, float v[8]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    v[2 * k] = bf_lo(wi[k]);
-    v[2 * k + 1] = bf_hi(wi[k]);
-  }
-  if (p.rht) {
-    fwht8_half(v, rs.h);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = fmaf(dpp_xor1(v[j]), rs.s4, v[j]);
-  }
-}
-
-__device__ __forceinline__ void col_transform(const QuantParams& p, const uint32_t w[16][4], int k,
-                                              float v[16]) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = (k & 1) ? bf_hi(w[i][k >> 1]) : bf_lo(w[i][k >> 1]);
-  if (p.rht) fwht16_inlane(v, p.sg);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -265,6 +245,7 @@ __device__ __forceinline__ uint32_t push_nibble(uint32_t m, uint32_t acc) {
 constexpr float kMagic = 12582912.0f;
 
 // ---------------------------------------------------------------- phase A
+template <bool RHT>
 __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
   __shared__ GroupLds g;
   __shared__ float red[2][kThreads / 64];
@@ -275,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
   load_tile(p, T, L, w);
   float acc_r = 0.0f, acc_c = 0.0f;
   if (p.do_row) {
-    const RowLaneSigns rs = row_lane_signs(p, L.lc & 1);
+    const RowLaneSigns rs = row_lane_signs<RHT>(p, L.lc & 1);
 #pragma clang loop unroll(full)
     for (int i = 0; i < 16; ++i) {
       float v[8];
@@ -284,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
         v[2 * k] = bf_lo(w[i][k]);
         v[2 * k + 1] = bf_hi(w[i][k]);
       }
-      if (p.rht) {
+      if (RHT) {
         fwht8_half(v, rs.h);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc_r = lastpair_max(acc_r, v[j], dpp_xor1(v[j]));
@@ -300,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
       float v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = (k & 1) ? bf_hi(w[i][k >> 1]) : bf_lo(w[i][k >> 1]);
-      if (p.rht) {
+      if (RHT) {
         // stages of half-width 1, 2, 4; the last stage folds into the max
 #pragma unroll
         for (int q = 0; q < 8; ++q) bfly(v[2 * q], v[2 * q + 1], p.sg.q1[q]);
@@ -385,7 +366,7 @@ struct ColStage {
   uint8_t scales[8][kBandCols + 4];
 };
 
-template <int GRID, bool SR, bool MX>
+template <int GRID, bool SR, bool MX, bool RHT>
 __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
   __shared__ GroupLds g;
   __shared__ float lut[2][128];
@@ -450,8 +431,8 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
       r = fmaxf(r, red[0][i]);
       c = fmaxf(c, red[1][i]);
     }
-    tsr = make_tensor_scale(r, p.rht != 0, qmax);
-    tsc = make_tensor_scale(c, p.rht != 0, qmax);
+    tsr = make_tensor_scale(r, RHT, qmax);
+    tsc = make_tensor_scale(c, RHT, qmax);
     {
       const int t = threadIdx.x, l = t >> 7, cc = t & 127;
       const float S = l ? tsc.S : tsr.S;
@@ -479,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     }
   }
   const int parity = L.lc & 1;
-  const RowLaneSigns rs = row_lane_signs(p, parity);
+  const RowLaneSigns rs = row_lane_signs<RHT>(p, parity);
   const int64_t C = p.cols;
   // RTNE onto E1M2/INT4 has an exact fast form; it needs no clamp when the
   // block scale is a normal E4M3 value (then |y| <= 1.0625 Qmax).
@@ -511,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[r][j] = xf[i][j];
-        if (p.rht) {
+        if (RHT) {
           fwht8_half(v[r], rs.h);
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[r][j] = fmaf(dpp_xor1(v[r][j]), rs.s4, v[r][j]);
@@ -521,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
         for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[r][j]));
         m = fmaxf(m, dpp_xor1(m));
         if (MX) m = fmaxf(m, dpp_xor2(m));
-        amax_b[r] = p.rht ? m * 0.25f : m;
+        amax_b[r] = RHT ? m * 0.25f : m;
         if (MX) {
           mx_scale<GRID>(amax_b[r], sbyte[r], inv[r]);
         } else {
@@ -594,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     // and byte runs per output line, instead of one scattered store per
     // lane and column.
     const bool blk_ok = L.m_h0 < T.P;  // this half's 16-row block exists
-    const float fin = p.rht ? p.sg.fin : 1.0f;
+    const float fin = RHT ? p.sg.fin : 1.0f;
     const int ch = 2 * L.wave + L.half;  // chunk of this half-wavefront
 #pragma clang loop unroll(full)
     for (int g2 = 0; g2 < 4; ++g2) {
@@ -608,12 +589,12 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
         const int k = 2 * g2 + r;
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[r][i] = xf[i][k];
-        if (p.rht) fwht16_inlane(v[r], p.sg);
+        if (RHT) fwht16_inlane(v[r], p.sg);
         float m = 0.0f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[r][j]));
         if (MX) m = fmaxf(m, __shfl_xor(m, 32));
-        amax_b[r] = p.rht ? m * 0.25f : m;
+        amax_b[r] = RHT ? m * 0.25f : m;
         if (MX) {
           mx_scale<GRID>(amax_b[r], sbyte[r], inv[r]);
         } else {
@@ -767,31 +748,55 @@ int64_t grid_size_quant(int64_t rows, int64_t cols, int32_t groups, int32_t bloc
   return (work + kNumXcd - 1) / kNumXcd * kNumXcd;
 }
 
-hipError_t launch_amax(const QuantParams& p, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL(ufp4_amax_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+// A kernel launch; with timing events, through hipExtLaunchKernelGGL, which
+// stamps the two events with the kernel's own start and end.
+template <typename K>
+static void launch(K kernel, const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (t0 || t1)
+    hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, t0, t1, 0u, p);
+  else
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+}
+
+hipError_t launch_amax(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (p.rht)
+    launch(ufp4_amax_kernel<true>, p, grid, s, t0, t1);
+  else
+    launch(ufp4_amax_kernel<false>, p, grid, s, t0, t1);
   return hipGetLastError();
 }
 
-template <int GRID, bool MX>
-static hipError_t launch_quant_grid(const QuantParams& p, int64_t grid, bool sr, hipStream_t s) {
-  if (sr)
-    hipLaunchKernelGGL((ufp4_quant_kernel<GRID, true, MX>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+template <int GRID, bool SR, bool MX>
+static void launch_quant_rht(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (p.rht)
+    launch(ufp4_quant_kernel<GRID, SR, MX, true>, p, grid, s, t0, t1);
   else
-    hipLaunchKernelGGL((ufp4_quant_kernel<GRID, false, MX>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    launch(ufp4_quant_kernel<GRID, SR, MX, false>, p, grid, s, t0, t1);
+}
+
+template <int GRID, bool MX>
+static hipError_t launch_quant_grid(const QuantParams& p, int64_t grid, bool sr, hipStream_t s, hipEvent_t t0,
+                                    hipEvent_t t1) {
+  if (sr)
+    launch_quant_rht<GRID, true, MX>(p, grid, s, t0, t1);
+  else
+    launch_quant_rht<GRID, false, MX>(p, grid, s, t0, t1);
   return hipGetLastError();
 }
 
 template <int GRID>
-static hipError_t launch_quant_mx(const QuantParams& p, int64_t grid, bool sr, hipStream_t s) {
-  return p.mx ? launch_quant_grid<GRID, true>(p, grid, sr, s) : launch_quant_grid<GRID, false>(p, grid, sr, s);
+static hipError_t launch_quant_mx(const QuantParams& p, int64_t grid, bool sr, hipStream_t s, hipEvent_t t0,
+                                  hipEvent_t t1) {
+  return p.mx ? launch_quant_grid<GRID, true>(p, grid, sr, s, t0, t1)
+              : launch_quant_grid<GRID, false>(p, grid, sr, s, t0, t1);
 }
 
-hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s) {
+hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const bool sr = p.sr != 0;
   switch (p.grid) {
-    case kGridE1M2: return launch_quant_mx<kGridE1M2>(p, grid, sr, s);
-    case kGridINT4: return launch_quant_mx<kGridINT4>(p, grid, sr, s);
-    case kGridE2M1: return launch_quant_mx<kGridE2M1>(p, grid, sr, s);
+    case kGridE1M2: return launch_quant_mx<kGridE1M2>(p, grid, sr, s, t0, t1);
+    case kGridINT4: return launch_quant_mx<kGridINT4>(p, grid, sr, s, t0, t1);
+    case kGridE2M1: return launch_quant_mx<kGridE2M1>(p, grid, sr, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }

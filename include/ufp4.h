@@ -197,6 +197,19 @@ int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_
 int ufp4_round_f32(const float* y_dev, int64_t n, int32_t grid, int32_t rounding,
                    uint64_t sr_seed, uint8_t* codes_dev, ufp4_stream_t stream);
 
+/* Measurement hook (not part of the quantization path): one
+ * ufp4_quantize_rowcol call with NV16 scaling on `stream`, whose two kernels
+ * (tensor maximum, then quantization) are launched with start/stop hipEvents
+ * that the runtime stamps with each kernel's own start and end.  Synchronizes
+ * the stream and writes the two kernel durations in milliseconds to host
+ * memory.  Other arguments and outputs exactly as ufp4_quantize_rowcol.
+ * rows or cols of 0, MX32 scaling or a null duration pointer give
+ * UFP4_ERR_INVALID_ARGUMENT.  Not for use under stream capture. */
+int ufp4_time_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                     const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out,
+                     void* ws, size_t ws_bytes, ufp4_stream_t stream, float* ms_amax_host,
+                     float* ms_quant_host);
+
 /* The 16 signs (+1/-1) selected by rht_seed (host memory). */
 int ufp4_rht_signs(uint64_t rht_seed, int8_t signs_host[16]);
 

@@ -132,3 +132,9 @@ def test_other_entry_point_errors(F):
     assert F.lib.ufp4_rht_signs(0, None) == 1
     assert F.lib.ufp4_workspace_init(None, 0, None) == 4
     assert F.lib.ufp4_grouped_col_offsets(None, 1, 16, None) == 1
+    ms = ctypes.c_float()
+    for c, rows, a, b in ((cfg, 64, None, ctypes.byref(ms)), (cfg, 64, ctypes.byref(ms), None),
+                          (F.config(scaling=1), 64, ctypes.byref(ms), ctypes.byref(ms)),
+                          (cfg, 0, ctypes.byref(ms), ctypes.byref(ms))):
+        assert F.lib.ufp4_time_rowcol(ctypes.c_void_p(FAKE), rows, 64, 64, ctypes.byref(c), q(F), q(F),
+                                      ctypes.c_void_p(FAKE), 1 << 30, None, a, b) == 1

@@ -196,6 +196,21 @@ def test_deterministic_repeat(env):
         assert torch.equal(qa.codes, qb.codes) and torch.equal(qa.scales, qb.scales)
 
 
+def test_timing_hook_matches_plain_call(env):
+    torch, F, orc = env
+    xb = synth.activation(384, 512, seed=9)
+    fc, oc = cfgs(F, orc, E1M2, RTNE, NV16, 1, 9, 9)
+    x = to_dev(torch, xb)
+    row, col = F.alloc_layout(384, 512, NV16), F.alloc_layout(512, 384, NV16)
+    ms_a, ms_q = F.ufp4_time_rowcol(x, fc, row, col, F.Workspace(384, 512))
+    assert ms_a > 0.0 and ms_q > 0.0
+    for name, qt, layout in (("row", row, ROW), ("col", col, COL)):
+        c, s_, t = orc.quantize(xb, oc, layout)
+        assert np.array_equal(qt.codes.cpu().numpy(), c), name
+        assert np.array_equal(qt.scales.cpu().numpy(), s_), name
+        assert qt.tensor_scale.cpu().numpy().view(np.uint32)[0] == t.view(np.uint32)[0], name
+
+
 # ------------------------------------------------------------------ grouped
 def gpu_grouped(env, xb, offsets, fc, row=True, col=True):
     torch, F, _ = env
