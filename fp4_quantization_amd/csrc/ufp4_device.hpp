@@ -110,11 +110,14 @@ __device__ __forceinline__ void fwht8_half(float v[8], const HalfSigns& S) {
 
 // Cross-lane value of the lane whose index differs in bit 0 (DPP quad_perm
 // [1,0,3,2]) and in bit 1 ([2,3,0,1]).
+// (Every lane has a source lane in these permutations, so bound_ctrl does not
+// change the result; setting it lets the compiler fold the move into the
+// consuming instruction as a DPP operand.)
 __device__ __forceinline__ float dpp_xor1(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float dpp_xor2(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
 
 // ---------------------------------------------------------------- E4M3 / E8M0

@@ -254,17 +254,25 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
   const LaneGeom L = lane_geom(p, T);
   uint32_t w[16][4];
   load_tile(p, T, L, w);
+  // Rows are consumed in load order, each as soon as it arrives: its
+  // row-wise half-blocks are transformed at once, and the column-wise
+  // butterflies advance one stage whenever the rows they pair are present,
+  // so the arithmetic overlaps the remaining loads.
   float acc_r = 0.0f, acc_c = 0.0f;
-  if (p.do_row) {
-    const RowLaneSigns rs = row_lane_signs<RHT>(p, L.lc & 1);
-#pragma clang loop unroll(full)
-    for (int i = 0; i < 16; ++i) {
+  const bool do_row = p.do_row != 0, do_col = p.do_col != 0;
+  const RowLaneSigns rs = row_lane_signs<RHT>(p, L.lc & 1);
+  float cv[16][8];  // column-wise values of the lane's 8 columns, by row
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      cv[i][2 * k] = bf_lo(w[i][k]);
+      cv[i][2 * k + 1] = bf_hi(w[i][k]);
+    }
+    if (do_row) {
       float v[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[2 * k] = bf_lo(w[i][k]);
-        v[2 * k + 1] = bf_hi(w[i][k]);
-      }
+      for (int j = 0; j < 8; ++j) v[j] = cv[i][j];
       if (RHT) {
         fwht8_half(v, rs.h);
 #pragma unroll
@@ -274,33 +282,36 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
         for (int j = 0; j < 8; ++j) acc_r = fmaxf(acc_r, fabsf(v[j]));
       }
     }
-  }
-  if (p.do_col) {
-#pragma clang loop unroll(full)
-    for (int k = 0; k < 8; ++k) {
-      float v[16];
+    if (RHT && do_col) {
+      // column-wise stages of half-width 1, 2, 4 once their rows are here
+      if (i % 2 == 1) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = (k & 1) ? bf_hi(w[i][k >> 1]) : bf_lo(w[i][k >> 1]);
-      if (RHT) {
-        // stages of half-width 1, 2, 4; the last stage folds into the max
-#pragma unroll
-        for (int q = 0; q < 8; ++q) bfly(v[2 * q], v[2 * q + 1], p.sg.q1[q]);
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          bfly(v[4 * gi + 0], v[4 * gi + 2], p.sg.q2[gi]);
-          bfly(v[4 * gi + 1], v[4 * gi + 3], p.sg.q2[gi]);
-        }
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bfly(v[8 * gi + j], v[8 * gi + j + 4], p.sg.q3[gi]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc_c = lastpair_max(acc_c, v[j], v[j + 8]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc_c = fmaxf(acc_c, fabsf(v[j]));
+        for (int c = 0; c < 8; ++c) bfly(cv[i - 1][c], cv[i][c], p.sg.q1[i / 2]);
       }
+      if (i % 4 == 3) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          bfly(cv[i - 3][c], cv[i - 1][c], p.sg.q2[i / 4]);
+          bfly(cv[i - 2][c], cv[i][c], p.sg.q2[i / 4]);
+        }
+      }
+      if (i % 8 == 7) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) bfly(cv[i - 7 + j][c], cv[i - 3 + j][c], p.sg.q3[i / 8]);
+        }
+      }
+    }
+  }
+  if (do_col) {
+    // the last stage folds into the max
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc_c = RHT ? lastpair_max(acc_c, cv[j][c], cv[j + 8][c])
+                    : fmaxf(acc_c, fmaxf(fabsf(cv[j][c]), fabsf(cv[j + 8][c])));
     }
   }
   acc_r = wave_max(acc_r);
@@ -324,38 +335,73 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
 // ---------------------------------------------------------------- phase B
 // Per-tensor quantities of one layout of the workgroup's segment.
 struct TensorScale {
-  float S;      // S_t
-  float D;      // fl(Qmax * S_t)
-  float R;      // fl(1 / D), for the bracketed block-scale estimate
-  bool fast;    // D normal and finite, amax small enough that 0.25*inv_b is exact
+  float S;     // S_t
+  float D;     // fl(Qmax * S_t)
+  float R4;    // fl(1 / D), times 1/4 under the transform (block maxima are
+               // taken before the transform's final 1/4)
+  bool fast;   // D normal and at most 2^120 (so R4 is exact), amax small
+               // enough that 0.25 * inv_b is exact
 };
 
 // raw = max |transform before the 1/4| over the tensor (or max |x| without
 // the transform).  S_t = amax / (Qmax * 448), 1 for an all-zero tensor.
-__device__ __forceinline__ TensorScale make_tensor_scale(float raw, bool rht, float qmax) {
+template <bool RHT>
+__device__ __forceinline__ TensorScale make_tensor_scale(float raw, float qmax) {
   TensorScale ts;
-  const float a = rht ? raw * 0.25f : raw;  // max of the scaled values (rounding is monotone)
+  const float a = RHT ? raw * 0.25f : raw;  // max of the scaled values (rounding is monotone)
   ts.S = (a > 0.0f) ? a / (qmax * 448.0f) : 1.0f;
   ts.D = qmax * ts.S;
-  ts.R = 1.0f / ts.D;
-  ts.fast = ts.D >= 0x1p-126f && ts.D <= 0x1p+127f && a < 0x1p+119f;
+  const float R = 1.0f / ts.D;
+  ts.R4 = RHT ? R * 0.25f : R;
+  ts.fast = ts.D >= 0x1p-126f && ts.D <= 0x1p+120f && a < 0x1p+119f;
   return ts;
 }
 
-// Block scale (NV16): s_b = E4M3(fl(amax_b / D)), saturated.  fl(amax_b * R)
-// is within 3 ulp of amax_b / D, so when both ends of a +-2^-21 bracket around
-// it encode to the same E4M3 code, that code is exact (E4M3 rounding is
-// monotone); otherwise, or when the per-tensor quantities are extreme, the
-// correctly rounded division decides.
-__device__ __forceinline__ uint32_t nv_block_code(float amax_b, const TensorScale& ts) {
-  if (ts.fast) {
-    const float q = amax_b * ts.R;
-    const float lo = fminf(q * 0x1.fffffp-1f, 448.0f);   // q (1 - 2^-21)
-    const float hi = fminf(q * 0x1.000004p+0f, 448.0f);  // q (1 + 2^-21)
-    const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false);
-    if ((pk & 0xFFu) == ((pk >> 8) & 0xFFu)) return pk & 0xFFu;
+// Block scales of NB blocks from their raw maxima (before the transform's
+// final 1/4).  NV16: s_b = E4M3(fl(amax_b / D)), saturated.  When the
+// per-tensor quantities allow it, fl(raw * R4) = fl(amax_b * fl(1/D)) lies
+// within 3 ulp of amax_b / D, so if both ends of a +-2^-21 bracket around it
+// encode to the same E4M3 code, that code is exact (E4M3 rounding is
+// monotone); if any block of the wavefront is not decided that way (or its
+// maximum is too small for the 1/4 to be exact), the correctly rounded
+// division decides for all of them.  MX32: a power-of-two scale.
+// Returns true when every real block of the wavefront allows the exact fast
+// rounding (normal block scale, no tiny nonzero maximum).
+template <int GRID, bool MX, bool RHT, int NB>
+__device__ __forceinline__ bool block_scales(const float raw[NB], const bool real[NB], const TensorScale& ts,
+                                             bool fast_u, const float* lut_l, uint32_t sbyte[NB], float inv[NB]) {
+  constexpr float kThr = RHT ? 0x1p-98f : 0x1p-100f;  // raw maxima whose 1/4 keeps codes exact
+  bool bad = false;
+  if (MX) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      mx_scale<GRID>(RHT ? raw[b] * 0.25f : raw[b], sbyte[b], inv[b]);
+      bad |= real[b] & (raw[b] != 0.0f) & !(raw[b] >= kThr);
+    }
+  } else {
+    bool need_div = !fast_u;
+    if (fast_u) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float q = raw[b] * ts.R4;
+        const float lo = fminf(q * 0x1.fffffp-1f, 448.0f);   // q (1 - 2^-21)
+        const float hi = fminf(q * 0x1.000004p+0f, 448.0f);  // q (1 + 2^-21)
+        const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false);
+        sbyte[b] = pk & 0xFFu;
+        need_div |= (((pk ^ (pk >> 8)) & 0xFFu) != 0u) | ((raw[b] != 0.0f) & (raw[b] < kThr));
+      }
+    }
+    if (__any(need_div)) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) sbyte[b] = e4m3_encode_sat((RHT ? raw[b] * 0.25f : raw[b]) / ts.D);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) inv[b] = lut_l[sbyte[b]];
+    bad = !fast_u;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) bad |= real[b] & (raw[b] != 0.0f) & ((raw[b] < kThr) | (sbyte[b] < 8u));
   }
-  return e4m3_encode_sat(amax_b / ts.D);
+  return !__any(bad);
 }
 
 // Staging of a tile's column-wise output: [chunk][column] with chunk = the
@@ -431,8 +477,8 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
       r = fmaxf(r, red[0][i]);
       c = fmaxf(c, red[1][i]);
     }
-    tsr = make_tensor_scale(r, RHT, qmax);
-    tsc = make_tensor_scale(c, RHT, qmax);
+    tsr = make_tensor_scale<RHT>(r, qmax);
+    tsc = make_tensor_scale<RHT>(c, qmax);
     {
       const int t = threadIdx.x, l = t >> 7, cc = t & 127;
       const float S = l ? tsc.S : tsr.S;
@@ -459,6 +505,9 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
       }
     }
   }
+  // wave-uniform (scalar) copies of the per-tensor fast-path conditions
+  const bool fast_r = __builtin_amdgcn_readfirstlane((int)tsr.fast) != 0;
+  const bool fast_c = __builtin_amdgcn_readfirstlane((int)tsc.fast) != 0;
   const int parity = L.lc & 1;
   const RowLaneSigns rs = row_lane_signs<RHT>(p, parity);
   const int64_t C = p.cols;
@@ -479,9 +528,9 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     for (int g4 = 0; g4 < 4; ++g4) {
       // four independent row blocks per step: transform, scale, vote, round
       float v[4][8];
-      float amax_b[4], inv[4];
+      float raw[4], inv[4];
       uint32_t sbyte[4];
-      bool ok = true;
+      bool real[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * g4 + r;
@@ -502,19 +551,12 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
         for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[r][j]));
         m = fmaxf(m, dpp_xor1(m));
         if (MX) m = fmaxf(m, dpp_xor2(m));
-        amax_b[r] = RHT ? m * 0.25f : m;
-        if (MX) {
-          mx_scale<GRID>(amax_b[r], sbyte[r], inv[r]);
-        } else {
-          sbyte[r] = nv_block_code(amax_b[r], tsr);
-          inv[r] = lut[0][sbyte[r]];
-        }
-        const bool real = L.lane_ok && L.m_h0 + i < T.M;
-        ok = ok && (!real || amax_b[r] == 0.0f ||
-                    (amax_b[r] >= 0x1p-100f && (MX || (sbyte[r] >= 8u && tsr.fast))));
+        raw[r] = m;
+        real[r] = L.lane_ok & (L.m_h0 + i < T.M);
       }
+      const bool ok = block_scales<GRID, MX, RHT, 4>(raw, real, tsr, fast_r, lut[0], sbyte, inv);
       uint32_t packed[4] = {0u, 0u, 0u, 0u};
-      if (kFastGrid && __all(ok)) {
+      if (kFastGrid && ok) {
         // t = y / (grid step) as one product: an exact power-of-two rescaling
         // of fl(fl(v/4) * inv_b) for every element whose code can be nonzero
 #pragma unroll
@@ -581,9 +623,9 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     for (int g2 = 0; g2 < 4; ++g2) {
       // two independent column blocks per step
       float v[2][16];
-      float amax_b[2], inv[2];
+      float raw[2], inv[2];
       uint32_t sbyte[2];
-      bool ok = true;
+      bool real[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int k = 2 * g2 + r;
@@ -594,18 +636,12 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[r][j]));
         if (MX) m = fmaxf(m, __shfl_xor(m, 32));
-        amax_b[r] = RHT ? m * 0.25f : m;
-        if (MX) {
-          mx_scale<GRID>(amax_b[r], sbyte[r], inv[r]);
-        } else {
-          sbyte[r] = nv_block_code(amax_b[r], tsc);
-          inv[r] = lut[1][sbyte[r]];
-        }
-        ok = ok && (!(L.lane_ok && blk_ok) || amax_b[r] == 0.0f ||
-                    (amax_b[r] >= 0x1p-100f && (MX || (sbyte[r] >= 8u && tsc.fast))));
+        raw[r] = m;
+        real[r] = L.lane_ok & blk_ok;
       }
+      const bool ok = block_scales<GRID, MX, RHT, 2>(raw, real, tsc, fast_c, lut[1], sbyte, inv);
       uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
-      if (kFastGrid && __all(ok)) {
+      if (kFastGrid && ok) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const float mult = inv[r] * (fin * kGridMul);
