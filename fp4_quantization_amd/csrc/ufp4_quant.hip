@@ -151,18 +151,19 @@ __device__ __forceinline__ LaneGeom lane_geom(const QuantParams& p, const TileIn
   return L;
 }
 
-// Load the lane's 16 x 8 sub-tile (zeros outside the segment / tensor).  The
-// loads are unconditional and in row order, so consumers that walk the rows
-// in order start before the last row arrives; lanes or rows outside the data
-// read an in-bounds address and are zeroed.
-__device__ __forceinline__ void load_tile(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
+// Load rows [R0, R1) of the lane's 16 x 8 sub-tile (zeros outside the
+// segment / tensor).  The loads are unconditional and in row order, so
+// consumers that walk the rows in order start before the last row arrives;
+// lanes or rows outside the data read an in-bounds address and are zeroed.
+template <int R0, int R1>
+__device__ __forceinline__ void load_rows(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
                                           uint32_t w[16][4]) {
   const int64_t rows_left = T.M - L.m_h0;
   const bool full = L.lane_ok && rows_left >= 16;
   if (__all(full)) {
     const uint16_t* ptr = p.x + (T.seg_row0 + L.m_h0) * p.ld + L.c0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = R0; i < R1; ++i) {
       const uint4 v = *reinterpret_cast<const uint4*>(ptr + (int64_t)i * p.ld);
       w[i][0] = v.x;
       w[i][1] = v.y;
@@ -172,7 +173,7 @@ __device__ __forceinline__ void load_tile(const QuantParams& p, const TileInfo& 
   } else {
     const int64_t c = L.lane_ok ? L.c0 : 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = R0; i < R1; ++i) {
       const bool ok = L.lane_ok && i < rows_left;
       const int64_t m = ok ? L.m_h0 + i : 0;  // row 0 of an active segment exists
       const uint4 v = *reinterpret_cast<const uint4*>(p.x + (T.seg_row0 + m) * p.ld + c);
@@ -182,6 +183,11 @@ __device__ __forceinline__ void load_tile(const QuantParams& p, const TileInfo& 
       w[i][3] = ok ? v.w : 0u;
     }
   }
+}
+
+__device__ __forceinline__ void load_tile(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
+                                          uint32_t w[16][4]) {
+  load_rows<0, 16>(p, T, L, w);
 }
 
 // Folded signs of the lane's half of a row-wise block (selected by lane
@@ -211,6 +217,27 @@ __device__ __forceinline__ RowLaneSigns row_lane_signs(const QuantParams& p, int
   r.s4 = lane_select(p.s4[0], p.s4[1], oddf);
   r.fin = RHT ? lane_select(p.fin_lane[0], p.fin_lane[1], oddf) : 1.0f;
   return r;
+}
+
+// Last butterfly stage of a row-wise block across a lane pair, for the
+// lane's 8 values: v += s4 * (the partner lane's v), one v_fmac_f32 with a DPP
+// quad_perm [1,0,3,2] operand per value (the compiler does not fold a DPP
+// move into a multiply-accumulate).  The leading s_nop provides the two wait
+// states a DPP read needs after a VALU write of its source; inside the block
+// each instruction reads a register no earlier instruction of the block
+// wrote.  All lanes are active wherever this is used.
+__device__ __forceinline__ void cross_stage8(float v[8], float s4) {
+  asm("s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+      : "v"(s4));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -437,31 +464,39 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
   constexpr float qmax = GRID == kGridE1M2 ? 3.5f : (GRID == kGridINT4 ? 7.0f : 6.0f);
   TensorScale tsr{1.0f, qmax, 1.0f / qmax, false}, tsc = tsr;
   // Phase-A partials of the segment: the first 4 per thread are requested
-  // before the tile, so their latency overlaps the tile loads.
-  const int64_t t0 = p.offsets ? g.tpre[T.seg] : 0;
-  const int64_t nt = p.offsets ? g.tpre[T.seg + 1] - g.tpre[T.seg] : p.n_tiles;
-  const int64_t cnt = MX ? 0 : nt * p.n_band;
+  // before the tile, so their latency overlaps the tile loads.  The loads are
+  // unconditional (clamped index, result selected afterwards), so they issue
+  // back to back; a dense tensor's partials are contiguous.
+  const uint32_t t0 = p.offsets ? (uint32_t)g.tpre[T.seg] : 0u;
+  const uint32_t nt = p.offsets ? (uint32_t)(g.tpre[T.seg + 1] - g.tpre[T.seg]) : (uint32_t)p.n_tiles;
+  const uint32_t cnt = MX ? 0u : nt * (uint32_t)p.n_band;
+  auto part_index = [&](uint32_t j) -> uint32_t {
+    return p.offsets ? (j / nt) * (uint32_t)p.n_tiles + t0 + j % nt : j;
+  };
   float2 pre[4];
+  if (!MX) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t i = threadIdx.x + q * kThreads;
-    const int64_t j = i < cnt ? i : 0;
-    const int64_t b = j / nt, t = t0 + j % nt;
-    pre[q] = (i < cnt) ? p.ws_part[b * p.n_tiles + t] : make_float2(0.0f, 0.0f);
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t i = threadIdx.x + q * kThreads;
+      pre[q] = p.ws_part[part_index(i < cnt ? i : cnt - 1u)];
+    }
   }
+  // The first four rows are requested before the prologue and the rest after
+  // it: with fewer requests ahead of them in the memory queues, the rows the
+  // first group needs arrive sooner.
   uint32_t w[16][4];
-  load_tile(p, T, L, w);
+  load_rows<0, 4>(p, T, L, w);
   if (!MX) {
     // per-tensor maximum of the segment from the phase-A partials
     float r = 0.0f, c = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      r = fmaxf(r, pre[q].x);
-      c = fmaxf(c, pre[q].y);
+      const bool in = threadIdx.x + q * kThreads < cnt;
+      r = fmaxf(r, in ? pre[q].x : 0.0f);
+      c = fmaxf(c, in ? pre[q].y : 0.0f);
     }
-    for (int64_t i = threadIdx.x + 4 * kThreads; i < cnt; i += kThreads) {
-      const int64_t b = i / nt, t = t0 + i % nt;
-      const float2 q = p.ws_part[b * p.n_tiles + t];
+    for (uint32_t i = threadIdx.x + 4 * kThreads; i < cnt; i += kThreads) {
+      const float2 q = p.ws_part[part_index(i)];
       r = fmaxf(r, q.x);
       c = fmaxf(c, q.y);
     }
@@ -491,6 +526,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     }
     __syncthreads();
   }
+  load_rows<4, 16>(p, T, L, w);
 
   // The sub-tile is unpacked once (row by row, in load order, inside the
   // row-wise pass) and kept for the column-wise pass.
@@ -543,8 +579,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
         for (int j = 0; j < 8; ++j) v[r][j] = xf[i][j];
         if (RHT) {
           fwht8_half(v[r], rs.h);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[r][j] = fmaf(dpp_xor1(v[r][j]), rs.s4, v[r][j]);
+          cross_stage8(v[r], rs.s4);
         }
         float m = 0.0f;
 #pragma unroll
