@@ -27,6 +27,8 @@
 
 namespace ufp4 {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 struct TileInfo {
   bool active;
   bool bad;
@@ -155,7 +157,19 @@ __device__ __forceinline__ LaneGeom lane_geom(const QuantParams& p, const TileIn
 // segment / tensor).  The loads are unconditional and in row order, so
 // consumers that walk the rows in order start before the last row arrives;
 // lanes or rows outside the data read an in-bounds address and are zeroed.
-template <int R0, int R1>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load; STREAM marks it non-temporal (last use of the data).
+template <bool STREAM>
+__device__ __forceinline__ uint4 load16(const uint16_t* a) {
+  if (STREAM) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  return *reinterpret_cast<const uint4*>(a);
+}
+
+template <int R0, int R1, bool STREAM = false>
 __device__ __forceinline__ void load_rows(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
                                           uint32_t w[16][4]) {
   const int64_t rows_left = T.M - L.m_h0;
@@ -164,7 +178,7 @@ __device__ __forceinline__ void load_rows(const QuantParams& p, const TileInfo& 
     const uint16_t* ptr = p.x + (T.seg_row0 + L.m_h0) * p.ld + L.c0;
 #pragma unroll
     for (int i = R0; i < R1; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4*>(ptr + (int64_t)i * p.ld);
+      const uint4 v = load16<STREAM>(ptr + (int64_t)i * p.ld);
       w[i][0] = v.x;
       w[i][1] = v.y;
       w[i][2] = v.z;
@@ -176,7 +190,7 @@ __device__ __forceinline__ void load_rows(const QuantParams& p, const TileInfo& 
     for (int i = R0; i < R1; ++i) {
       const bool ok = L.lane_ok && i < rows_left;
       const int64_t m = ok ? L.m_h0 + i : 0;  // row 0 of an active segment exists
-      const uint4 v = *reinterpret_cast<const uint4*>(p.x + (T.seg_row0 + m) * p.ld + c);
+      const uint4 v = load16<STREAM>(p.x + (T.seg_row0 + m) * p.ld + c);
       w[i][0] = ok ? v.x : 0u;
       w[i][1] = ok ? v.y : 0u;
       w[i][2] = ok ? v.z : 0u;
@@ -485,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
   // it: with fewer requests ahead of them in the memory queues, the rows the
   // first group needs arrive sooner.
   uint32_t w[16][4];
-  load_rows<0, 4>(p, T, L, w);
+  load_rows<0, 4, true>(p, T, L, w);
   if (!MX) {
     // per-tensor maximum of the segment from the phase-A partials
     float r = 0.0f, c = 0.0f;
@@ -526,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     }
     __syncthreads();
   }
-  load_rows<4, 16>(p, T, L, w);
+  load_rows<4, 16, true>(p, T, L, w);
 
   // The sub-tile is unpacked once (row by row, in load order, inside the
   // row-wise pass) and kept for the column-wise pass.
@@ -635,11 +649,11 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
         const int i = 4 * g4 + r;
         if (L.lane_ok && L.m_h0 + i < T.M) {
           const uint32_t li = lrow + (uint32_t)i;
-          *reinterpret_cast<uint32_t*>(rc_base + (li * rc_stride + 4u * (uint32_t)L.lc)) = packed[r];
+          __builtin_nontemporal_store(packed[r], reinterpret_cast<uint32_t*>(rc_base + (li * rc_stride + 4u * (uint32_t)L.lc)));
           if (MX) {
-            if ((L.lc & 3) == 0) rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 2)] = (uint8_t)sbyte[r];
+            if ((L.lc & 3) == 0) __builtin_nontemporal_store((uint8_t)sbyte[r], &rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 2)]);
           } else if (parity == 0) {
-            rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 1)] = (uint8_t)sbyte[r];
+            __builtin_nontemporal_store((uint8_t)sbyte[r], &rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 1)]);
           }
         }
       }
@@ -742,8 +756,11 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     for (int j = 0; j < 8; ++j) {
       const int q = threadIdx.x + j * kThreads;
       const int col = q >> 3, chq = q & 7;
-      if (col < ncols && chq < nch)
-        *reinterpret_cast<uint2*>(cc + (int64_t)col * (Rp / 2) + 8 * chq) = cst.codes[chq][col];
+      if (col < ncols && chq < nch) {
+        const uint2 cw = cst.codes[chq][col];
+        const u32x2 cv2 = {cw.x, cw.y};
+        __builtin_nontemporal_store(cv2, reinterpret_cast<u32x2*>(cc + (int64_t)col * (Rp / 2) + 8 * chq));
+      }
     }
     uint8_t* cs = p.col_scales + band_c0 * (Rp / B) + (T.coff + T.m0) / B;
     const int nsc = MX ? nch / 2 : nch;  // scale bytes per line in this tile
@@ -752,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     for (int j = 0; j < (MX ? 4 : 8); ++j) {
       const int q = threadIdx.x + j * kThreads;
       const int col = q / per, b = q % per;
-      if (col < ncols && b < nsc) cs[(int64_t)col * (Rp / B) + b] = cst.scales[MX ? 2 * b : b][col];
+      if (col < ncols && b < nsc) __builtin_nontemporal_store(cst.scales[MX ? 2 * b : b][col], &cs[(int64_t)col * (Rp / B) + b]);
     }
   }
 }
