@@ -403,33 +403,39 @@ __device__ __forceinline__ TensorScale make_tensor_scale(float raw, float qmax) 
 // per-tensor quantities allow it, fl(raw * R4) = fl(amax_b * fl(1/D)) lies
 // within 3 ulp of amax_b / D, so if both ends of a +-2^-21 bracket around it
 // encode to the same E4M3 code, that code is exact (E4M3 rounding is
-// monotone); if any block of the wavefront is not decided that way (or its
-// maximum is too small for the 1/4 to be exact), the correctly rounded
-// division decides for all of them.  MX32: a power-of-two scale.
-// Returns true when every real block of the wavefront allows the exact fast
-// rounding (normal block scale, no tiny nonzero maximum).
+// monotone).  Every block maximum is at most the tensor maximum, so the
+// bracket stays below 448 (1 + 2^-20), inside the range where the hardware
+// conversion rounds to nearest even and saturates to 448.  If any block of the
+// wavefront is not decided that way (or its maximum is too small for the 1/4
+// to be exact), the correctly rounded division decides for all of them.
+// MX32: a power-of-two scale.  Returns true when every block of the
+// wavefront allows the exact fast rounding (normal block scale, no tiny
+// nonzero maximum); blocks outside the data hold zeros and always allow it.
 template <int GRID, bool MX, bool RHT, int NB>
-__device__ __forceinline__ bool block_scales(const float raw[NB], const bool real[NB], const TensorScale& ts,
-                                             bool fast_u, const float* lut_l, uint32_t sbyte[NB], float inv[NB]) {
+__device__ __forceinline__ bool block_scales(const float raw[NB], const TensorScale& ts, bool fast_u,
+                                             const float* lut_l, uint32_t sbyte[NB], float inv[NB]) {
   constexpr float kThr = RHT ? 0x1p-98f : 0x1p-100f;  // raw maxima whose 1/4 keeps codes exact
   bool bad = false;
   if (MX) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       mx_scale<GRID>(RHT ? raw[b] * 0.25f : raw[b], sbyte[b], inv[b]);
-      bad |= real[b] & (raw[b] != 0.0f) & !(raw[b] >= kThr);
+      bad |= (raw[b] != 0.0f) & !(raw[b] >= kThr);
     }
   } else {
     bool need_div = !fast_u;
+    bool tiny[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) tiny[b] = (raw[b] != 0.0f) & (raw[b] < kThr);
     if (fast_u) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const float q = raw[b] * ts.R4;
-        const float lo = fminf(q * 0x1.fffffp-1f, 448.0f);   // q (1 - 2^-21)
-        const float hi = fminf(q * 0x1.000004p+0f, 448.0f);  // q (1 + 2^-21)
-        const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false);
+        const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q * 0x1.fffffp-1f,   // q (1 - 2^-21)
+                                                                       q * 0x1.000004p+0f,  // q (1 + 2^-21)
+                                                                       0, false);
         sbyte[b] = pk & 0xFFu;
-        need_div |= (((pk ^ (pk >> 8)) & 0xFFu) != 0u) | ((raw[b] != 0.0f) & (raw[b] < kThr));
+        need_div |= (sbyte[b] != ((pk >> 8) & 0xFFu)) | tiny[b];
       }
     }
     if (__any(need_div)) {
@@ -440,7 +446,7 @@ __device__ __forceinline__ bool block_scales(const float raw[NB], const bool rea
     for (int b = 0; b < NB; ++b) inv[b] = lut_l[sbyte[b]];
     bad = !fast_u;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) bad |= real[b] & (raw[b] != 0.0f) & ((raw[b] < kThr) | (sbyte[b] < 8u));
+    for (int b = 0; b < NB; ++b) bad |= tiny[b] | ((raw[b] != 0.0f) & (sbyte[b] < 8u));
   }
   return !__any(bad);
 }
@@ -580,7 +586,6 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
       float v[4][8];
       float raw[4], inv[4];
       uint32_t sbyte[4];
-      bool real[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * g4 + r;
@@ -601,9 +606,8 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
         m = fmaxf(m, dpp_xor1(m));
         if (MX) m = fmaxf(m, dpp_xor2(m));
         raw[r] = m;
-        real[r] = L.lane_ok & (L.m_h0 + i < T.M);
       }
-      const bool ok = block_scales<GRID, MX, RHT, 4>(raw, real, tsr, fast_r, lut[0], sbyte, inv);
+      const bool ok = block_scales<GRID, MX, RHT, 4>(raw, tsr, fast_r, lut[0], sbyte, inv);
       uint32_t packed[4] = {0u, 0u, 0u, 0u};
       if (kFastGrid && ok) {
         // t = y / (grid step) as one product: an exact power-of-two rescaling
@@ -665,7 +669,6 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     // half-wavefront's 16 rows), then leave as contiguous 8-byte code runs
     // and byte runs per output line, instead of one scattered store per
     // lane and column.
-    const bool blk_ok = L.m_h0 < T.P;  // this half's 16-row block exists
     const float fin = RHT ? p.sg.fin : 1.0f;
     const int ch = 2 * L.wave + L.half;  // chunk of this half-wavefront
 #pragma clang loop unroll(full)
@@ -674,7 +677,6 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
       float v[2][16];
       float raw[2], inv[2];
       uint32_t sbyte[2];
-      bool real[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int k = 2 * g2 + r;
@@ -686,9 +688,8 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
         for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[r][j]));
         if (MX) m = fmaxf(m, __shfl_xor(m, 32));
         raw[r] = m;
-        real[r] = L.lane_ok & blk_ok;
       }
-      const bool ok = block_scales<GRID, MX, RHT, 2>(raw, real, tsc, fast_c, lut[1], sbyte, inv);
+      const bool ok = block_scales<GRID, MX, RHT, 2>(raw, tsc, fast_c, lut[1], sbyte, inv);
       uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
       if (kFastGrid && ok) {
 #pragma unroll
