@@ -27,7 +27,6 @@
 
 namespace ufp4 {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct TileInfo {
   bool active;
@@ -157,6 +156,7 @@ __device__ __forceinline__ LaneGeom lane_geom(const QuantParams& p, const TileIn
 // segment / tensor).  The loads are unconditional and in row order, so
 // consumers that walk the rows in order start before the last row arrives;
 // lanes or rows outside the data read an in-bounds address and are zeroed.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte load; STREAM marks it non-temporal (last use of the data).
@@ -655,9 +655,9 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
           const uint32_t li = lrow + (uint32_t)i;
           __builtin_nontemporal_store(packed[r], reinterpret_cast<uint32_t*>(rc_base + (li * rc_stride + 4u * (uint32_t)L.lc)));
           if (MX) {
-            if ((L.lc & 3) == 0) __builtin_nontemporal_store((uint8_t)sbyte[r], &rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 2)]);
+            if ((L.lc & 3) == 0) rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 2)] = (uint8_t)sbyte[r];
           } else if (parity == 0) {
-            __builtin_nontemporal_store((uint8_t)sbyte[r], &rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 1)]);
+            rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 1)] = (uint8_t)sbyte[r];
           }
         }
       }
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     for (int j = 0; j < (MX ? 4 : 8); ++j) {
       const int q = threadIdx.x + j * kThreads;
       const int col = q / per, b = q % per;
-      if (col < ncols && b < nsc) __builtin_nontemporal_store(cst.scales[MX ? 2 * b : b][col], &cs[(int64_t)col * (Rp / B) + b]);
+      if (col < ncols && b < nsc) cs[(int64_t)col * (Rp / B) + b] = cst.scales[MX ? 2 * b : b][col];
     }
   }
 }
