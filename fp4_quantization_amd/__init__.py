@@ -12,11 +12,11 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import (GRID_E1M2, GRID_E2M1, GRID_INT4, LIB_PATH, ROUND_RTNE, ROUND_STOCHASTIC,
+from ._lib import (GRID_E1M2, GRID_E2M1, GRID_E2M1C, GRID_INT4, LIB_PATH, ROUND_RTNE, ROUND_STOCHASTIC,
                    SCALE_MX32, SCALE_NV16, Ufp4Error, check, lib, ufp4_config, ufp4_qtensor,
                    ufp4_stats_t)
 
-__all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "ROUND_RTNE", "ROUND_STOCHASTIC", "SCALE_NV16",
+__all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "GRID_E2M1C", "ROUND_RTNE", "ROUND_STOCHASTIC", "SCALE_NV16",
            "SCALE_MX32", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
            "ufp4_quantize", "ufp4_quantize_rowcol", "ufp4_quantize_grouped", "ufp4_dequantize",
            "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol",

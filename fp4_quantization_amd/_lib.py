@@ -17,7 +17,7 @@ STATUS_NAMES = {0: "UFP4_OK", 1: "UFP4_ERR_INVALID_ARGUMENT", 2: "UFP4_ERR_SHAPE
                 3: "UFP4_ERR_ALIGNMENT", 4: "UFP4_ERR_WORKSPACE", 5: "UFP4_ERR_HIP",
                 6: "UFP4_ERR_OFFSETS"}
 
-GRID_E1M2, GRID_INT4, GRID_E2M1 = 0, 1, 2
+GRID_E1M2, GRID_INT4, GRID_E2M1, GRID_E2M1C = 0, 1, 2, 3
 ROUND_RTNE, ROUND_STOCHASTIC = 0, 1
 SCALE_NV16, SCALE_MX32 = 0, 1
 

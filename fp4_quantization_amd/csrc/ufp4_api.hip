@@ -17,7 +17,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_cfg(const ufp4_config* cfg) {
   if (!cfg) return UFP4_ERR_INVALID_ARGUMENT;
-  if (cfg->grid < 0 || cfg->grid > 2) return UFP4_ERR_INVALID_ARGUMENT;
+  if (cfg->grid < 0 || cfg->grid > 3) return UFP4_ERR_INVALID_ARGUMENT;
   if (cfg->rounding < 0 || cfg->rounding > 1) return UFP4_ERR_INVALID_ARGUMENT;
   if (cfg->scaling < 0 || cfg->scaling > 1) return UFP4_ERR_INVALID_ARGUMENT;
   if (cfg->rht != 0 && cfg->rht != 1) return UFP4_ERR_INVALID_ARGUMENT;
@@ -364,7 +364,7 @@ int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_
 
 int ufp4_round_f32(const float* y_dev, int64_t n, int32_t grid, int32_t rounding, uint64_t sr_seed,
                    uint8_t* codes_dev, ufp4_stream_t stream) {
-  if (n < 0 || grid < 0 || grid > 2 || rounding < 0 || rounding > 1) return UFP4_ERR_INVALID_ARGUMENT;
+  if (n < 0 || grid < 0 || grid > 3 || rounding < 0 || rounding > 1) return UFP4_ERR_INVALID_ARGUMENT;
   if (n == 0) return UFP4_OK;
   if (!y_dev || !codes_dev) return UFP4_ERR_INVALID_ARGUMENT;
   if (!aligned(y_dev, 4)) return UFP4_ERR_ALIGNMENT;

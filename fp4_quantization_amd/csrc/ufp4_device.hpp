@@ -18,7 +18,9 @@
 
 namespace ufp4 {
 
-constexpr int kGridE1M2 = 0, kGridINT4 = 1, kGridE2M1 = 2;
+// E2M1C: E2M1 codes limited to the uniformly spaced magnitudes {0, 0.5, 1,
+// 1.5, 2} (E2M1 with its range clamped to imitate a uniform grid).
+constexpr int kGridE1M2 = 0, kGridINT4 = 1, kGridE2M1 = 2, kGridE2M1C = 3;
 
 // ---------------------------------------------------------------- bf16
 // A dword holds two bf16 values; each is the upper half of a binary32.
@@ -138,15 +140,19 @@ __device__ __forceinline__ float e4m3_decode_pos(uint32_t c) {
 
 // emax of the element format (floor(log2(Qmax))) for the E8M0 exponent.
 template <int GRID>
-__device__ __forceinline__ int grid_emax() { return GRID == kGridE1M2 ? 1 : 2; }
+__device__ __forceinline__ int grid_emax() { return (GRID == kGridE1M2 || GRID == kGridE2M1C) ? 1 : 2; }
 
 template <int GRID>
-__device__ __forceinline__ float grid_qmax() {
-  return GRID == kGridE1M2 ? 3.5f : (GRID == kGridINT4 ? 7.0f : 6.0f);
+__device__ __forceinline__ constexpr float grid_qmax() {
+  return GRID == kGridE1M2 ? 3.5f : (GRID == kGridINT4 ? 7.0f : (GRID == kGridE2M1 ? 6.0f : 2.0f));
 }
 
+// Largest magnitude index of the grid.
+template <int GRID>
+__device__ __forceinline__ constexpr uint32_t grid_top() { return GRID == kGridE2M1C ? 4u : 7u; }
+
 __device__ __forceinline__ float qmax_of(int grid) {
-  return grid == kGridE1M2 ? 3.5f : (grid == kGridINT4 ? 7.0f : 6.0f);
+  return grid == kGridE1M2 ? 3.5f : (grid == kGridINT4 ? 7.0f : (grid == kGridE2M1 ? 6.0f : 2.0f));
 }
 
 // MX32 scale of a block: exponent X = clamp(floor(log2 amax) - emax, -127, 127)
@@ -179,8 +185,8 @@ template <int GRID>
 __device__ __forceinline__ uint32_t round_rtne(float y) {
   const float a = fabsf(y);
   uint32_t k;
-  if (GRID == kGridE1M2) {
-    k = (uint32_t)__builtin_rintf(fminf(a + a, 7.0f));
+  if (GRID == kGridE1M2 || GRID == kGridE2M1C) {
+    k = (uint32_t)__builtin_rintf(fminf(a + a, (float)grid_top<GRID>()));
   } else if (GRID == kGridINT4) {
     k = (uint32_t)__builtin_rintf(fminf(a, 7.0f));
   } else {
@@ -199,10 +205,10 @@ __device__ __forceinline__ uint32_t round_sr(float y, uint32_t r) {
   if (!(a == a)) return 0u;
   uint32_t k;
   if (a >= grid_qmax<GRID>()) {
-    k = 7u;
+    k = grid_top<GRID>();
   } else {
     float lo_idx, frac;
-    if (GRID == kGridE1M2) {
+    if (GRID == kGridE1M2 || GRID == kGridE2M1C) {
       const float t = a + a;
       lo_idx = floorf(t);
       frac = t - lo_idx;

@@ -60,6 +60,7 @@ hipError_t launch_dequant(const DequantParams& p, hipStream_t s) {
     case kGridE1M2: hipLaunchKernelGGL(ufp4_dequant_kernel<kGridE1M2>, dim3((unsigned)blocks), dim3(256), 0, s, p); break;
     case kGridINT4: hipLaunchKernelGGL(ufp4_dequant_kernel<kGridINT4>, dim3((unsigned)blocks), dim3(256), 0, s, p); break;
     case kGridE2M1: hipLaunchKernelGGL(ufp4_dequant_kernel<kGridE2M1>, dim3((unsigned)blocks), dim3(256), 0, s, p); break;
+    case kGridE2M1C: hipLaunchKernelGGL(ufp4_dequant_kernel<kGridE2M1C>, dim3((unsigned)blocks), dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -154,6 +155,7 @@ hipError_t launch_stats(const StatsParams& p, hipStream_t s) {
     case kGridE1M2: hipLaunchKernelGGL(ufp4_stats_kernel<kGridE1M2>, dim3(p.n_wg), dim3(256), 0, s, p); break;
     case kGridINT4: hipLaunchKernelGGL(ufp4_stats_kernel<kGridINT4>, dim3(p.n_wg), dim3(256), 0, s, p); break;
     case kGridE2M1: hipLaunchKernelGGL(ufp4_stats_kernel<kGridE2M1>, dim3(p.n_wg), dim3(256), 0, s, p); break;
+    case kGridE2M1C: hipLaunchKernelGGL(ufp4_stats_kernel<kGridE2M1C>, dim3(p.n_wg), dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -195,6 +197,7 @@ hipError_t launch_round(const float* y, int64_t n, int32_t grid, int32_t roundin
     case kGridE1M2: launch_round_grid<kGridE1M2>(y, n, sr, k0, k1, codes, blocks, s); break;
     case kGridINT4: launch_round_grid<kGridINT4>(y, n, sr, k0, k1, codes, blocks, s); break;
     case kGridE2M1: launch_round_grid<kGridE2M1>(y, n, sr, k0, k1, codes, blocks, s); break;
+    case kGridE2M1C: launch_round_grid<kGridE2M1C>(y, n, sr, k0, k1, codes, blocks, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -481,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
   }
   if (!T.active) return;  // uniform per workgroup
   const LaneGeom L = lane_geom(p, T);
-  constexpr float qmax = GRID == kGridE1M2 ? 3.5f : (GRID == kGridINT4 ? 7.0f : 6.0f);
+  constexpr float qmax = grid_qmax<GRID>();
   TensorScale tsr{1.0f, qmax, 1.0f / qmax, false}, tsc = tsr;
   // Phase-A partials of the segment: the first 4 per thread are requested
   // before the tile, so their latency overlaps the tile loads.  The loads are
@@ -569,8 +569,9 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
   const int64_t C = p.cols;
   // RTNE onto E1M2/INT4 has an exact fast form; it needs no clamp when the
   // block scale is a normal E4M3 value (then |y| <= 1.0625 Qmax).
-  constexpr bool kFastGrid = !SR && (GRID == kGridE1M2 || GRID == kGridINT4);
-  constexpr float kGridMul = GRID == kGridE1M2 ? 2.0f : 1.0f;  // grid step -> integer
+  constexpr bool kFastGrid = !SR && GRID != kGridE2M1;  // uniform grids
+  constexpr float kGridMul = GRID == kGridINT4 ? 1.0f : 2.0f;  // grid step -> integer
+  constexpr float kTop = (float)grid_top<GRID>();              // MX32 clamp, in grid steps
   // Addresses: a uniform tile base plus a 32-bit per-lane offset.
   const int64_t tile_row0 = T.seg_row0 + T.m0;
   const uint32_t lrow = (uint32_t)(32 * L.wave + 16 * L.half);  // lane's first row in the tile
@@ -619,10 +620,10 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             float t = v[r][j] * mult;
-            if (MX) t = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
+            if (MX) t = __builtin_amdgcn_fmed3f(t, -kTop, kTop);
             acc = push_nibble(__float_as_uint(t + kMagic), acc);
           }
-          packed[r] = GRID == kGridE1M2 ? tc_to_signmag8(acc) : acc;
+          packed[r] = GRID == kGridINT4 ? acc : tc_to_signmag8(acc);
         }
       } else {
 #pragma unroll
@@ -700,14 +701,14 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
           for (int j = 0; j < 8; ++j) {
             float t0 = v[r][j] * mult, t1 = v[r][8 + j] * mult;
             if (MX) {
-              t0 = __builtin_amdgcn_fmed3f(t0, -7.0f, 7.0f);
-              t1 = __builtin_amdgcn_fmed3f(t1, -7.0f, 7.0f);
+              t0 = __builtin_amdgcn_fmed3f(t0, -kTop, kTop);
+              t1 = __builtin_amdgcn_fmed3f(t1, -kTop, kTop);
             }
             a0 = push_nibble(__float_as_uint(t0 + kMagic), a0);
             a1 = push_nibble(__float_as_uint(t1 + kMagic), a1);
           }
-          lo[r] = GRID == kGridE1M2 ? tc_to_signmag8(a0) : a0;
-          hi[r] = GRID == kGridE1M2 ? tc_to_signmag8(a1) : a1;
+          lo[r] = GRID == kGridINT4 ? a0 : tc_to_signmag8(a0);
+          hi[r] = GRID == kGridINT4 ? a1 : tc_to_signmag8(a1);
         }
       } else {
 #pragma unroll
@@ -886,6 +887,7 @@ hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s, hipEv
     case kGridE1M2: return launch_quant_mx<kGridE1M2>(p, grid, sr, s, t0, t1);
     case kGridINT4: return launch_quant_mx<kGridINT4>(p, grid, sr, s, t0, t1);
     case kGridE2M1: return launch_quant_mx<kGridE2M1>(p, grid, sr, s, t0, t1);
+    case kGridE2M1C: return launch_quant_mx<kGridE2M1C>(p, grid, sr, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }

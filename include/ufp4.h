@@ -25,8 +25,9 @@
  *      scale (NVFP4-style), or by a power-of-two E8M0 scale per 32 elements
  *      (MXFP4-style);
  *   3. rounds onto the uniform E1M2 grid {0, .5, ..., 3.5}, symmetric INT4
- *      {-7..7} or the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}, with
- *      round-to-nearest-even or Philox-driven stochastic rounding;
+ *      {-7..7}, the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6} or E2M1 clamped
+ *      to its uniform part {0, .5, 1, 1.5, 2}, with round-to-nearest-even
+ *      or Philox-driven stochastic rounding;
  *   4. packs two 4-bit codes per byte.
  * Outputs come in the row-wise layout (blocks along a row; the fwd_y and
  * bwd_dx operands) and the column-wise layout (blocks down a column, stored
@@ -70,7 +71,13 @@ enum ufp4_status {
   UFP4_ERR_OFFSETS = 6           /* grouped offsets were found invalid on the device */
 };
 
-enum ufp4_grid { UFP4_GRID_E1M2 = 0, UFP4_GRID_INT4 = 1, UFP4_GRID_E2M1 = 2 };
+/* Code layouts: E1M2, E2M1 and E2M1C store sign | magnitude index (index 0..7,
+ * 0..7, 0..4); INT4 stores the two's-complement integer.  E2M1C is E2M1 with
+ * its range clamped to the uniformly spaced magnitudes {0, .5, 1, 1.5, 2}
+ * (Qmax 2, MX32 element emax 1): the "simulated uniform" E2M1 alternative of
+ * "Shrinkage Bias: The Hidden Geometric Trap in FP4 Training" (zhichai.net),
+ * section "Key points", validation results. */
+enum ufp4_grid { UFP4_GRID_E1M2 = 0, UFP4_GRID_INT4 = 1, UFP4_GRID_E2M1 = 2, UFP4_GRID_E2M1C = 3 };
 enum ufp4_rounding { UFP4_ROUND_RTNE = 0, UFP4_ROUND_STOCHASTIC = 1 };
 /* NV16: E4M3 scale per 16 elements + FP32 per-tensor scale.
  * MX32: E8M0 (power-of-two) scale per 32 elements, no tensor scale (1.0). */

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libufp4_oracle.so")
 SOURCES = [os.path.join(_HERE, "ufp4_oracle.c")]
 
-GRID_E1M2, GRID_INT4, GRID_E2M1 = 0, 1, 2
+GRID_E1M2, GRID_INT4, GRID_E2M1, GRID_E2M1_CLAMP = 0, 1, 2, 3
 ROUND_RTNE, ROUND_SR = 0, 1
 SCALE_NV16, SCALE_MX32 = 0, 1
 LAYOUT_ROW, LAYOUT_COL = 0, 1

@@ -171,20 +171,29 @@ float orc_e4m3_decode(uint8_t c) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* The three 4-bit grids: magnitudes indexed by the 3 magnitude bits.        */
+/* The 4-bit grids: magnitudes indexed by the 3 magnitude bits.  The clamped
+ * E2M1 grid keeps E2M1's codes but only its uniformly spaced part, indices
+ * 0..4 ({0, 0.5, 1, 1.5, 2}): E2M1 with its range clamped to imitate a
+ * uniform grid, the alternative [Z] "Key points" (validation results) reports
+ * as not recovering the uniform grid's accuracy.                           */
 static const float kE1M2[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 2.5f, 3.0f, 3.5f};
 static const float kINT4[8] = {0.0f, 1.0f, 2.0f, 3.0f, 4.0f, 5.0f, 6.0f, 7.0f};
 static const float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 
 static const float* grid_mags(int32_t grid) {
-  return grid == ORC_GRID_INT4 ? kINT4 : grid == ORC_GRID_E2M1 ? kE2M1 : kE1M2;
+  return grid == ORC_GRID_INT4 ? kINT4 : (grid == ORC_GRID_E2M1 || grid == ORC_GRID_E2M1_CLAMP) ? kE2M1 : kE1M2;
 }
 
-float orc_grid_qmax(int32_t grid) { return grid_mags(grid)[7]; }
+/* Largest magnitude index the grid uses. */
+static int grid_top(int32_t grid) { return grid == ORC_GRID_E2M1_CLAMP ? 4 : 7; }
+
+float orc_grid_qmax(int32_t grid) { return grid_mags(grid)[grid_top(grid)]; }
 
 /* emax of the element format, used by the E8M0 shared exponent (OCP MX):
  * floor(log2(Qmax)).                                                        */
-static int grid_emax(int32_t grid) { return grid == ORC_GRID_E1M2 ? 1 : 2; }
+static int grid_emax(int32_t grid) {
+  return (grid == ORC_GRID_E1M2 || grid == ORC_GRID_E2M1_CLAMP) ? 1 : 2;
+}
 
 /* Code layout.  E1M2 and E2M1: sign << 3 | magnitude index (the magnitude
  * index equals the format's own bit pattern).  INT4: 4-bit two's complement.
@@ -213,14 +222,15 @@ float orc_code_value(uint8_t code, int32_t grid) {
 uint8_t orc_round_to_code(float y, int32_t grid, int32_t rounding, uint32_t r32) {
   if (y != y) return 0;
   const float* g = grid_mags(grid);
+  const int top = grid_top(grid);
   float a = fabsf(y);
   int neg = signbit(y) ? 1 : 0;
   int k;
-  if (a >= g[7]) {
-    k = 7;
+  if (a >= g[top]) {
+    k = top;
   } else {
     int i = 0;
-    while (i < 6 && g[i + 1] <= a) ++i;   /* g[i] <= a < g[i+1] */
+    while (i < top - 1 && g[i + 1] <= a) ++i;   /* g[i] <= a < g[i+1] */
     float lo = g[i], hi = g[i + 1];
     if (rounding == ORC_ROUND_SR) {
       /* a - lo is exact (lo == 0, or lo <= a <= hi <= 2 lo); hi - lo is a
@@ -338,7 +348,7 @@ static void block_scale(const orc_config* cfg, float S_t, float amax_b,
 static float tensor_scale_from_amax(const orc_config* cfg, float amax_t) {
   if (cfg->scaling == ORC_SCALE_MX32) return 1.0f;
   if (!(amax_t > 0.0f)) return 1.0f;      /* all-zero tensor: S_t = 1 */
-  float qmax448 = orc_grid_qmax(cfg->grid) * 448.0f;  /* 1568, 3136, 2688: exact */
+  float qmax448 = orc_grid_qmax(cfg->grid) * 448.0f;  /* 1568, 3136, 2688, 896: exact */
   return amax_t / qmax448;
 }
 
@@ -385,7 +395,7 @@ static float quantize_lineset(const lineset* L, const orc_config* cfg, uint8_t* 
 
 static int check_cfg(const orc_config* cfg) {
   if (!cfg) return 1;
-  if (cfg->grid < 0 || cfg->grid > 2) return 1;
+  if (cfg->grid < 0 || cfg->grid > 3) return 1;
   if (cfg->rounding < 0 || cfg->rounding > 1) return 1;
   if (cfg->scaling < 0 || cfg->scaling > 1) return 1;
   return 0;

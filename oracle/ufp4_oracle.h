@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-enum { ORC_GRID_E1M2 = 0, ORC_GRID_INT4 = 1, ORC_GRID_E2M1 = 2 };
+enum { ORC_GRID_E1M2 = 0, ORC_GRID_INT4 = 1, ORC_GRID_E2M1 = 2, ORC_GRID_E2M1_CLAMP = 3 };
 enum { ORC_ROUND_RTNE = 0, ORC_ROUND_SR = 1 };
 enum { ORC_SCALE_NV16 = 0, ORC_SCALE_MX32 = 1 };
 enum { ORC_LAYOUT_ROW = 0, ORC_LAYOUT_COL = 1 };

@@ -72,7 +72,7 @@ def call_quant(F, rows=64, cols=64, ld=64, cfg=None, out=None, ws=FAKE, ws_bytes
 
 
 def test_quantize_argument_errors(F):
-    assert call_quant(F, cfg=F.config(grid=3)) == 1
+    assert call_quant(F, cfg=F.config(grid=4)) == 1
     assert call_quant(F, cfg=F.config(rounding=2)) == 1
     assert call_quant(F, cfg=F.config(scaling=5)) == 1
     assert call_quant(F, cfg=F.config(rht=2)) == 1
@@ -127,7 +127,7 @@ def test_other_entry_point_errors(F):
     assert F.lib.ufp4_stats(None, 16, 16, 16, 0, ctypes.byref(cfg), None, None, None, None, 0,
                             ctypes.byref(st), None) == 4
     assert F.lib.ufp4_round_f32(None, 10, 0, 0, 0, None, None) == 1
-    assert F.lib.ufp4_round_f32(None, 10, 3, 0, 0, None, None) == 1
+    assert F.lib.ufp4_round_f32(None, 10, 4, 0, 0, None, None) == 1
     assert F.lib.ufp4_round_f32(None, 0, 0, 0, 0, None, None) == 0
     assert F.lib.ufp4_rht_signs(0, None) == 1
     assert F.lib.ufp4_workspace_init(None, 0, None) == 4

@@ -18,7 +18,7 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-E1M2, INT4, E2M1 = 0, 1, 2
+E1M2, INT4, E2M1, E2M1C = 0, 1, 2, 3
 RTNE, SR = 0, 1
 NV16, MX32 = 0, 1
 ROW, COL = 0, 1
@@ -79,7 +79,7 @@ def test_weight_grid_sweep_2048x8192(env):
     x = to_dev(torch, xb)
     ws = F.Workspace(2048, 8192)
     floor = 1e-6 * float(np.mean(np.abs(synth.bf16_to_f32(xb))))
-    for grid in (E1M2, INT4, E2M1):
+    for grid in (E1M2, INT4, E2M1, E2M1C):
         for rht in (1, 0):
             say(f"[full] weight 2048x8192 grid={grid} rht={rht} row + stats")
             fc = F.config(grid, RTNE, NV16, rht, 2, 2)

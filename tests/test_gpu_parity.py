@@ -13,7 +13,7 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-E1M2, INT4, E2M1 = 0, 1, 2
+E1M2, INT4, E2M1, E2M1C = 0, 1, 2, 3
 RTNE, SR = 0, 1
 NV16, MX32 = 0, 1
 ROW, COL = 0, 1
@@ -85,7 +85,7 @@ def assert_layout_equal(q, ref, what):
 
 
 # ------------------------------------------------------------- rounding hook
-@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
 @pytest.mark.parametrize("rounding", [RTNE, SR])
 def test_round_f32_all_bf16_patterns(env, grid, rounding):
     torch, F, orc = env
@@ -107,7 +107,7 @@ def test_round_f32_dense_fp32_sweep(env):
     y = np.concatenate([bits.view(np.float32), -bits.view(np.float32)])
     yd = torch.from_numpy(y).cuda()
     codes = torch.empty(y.size, dtype=torch.uint8, device="cuda")
-    for grid in (E1M2, INT4, E2M1):
+    for grid in (E1M2, INT4, E2M1, E2M1C):
         for rounding in (RTNE, SR):
             F.ufp4_round_f32(yd, grid, rounding, 9, codes)
             np.testing.assert_array_equal(codes.cpu().numpy(), orc.round_f32(y, grid, rounding, sr_seed=9))
@@ -126,7 +126,7 @@ def test_tiny_config_row(env):
 SHAPES = [(384, 320), (160, 512), (32, 2048)]
 
 
-@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
 @pytest.mark.parametrize("rounding", [RTNE, SR])
 @pytest.mark.parametrize("scaling", [NV16, MX32])
 @pytest.mark.parametrize("rht", [1, 0])
@@ -166,7 +166,7 @@ def test_edge_values(env):
                                          (10.0 ** np.random.default_rng(6).integers(-30, 30, (R, C))).astype(np.float32)),
     }
     for name, xb in cases.items():
-        for grid in (E1M2, INT4, E2M1):
+        for grid in (E1M2, INT4, E2M1, E2M1C):
             for scaling in (NV16, MX32):
                 for rounding in (RTNE, SR):
                     say(f"[edge] {name} grid={grid} scl={scaling} rnd={rounding}")
@@ -269,7 +269,7 @@ def test_grouped_single_outputs_and_bad_offsets(env):
 
 
 # ------------------------------------------------------- dequantize / stats
-@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
 @pytest.mark.parametrize("scaling", [NV16, MX32])
 def test_dequantize_bit_exact(env, grid, scaling):
     torch, F, orc = env
@@ -296,7 +296,7 @@ def assert_stats_close(g, o, floor):
         assert abs(a - b) <= 1e-6 * max(abs(a), abs(b)) + floor, (k, a, b)
 
 
-@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1])
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
 @pytest.mark.parametrize("layout", [ROW, COL])
 def test_stats_match_oracle(env, grid, layout):
     torch, F, orc = env

@@ -227,12 +227,18 @@ def test_e4m3_saturates(orc):
 
 
 # ------------------------------------------------------------ grid rounding
-GRID_IDS = {"E1M2": 0, "INT4": 1, "E2M1": 2}
+GRID_IDS = {"E1M2": 0, "INT4": 1, "E2M1": 2, "E2M1_CLAMP": 3}
+ALL_GRIDS = ["E1M2", "INT4", "E2M1", "E2M1_CLAMP"]
 
 
 def _grid_mags(orc):
     g = _golden_grids()
-    return {"E1M2": g["E1M2"], "E2M1": g["E2M1"], "INT4": np.arange(8.0)}
+    e2m1 = g["E2M1"]
+    # The clamped grid is E2M1 limited to its uniformly spaced part: the
+    # printed E2M1 magnitudes up to the first step that is not 0.5.
+    steps = np.diff(e2m1)
+    uniform_end = int(np.argmax(steps != 0.5)) + 1
+    return {"E1M2": g["E1M2"], "E2M1": e2m1, "INT4": np.arange(8.0), "E2M1_CLAMP": e2m1[:uniform_end]}
 
 
 def _brute_force_codes(y, mags, int4):
@@ -242,12 +248,12 @@ def _brute_force_codes(y, mags, int4):
     with np.errstate(invalid="ignore"):
         d = np.abs(a[:, None] - mags[None, :])
     best = d.min(axis=1, keepdims=True)
-    idx = np.arange(8)[None, :]
+    idx = np.arange(len(mags))[None, :]
     ties = d == best
     even = np.where(ties & (idx % 2 == 0), idx, 99).min(axis=1)
     any_ = np.where(ties, idx, 99).min(axis=1)
     k = np.where(even < 99, even, any_)
-    k = np.where(a >= mags[-1], 7, k)
+    k = np.where(a >= mags[-1], len(mags) - 1, k)
     neg = np.signbit(y)
     if int4:
         code = np.where(neg, (16 - k) % 16, k)
@@ -258,7 +264,7 @@ def _brute_force_codes(y, mags, int4):
     return code.astype(np.uint8)
 
 
-@pytest.mark.parametrize("grid", ["E1M2", "INT4", "E2M1"])
+@pytest.mark.parametrize("grid", ALL_GRIDS)
 def test_rtne_exhaustive_bf16_vs_brute_force(orc, grid):
     y = synth.all_bf16_patterns()
     got = orc.round_f32(y, GRID_IDS[grid], 0)
@@ -266,10 +272,10 @@ def test_rtne_exhaustive_bf16_vs_brute_force(orc, grid):
     np.testing.assert_array_equal(got, want)
 
 
-@pytest.mark.parametrize("grid", ["E1M2", "INT4", "E2M1"])
+@pytest.mark.parametrize("grid", ALL_GRIDS)
 def test_code_values_match_printed_grid(orc, grid):
     mags = _grid_mags(orc)[grid]
-    for k in range(8):
+    for k in range(len(mags)):
         assert orc.code_value(k, GRID_IDS[grid]) == mags[k]
         neg = (16 - k) % 16 if grid == "INT4" else 8 | k
         if k:
@@ -295,6 +301,20 @@ def test_e2m1_bucket_bias_matches_page(orc):
     vals = np.array([orc.code_value(c, 2) for c in range(16)])[codes]
     assert np.all(vals == q)
     assert abs(np.mean(vals - y.astype(np.float64)) - mean) < 1e-4
+
+
+def test_clamped_e2m1_is_uniform_and_saturates_at_two(orc):
+    mags = _grid_mags(orc)["E2M1_CLAMP"]
+    assert np.array_equal(mags, [0.0, 0.5, 1.0, 1.5, 2.0]) and orc.grid_qmax(3) == 2.0
+    # interior buckets are symmetric, as for E1M2: no rounding bias
+    n = 1 << 20
+    for q in (0.5, 1.0, 1.5):
+        y = (q - 0.25 + (np.arange(n) + 0.5) * 0.5 / n).astype(np.float32)
+        vals = np.array([orc.code_value(c, 3) for c in range(16)])[orc.round_f32(y, 3, 0)]
+        assert np.all(vals == q) and abs(np.mean(vals - y.astype(np.float64))) < 1e-6
+    # everything from 2 up to E2M1's own range ends at the largest code
+    y = np.array([2.0, 2.4, 3.0, 5.9, 6.0, 1e30], np.float32)
+    assert np.all(orc.round_f32(y, 3, 0) == 4) and np.all(orc.round_f32(-y, 3, 0) == 12)
 
 
 def test_e1m2_bucket_unbiased(orc):
