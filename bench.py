@@ -2,6 +2,7 @@
 activation on one MI355X, reported as HBM GB/s (algorithmic bytes / time).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--warm] [--copy]
+                [--schedule auto|two-pass|single-pass]
 
 A step is one ufp4_quantize_rowcol call (every stage of the hot path: load,
 random signs, 16-point Walsh-Hadamard transform, tensor and block maxima,
@@ -13,11 +14,14 @@ HBM.  Steps rotate over enough input/output buffer sets (>= 600 MB) that the
 Algorithmic bytes per call: 2 B/element read (bf16) + 2 x 0.5 B/element codes
 + 2 x 1/16 B/element E4M3 scales + 2 x 4 B tensor scales.
 
-A call runs two kernels: the tensor-maximum pass (reads the input) and the
-quantization pass (reads the input again and writes every output).  The
-roofline object describes the quantization kernel, the dominant one: its
-algorithmic bytes per launch are the call's (input once, all outputs), and its
-duration is the mean of hipEvent intervals recorded on the launch stream
+The default schedule runs two kernels: the tensor-maximum pass (reads the
+input) and the quantization pass (reads the input again and writes every
+output).  The single-pass schedule (one kernel that keeps each tile on chip
+while the tile maxima are exchanged device-wide) is timed beside it.  The
+roofline object describes the dominant kernel (the two-pass quantization
+kernel, or the single-pass kernel under --schedule single-pass): its
+algorithmic bytes per launch are the call's (input once, all outputs), and
+its duration is the mean of hipEvent intervals recorded on the launch stream
 around that kernel alone, over calls that rotate through the buffer sets.
 
 The oracle leg (cpu_baseline) times the single-threaded CPU oracle on the same
@@ -55,10 +59,10 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
-def counter_traffic():
-    """HBM bytes per launch of the quantization kernel and per call, from the
-    committed rocprofv3 counter summary, if it was taken on the current kernel
-    sources; else (None, None)."""
+def counter_traffic(single: bool):
+    """HBM bytes per launch of the dominant kernel and per call under the
+    schedule, from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else (None, None)."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
@@ -66,9 +70,13 @@ def counter_traffic():
         return None, None
     if c.get("kernel_source_sha256") != kernel_source_sha():
         return None, None
-    return c.get("hbm_bytes_quant_kernel"), c.get("hbm_bytes_per_call")
+    h = c.get("hbm_bytes", {})
+    if single:
+        return h.get("single_pass_kernel"), h.get("single_pass_kernel")
+    return h.get("two_pass_quant_kernel"), h.get("two_pass_call")
 
 
+FUSED_KERNEL = "ufp4_fused_kernel<0, false, true>"
 AMAX_KERNEL = "ufp4_amax_kernel<true>"
 QUANT_KERNEL = "ufp4_quant_kernel<0, false, false, true>"
 
@@ -103,8 +111,9 @@ def _counter_means(csv_dir, counter):
 
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
     """Write the counter summary bench.py reads: HBM bytes per launch of the
-    quantization kernel and per call, each counter scaled by what it reads
-    for a plain 512 MiB device copy."""
+    single-pass kernel, of the two-pass quantization kernel and per two-pass
+    call, each counter scaled by what it reads for a plain 512 MiB device
+    copy."""
     fetch, _ = _counter_means(fetch_dir, "FETCH_SIZE")
     write, _ = _counter_means(write_dir, "WRITE_SIZE")
     _, copy_fetch = _counter_means(copy_fetch_dir, "FETCH_SIZE")
@@ -118,16 +127,20 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
             raise SystemExit(f"kernel {key!r}: found {hits}")
         return hits[0], d[hits[0]]
 
+    kf, ff_ = pick(fetch, FUSED_KERNEL)
     ka, fa = pick(fetch, AMAX_KERNEL)
     kq, fq = pick(fetch, QUANT_KERNEL)
+    _, wf_ = pick(write, FUSED_KERNEL)
     _, wa = pick(write, AMAX_KERNEL)
     _, wq = pick(write, QUANT_KERNEL)
+    fused = (ff_ * ff + wf_ * wf) * 1024
     quant = (fq * ff + wq * wf) * 1024
     call = quant + (fa * ff + wa * wf) * 1024
-    out = {"fetch_kib_raw": {ka: fa, kq: fq}, "write_kib_raw": {ka: wa, kq: wq},
+    out = {"fetch_kib_raw": {kf: ff_, ka: fa, kq: fq}, "write_kib_raw": {kf: wf_, ka: wa, kq: wq},
            "copy_calibration": {"copy_bytes": copy_kib * 1024, "fetch_kib_raw": copy_fetch,
                                 "write_kib_raw": copy_write, "fetch_factor": ff, "write_factor": wf},
-           "hbm_bytes_quant_kernel": round(quant), "hbm_bytes_per_call": round(call),
+           "hbm_bytes": {"single_pass_kernel": round(fused), "two_pass_quant_kernel": round(quant),
+                         "two_pass_call": round(call)},
            "algorithmic_bytes_per_call": algorithmic_bytes(ROWS, COLS),
            "kernel_source_sha256": kernel_source_sha(), "commands": commands,
            "note": "KiB per dispatch, mean over dispatches; bytes = (fetch * fetch_factor + "
@@ -235,6 +248,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true",
                     help="also time repeated calls on one buffer set (input cache-resident)")
+    ap.add_argument("--schedule", choices=("auto", "two-pass", "single-pass"), default="auto",
+                    help="schedule of the timed calls (the other one is timed beside it)")
     ap.add_argument("--copy", action="store_true",
                     help="time a plain device copy of 512 MiB instead (bandwidth and counter calibration)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -302,6 +317,9 @@ def main():
             fns.append(fn)
         return fns
 
+    modes = {"auto": F.SCHEDULE_AUTO, "two-pass": F.SCHEDULE_TWO_PASS, "single-pass": F.SCHEDULE_SINGLE_PASS}
+    F.ufp4_set_schedule(modes[args.schedule])
+    single = F.ufp4_schedule_of(ROWS, COLS, cfg) == F.SCHEDULE_SINGLE_PASS
     on, off = prebuilt(cfg), prebuilt(cfg_off)
     ms, graph = time_graph(torch, on, args.steps, args.warmup, stream)
     ms_off, _ = time_graph(torch, off, args.steps, args.warmup, stream)
@@ -315,6 +333,19 @@ def main():
         per_kernel.append(F.ufp4_time_rowcol(x, cfg, row, col, ws, stream))
     k_amax = np.array([a for a, _ in per_kernel])
     k_quant = np.array([b for _, b in per_kernel])
+    # the other schedule on the same buffers, for comparison
+    other = "two_pass" if single else "single_pass"
+    F.ufp4_set_schedule(F.SCHEDULE_TWO_PASS if single else F.SCHEDULE_SINGLE_PASS)
+    ms_other, _ = time_graph(torch, on, args.steps, args.warmup, stream)
+    tk = []
+    for i in range(args.steps):
+        x, row, col, ws = sets[i % len(sets)]
+        tk.append(F.ufp4_time_rowcol(x, cfg, row, col, ws, stream))
+    two = {f"{other}_ms": round(ms_other, 6),
+           f"{other}_amax_kernel_ms_mean": round(float(np.mean([a for a, _ in tk])), 6),
+           f"{other}_quant_kernel_ms_mean": round(float(np.mean([b for _, b in tk])), 6),
+           f"{other}_time_ratio": round(ms_other / ms, 4)}
+    F.ufp4_set_schedule(modes[args.schedule])
     # the graph's outputs equal an eager call's
     x, row, col, ws = sets[0]
     ref_row, ref_col = row.codes.clone(), col.codes.clone()
@@ -326,7 +357,7 @@ def main():
 
     nbytes = algorithmic_bytes(ROWS, COLS)
     gbps = nbytes / (ms * 1e-3) / 1e9
-    traffic_quant, traffic_call = counter_traffic()
+    traffic_quant, traffic_call = counter_traffic(single)
     quant_gbps = nbytes / (float(k_quant.mean()) * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -347,7 +378,8 @@ def main():
                    "algorithmic_bytes_per_call": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(quant_gbps, 2), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(quant_gbps / PEAK_GBPS, 4), "traffic": traffic_quant,
-                     "kernel": "ufp4_quant_kernel<E1M2, RTNE, NV16, RHT>",
+                     "kernel": ("ufp4_fused_kernel<E1M2, RTNE, RHT> (single pass)" if single
+                                else "ufp4_quant_kernel<E1M2, RTNE, NV16, RHT>"),
                      "bytes_per_launch": nbytes,
                      "kernel_ms_mean": round(float(k_quant.mean()), 6)},
         "extra": {"elements_per_s": round(ROWS * COLS / (ms * 1e-3), 1),
@@ -360,8 +392,11 @@ def main():
                   "rht_off_ms": round(ms_off, 6),
                   "rht_overhead": round(ms / ms_off - 1.0, 4),
                   "eager_launch_ms": round(ms_eager, 6),
+                  "schedule": "single-pass" if single else "two-pass",
                   "timing": "HIP graph of the K calls, one replay, hipEvents on the launch stream"},
     }
+    if two:
+        line["extra"].update(two)
     if ms_warm is not None:
         line["extra"]["warm_same_buffer_ms"] = round(ms_warm, 6)
         line["extra"]["warm_same_buffer_gbps"] = round(nbytes / (ms_warm * 1e-3) / 1e9, 2)

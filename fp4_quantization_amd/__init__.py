@@ -13,11 +13,12 @@ import numpy as np
 import torch
 
 from ._lib import (GRID_E1M2, GRID_E2M1, GRID_E2M1C, GRID_INT4, LIB_PATH, ROUND_RTNE, ROUND_STOCHASTIC,
-                   SCALE_MX32, SCALE_NV16, Ufp4Error, check, lib, ufp4_config, ufp4_qtensor,
+                   SCALE_MX32, SCALE_NV16, SCHEDULE_AUTO, SCHEDULE_SINGLE_PASS, SCHEDULE_TWO_PASS, Ufp4Error, check, lib, ufp4_config, ufp4_qtensor,
                    ufp4_stats_t)
 
 __all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "GRID_E2M1C", "ROUND_RTNE", "ROUND_STOCHASTIC", "SCALE_NV16",
-           "SCALE_MX32", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
+           "SCALE_MX32", "SCHEDULE_AUTO", "SCHEDULE_TWO_PASS", "SCHEDULE_SINGLE_PASS", "ufp4_set_schedule",
+           "ufp4_schedule_of", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
            "ufp4_quantize", "ufp4_quantize_rowcol", "ufp4_quantize_grouped", "ufp4_dequantize",
            "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol",
            "block_len"]
@@ -123,11 +124,28 @@ def ufp4_quantize_grouped(x: torch.Tensor, offsets_dev: torch.Tensor, padded_row
                                     ws.nbytes if ws else 0, _stream(stream)))
 
 
+def ufp4_set_schedule(schedule: int, left_stride: int = 0) -> None:
+    """Process-wide schedule of dense NV16 calls (SCHEDULE_AUTO, _TWO_PASS,
+    _SINGLE_PASS); left_stride > 1 makes the single pass leave every tile whose
+    index is not a multiple of it to the other workgroups (test hook)."""
+    check("ufp4_set_schedule", lib.ufp4_set_schedule(int(schedule), int(left_stride)))
+
+
+def ufp4_schedule_of(rows: int, cols: int, cfg: ufp4_config, num_groups: int = 1) -> int:
+    """SCHEDULE_SINGLE_PASS or SCHEDULE_TWO_PASS: what a call on this shape
+    and configuration takes on the current device."""
+    out = ctypes.c_int32(0)
+    check("ufp4_schedule_of", lib.ufp4_schedule_of(int(rows), int(cols), int(num_groups), ctypes.byref(cfg),
+                                                   ctypes.byref(out)))
+    return out.value
+
+
 def ufp4_time_rowcol(x: torch.Tensor, cfg: ufp4_config, row_out: QTensor, col_out: QTensor,
                      ws: Workspace, stream=None) -> tuple[float, float]:
-    """One ufp4_quantize_rowcol call with hipEvents around each of its two
+    """One ufp4_quantize_rowcol call with hipEvents around each of its
     kernels; returns (ms of the tensor-maximum kernel, ms of the quantization
-    kernel).  Synchronizes."""
+    kernel); under the single-pass schedule (0, ms of the one kernel).
+    Synchronizes."""
     rows, cols, ld = _bf16_view(x)
     a, b = ctypes.c_float(0), ctypes.c_float(0)
     check("ufp4_time_rowcol", lib.ufp4_time_rowcol(_ptr(x), rows, cols, ld, ctypes.byref(cfg), row_out.c(),

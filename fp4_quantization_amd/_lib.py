@@ -15,16 +15,18 @@ LIB_PATH = os.path.join(_HERE, "libufp4.so")
 UFP4_OK = 0
 STATUS_NAMES = {0: "UFP4_OK", 1: "UFP4_ERR_INVALID_ARGUMENT", 2: "UFP4_ERR_SHAPE",
                 3: "UFP4_ERR_ALIGNMENT", 4: "UFP4_ERR_WORKSPACE", 5: "UFP4_ERR_HIP",
-                6: "UFP4_ERR_OFFSETS"}
+                6: "UFP4_ERR_OFFSETS", 7: "UFP4_ERR_SYNC"}
 
 GRID_E1M2, GRID_INT4, GRID_E2M1, GRID_E2M1C = 0, 1, 2, 3
 ROUND_RTNE, ROUND_STOCHASTIC = 0, 1
 SCALE_NV16, SCALE_MX32 = 0, 1
+SCHEDULE_AUTO, SCHEDULE_TWO_PASS, SCHEDULE_SINGLE_PASS = 0, 1, 2
 
 EXPORTED = ["ufp4_status_string", "ufp4_workspace_size", "ufp4_workspace_init",
             "ufp4_workspace_status", "ufp4_quantize", "ufp4_quantize_rowcol",
             "ufp4_quantize_grouped", "ufp4_dequantize", "ufp4_stats", "ufp4_round_f32",
-            "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol"]
+            "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol", "ufp4_set_schedule",
+            "ufp4_schedule_of"]
 
 
 class Ufp4Error(RuntimeError):
@@ -92,6 +94,10 @@ def _load():
     L.ufp4_rht_signs.argtypes = [u64, P]
     L.ufp4_grouped_col_offsets.restype = ctypes.c_int
     L.ufp4_grouped_col_offsets.argtypes = [P, i32, i32, P]
+    L.ufp4_set_schedule.restype = ctypes.c_int
+    L.ufp4_set_schedule.argtypes = [i32, i32]
+    L.ufp4_schedule_of.restype = ctypes.c_int
+    L.ufp4_schedule_of.argtypes = [i64, i64, i32, cfgp, ctypes.POINTER(i32)]
     return L
 
 

@@ -3,6 +3,8 @@
 // enqueued; nothing here allocates device memory.
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/ufp4.h"
 #include "ufp4_internal.hpp"
 
@@ -31,10 +33,14 @@ size_t quant_ws_bytes(int64_t rows, int64_t cols, int32_t groups) {
   const int64_t g16 = grid_size_quant(rows, cols, groups, 16, &nb, &nt);
   const int64_t g32 = grid_size_quant(rows, cols, groups, 32, &nb, &nt);
   const int64_t g = g16 > g32 ? g16 : g32;
-  return kWsHeader + (size_t)g * sizeof(float2);
+  return kWsPartOffset + (size_t)g * sizeof(float2);
 }
 
-size_t stats_ws_bytes() { return kWsHeader + (size_t)kStatsMaxWg * kStatsSlots * sizeof(double); }
+// Schedule of dense NV16 calls (ufp4_set_schedule).
+std::atomic<int> g_schedule{UFP4_SCHEDULE_AUTO};
+std::atomic<int> g_left_stride{0};
+
+size_t stats_ws_bytes() { return kWsPartOffset + (size_t)kStatsMaxWg * kStatsSlots * sizeof(double); }
 
 // An empty output (no elements) may pass null codes/scales; the tensor
 // scale is always written.
@@ -66,6 +72,14 @@ void base_params(QuantParams& p, const uint16_t* x, int64_t rows, int64_t cols, 
   p.ws_status = ws ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + 4) : nullptr;
 }
 
+// Whether a dense NV16 call of n_work tiles takes the single pass.  AUTO
+// takes the two-pass schedule: on MI355X it is the faster one for every
+// tensor measured (an 8192 x 2048 call: 26.8 us against 42.6 us).
+bool single_pass(bool grouped, bool mx, int64_t n_work) {
+  if (grouped || mx || n_work > kMaxFusedTiles) return false;
+  return g_schedule.load(std::memory_order_relaxed) == UFP4_SCHEDULE_SINGLE_PASS;
+}
+
 // Start and end events of the two kernels of one call.
 struct KernelTimer {
   hipEvent_t ev[4];
@@ -90,7 +104,23 @@ int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream, Ker
   if (!p.mx) {
     const size_t need = quant_ws_bytes(p.rows, p.cols, p.num_groups);
     if (!ws || ws_bytes < need || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
-    p.ws_part = reinterpret_cast<float2*>(static_cast<uint8_t*>(ws) + kWsHeader);
+    p.ws_part = reinterpret_cast<float2*>(static_cast<uint8_t*>(ws) + kWsPartOffset);
+    if (single_pass(p.offsets != nullptr, false, p.n_work)) {
+      const int mode = g_schedule.load(std::memory_order_relaxed);
+      // every tile fits on the device at once: one pass over the input
+      uint8_t* base = static_cast<uint8_t*>(ws);
+      p.fs_gen = reinterpret_cast<uint32_t*>(base + kWsGenOffset);
+      p.fs_words = reinterpret_cast<uint64_t*>(base + kWsHeader);
+      p.fs_orphan_stride = mode == UFP4_SCHEDULE_SINGLE_PASS ? g_left_stride.load(std::memory_order_relaxed) : 0;
+      if (tm) {
+        // no separate maxima kernel: its interval is empty
+        if (hipEventRecord(tm->ev[0], stream) != hipSuccess || hipEventRecord(tm->ev[1], stream) != hipSuccess)
+          return UFP4_ERR_HIP;
+      }
+      if (launch_fused(p, grid, stream, tm ? tm->ev[2] : nullptr, tm ? tm->ev[3] : nullptr) != hipSuccess)
+        return UFP4_ERR_HIP;
+      return UFP4_OK;
+    }
     if (launch_amax(p, grid, stream, tm ? tm->ev[0] : nullptr, tm ? tm->ev[1] : nullptr) != hipSuccess)
       return UFP4_ERR_HIP;
   } else if (p.offsets) {
@@ -114,6 +144,7 @@ const char* ufp4_status_string(int status) {
     case UFP4_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case UFP4_ERR_HIP: return "HIP runtime error";
     case UFP4_ERR_OFFSETS: return "grouped offsets invalid";
+    case UFP4_ERR_SYNC: return "single-pass device-wide exchange did not complete";
     default: return "unknown status";
   }
 }
@@ -126,8 +157,28 @@ size_t ufp4_workspace_size(int64_t rows, int64_t cols, int32_t num_groups) {
 
 int ufp4_workspace_init(void* ws, size_t ws_bytes, ufp4_stream_t stream) {
   if (!ws || ws_bytes < kWsHeader || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
-  if (launch_fill(static_cast<uint32_t*>(ws), (int64_t)(kWsHeader / 4), 0u, (hipStream_t)stream) != hipSuccess)
+  if (launch_fill(static_cast<uint32_t*>(ws), (int64_t)(ws_bytes / 4), 0u, (hipStream_t)stream) != hipSuccess)
     return UFP4_ERR_HIP;
+  return UFP4_OK;
+}
+
+int ufp4_schedule_of(int64_t rows, int64_t cols, int32_t num_groups, const ufp4_config* cfg,
+                     int32_t* schedule_out) {
+  if (check_cfg(cfg) || !schedule_out || rows < 0 || cols < 0 || num_groups < 1)
+    return UFP4_ERR_INVALID_ARGUMENT;
+  int32_t nb, nt;
+  grid_size_quant(rows, cols, num_groups, block_of(cfg), &nb, &nt);
+  const bool one = rows > 0 && cols > 0 &&
+                   single_pass(num_groups > 1, cfg->scaling == UFP4_SCALE_MX32, (int64_t)nb * nt);
+  *schedule_out = one ? UFP4_SCHEDULE_SINGLE_PASS : UFP4_SCHEDULE_TWO_PASS;
+  return UFP4_OK;
+}
+
+int ufp4_set_schedule(int32_t schedule, int32_t left_stride) {
+  if (schedule < UFP4_SCHEDULE_AUTO || schedule > UFP4_SCHEDULE_SINGLE_PASS || left_stride < 0)
+    return UFP4_ERR_INVALID_ARGUMENT;
+  g_left_stride.store(left_stride, std::memory_order_relaxed);
+  g_schedule.store(schedule, std::memory_order_relaxed);
   return UFP4_OK;
 }
 
@@ -331,7 +382,7 @@ int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_
   int64_t wg = (nblk + 255) / 256;
   if (wg > kStatsMaxWg) wg = kStatsMaxWg;
   p.n_wg = (int32_t)wg;
-  p.part = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + kWsHeader);
+  p.part = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + kWsPartOffset);
   hipStream_t s = (hipStream_t)stream;
   if (launch_stats(p, s) != hipSuccess) return UFP4_ERR_HIP;
   static thread_local double host[kStatsMaxWg * kStatsSlots];

@@ -44,11 +44,22 @@ struct QuantParams {
   // workspace
   uint32_t* ws_status;  // grouped calls: 0, or UFP4_ERR_OFFSETS
   float2* ws_part;      // [n_work]: per tile, max |transform| (row-wise, column-wise)
+  // single-pass schedule
+  uint32_t* fs_gen;          // call generation, advanced once per call
+  uint64_t* fs_words;        // [3][n_work] generation-tagged words: start, row-wise and column-wise partial
+  int32_t fs_orphan_stride;  // > 1: tiles whose index is not a multiple leave their work to others
 };
 
-// Workspace layout (bytes): a 256-byte header (status word), then one
-// float2 partial per tile.
+// Workspace layout (bytes): a 256-byte header (status word at 4, call
+// generation at 128), the single-pass schedule's generation-tagged words
+// (three 8-byte words per tile, up to kMaxFusedTiles tiles; nothing else is
+// ever stored there, so a stale word carries an older generation), then one
+// float2 partial per tile for the two-pass schedule.
 constexpr size_t kWsHeader = 256;
+constexpr size_t kWsGenOffset = 128;
+constexpr int kMaxFusedTiles = 1024;
+constexpr size_t kWsFusedWords = (size_t)kMaxFusedTiles * 3 * sizeof(uint64_t);
+constexpr size_t kWsPartOffset = kWsHeader + kWsFusedWords;
 
 void fill_rht_signs(uint64_t seed, QuantParams& p);
 uint32_t rht_sign_mask(uint64_t seed);
@@ -60,6 +71,11 @@ int64_t grid_size_quant(int64_t rows, int64_t cols, int32_t groups, int32_t bloc
 hipError_t launch_amax(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0 = nullptr,
                        hipEvent_t t1 = nullptr);
 hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0 = nullptr,
+                        hipEvent_t t1 = nullptr);
+// The single-pass schedule (dense NV16 tensors of at most kMaxFusedTiles
+// tiles): one kernel, every tile kept in registers across a device-wide
+// exchange of the tile maxima.
+hipError_t launch_fused(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0 = nullptr,
                         hipEvent_t t1 = nullptr);
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
 

@@ -55,9 +55,27 @@ __device__ __forceinline__ int32_t remap_xcd(int32_t b, int32_t nblocks) {
   return (b % kNumXcd) * per + b / kNumXcd;
 }
 
+// Tile of work index w of a dense tensor.
+__device__ __forceinline__ TileInfo dense_tile(const QuantParams& p, int32_t w) {
+  TileInfo T;
+  T.bad = false;
+  T.work = w;
+  T.active = w >= 0 && w < p.n_work;
+  T.band = T.active ? w / p.n_tiles : 0;
+  const int32_t t = T.active ? w % p.n_tiles : 0;
+  T.seg = 0;
+  T.seg_row0 = 0;
+  T.M = p.rows;
+  T.P = (p.rows + p.block - 1) / p.block * p.block;
+  T.coff = 0;
+  T.m0 = (int64_t)t * kTileRows;
+  T.active = T.active && T.m0 < T.P;
+  return T;
+}
+
 // Resolve the workgroup's tile.  For grouped calls every workgroup scans the
 // offsets (at most kMaxGroups+1 values) into LDS and validates them.
-__device__ TileInfo tile_info(const QuantParams& p, GroupLds& g) {
+__device__ __forceinline__ TileInfo tile_info(const QuantParams& p, GroupLds& g) {
   TileInfo T;
   T.bad = false;
   const int32_t w = remap_xcd((int32_t)blockIdx.x, (int32_t)gridDim.x);
@@ -65,16 +83,7 @@ __device__ TileInfo tile_info(const QuantParams& p, GroupLds& g) {
   T.work = w;
   T.band = T.active ? w / p.n_tiles : 0;
   const int32_t t = T.active ? w % p.n_tiles : 0;
-  if (p.offsets == nullptr) {
-    T.seg = 0;
-    T.seg_row0 = 0;
-    T.M = p.rows;
-    T.P = (p.rows + p.block - 1) / p.block * p.block;
-    T.coff = 0;
-    T.m0 = (int64_t)t * kTileRows;
-    T.active = T.active && T.m0 < T.P;
-    return T;
-  }
+  if (p.offsets == nullptr) return dense_tile(p, w);
   const int E = p.num_groups;
   const int tid = threadIdx.x;
   if (tid == 0) g.bad = 0;
@@ -286,25 +295,24 @@ __device__ __forceinline__ uint32_t push_nibble(uint32_t m, uint32_t acc) {
 constexpr float kMagic = 12582912.0f;
 
 // ---------------------------------------------------------------- phase A
-template <bool RHT>
-__global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
-  __shared__ GroupLds g;
-  __shared__ float red[2][kThreads / 64];
-  const TileInfo T = tile_info(p, g);
-  if (!T.active) return;  // uniform per workgroup; its partial slot is never read
-  const LaneGeom L = lane_geom(p, T);
-  uint32_t w[16][4];
-  load_tile(p, T, L, w);
-  // Rows are consumed in load order, each as soon as it arrives: its
-  // row-wise half-blocks are transformed at once, and the column-wise
-  // butterflies advance one stage whenever the rows they pair are present,
-  // so the arithmetic overlaps the remaining loads.
+// Largest magnitudes of the tile's row-wise and column-wise transforms
+// (before the final 1/4), reduced over the workgroup and returned to every
+// thread.  Rows are consumed in load order, each as soon as it arrives: its
+// row-wise half-blocks are transformed at once, and the column-wise
+// butterflies advance one stage whenever the rows they pair are present, so
+// the arithmetic overlaps the remaining loads.  mid() runs once, after the
+// first eight rows (a place to issue loads whose results are needed only at
+// the end); on_row(i) runs when row i is first used.
+template <bool RHT, typename Mid, typename OnRow>
+__device__ __forceinline__ float2 tile_amax(const QuantParams& p, const LaneGeom& L, const uint32_t (&w)[16][4],
+                                            float (&red)[2][kThreads / 64], Mid&& mid, OnRow&& on_row) {
   float acc_r = 0.0f, acc_c = 0.0f;
   const bool do_row = p.do_row != 0, do_col = p.do_col != 0;
   const RowLaneSigns rs = row_lane_signs<RHT>(p, L.lc & 1);
   float cv[16][8];  // column-wise values of the lane's 8 columns, by row
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
+    on_row(i);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       cv[i][2 * k] = bf_lo(w[i][k]);
@@ -323,6 +331,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
         for (int j = 0; j < 8; ++j) acc_r = fmaxf(acc_r, fabsf(v[j]));
       }
     }
+    if (i == 8) mid();
     if (RHT && do_col) {
       // column-wise stages of half-width 1, 2, 4 once their rows are here
       if (i % 2 == 1) {
@@ -362,15 +371,26 @@ __global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
     red[1][threadIdx.x >> 6] = acc_c;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = red[0][0], c = red[1][0];
+  float r = red[0][0], c = red[1][0];
 #pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) {
-      r = fmaxf(r, red[0][i]);
-      c = fmaxf(c, red[1][i]);
-    }
-    p.ws_part[T.work] = make_float2(r, c);
+  for (int i = 1; i < kThreads / 64; ++i) {
+    r = fmaxf(r, red[0][i]);
+    c = fmaxf(c, red[1][i]);
   }
+  return make_float2(r, c);
+}
+
+template <bool RHT>
+__global__ __launch_bounds__(kThreads) void ufp4_amax_kernel(QuantParams p) {
+  __shared__ GroupLds g;
+  __shared__ float red[2][kThreads / 64];
+  const TileInfo T = tile_info(p, g);
+  if (!T.active) return;  // uniform per workgroup; its partial slot is never read
+  const LaneGeom L = lane_geom(p, T);
+  uint32_t w[16][4];
+  load_tile(p, T, L, w);
+  const float2 m = tile_amax<RHT>(p, L, w, red, [] {}, [](int) {});
+  if (threadIdx.x == 0) p.ws_part[T.work] = m;
 }
 
 // ---------------------------------------------------------------- phase B
@@ -459,99 +479,21 @@ struct ColStage {
   uint8_t scales[8][kBandCols + 4];
 };
 
-template <int GRID, bool SR, bool MX, bool RHT>
-__global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
-  __shared__ GroupLds g;
-  __shared__ float lut[2][128];
-  __shared__ float red[2][kThreads / 64];
-  __shared__ ColStage cst;
-  const TileInfo T = tile_info(p, g);
-  if (blockIdx.x == 0) {
-    // tensor scales nobody else writes: MX32 (always 1) and empty segments
-    if (p.offsets && p.ws_status && threadIdx.x == 0) *p.ws_status = T.bad ? 6u : 0u;
-    if (p.offsets == nullptr || !T.bad) {
-      for (int e = threadIdx.x; e < p.num_groups; e += kThreads) {
-        const bool empty = p.offsets != nullptr && g.off[e + 1] == g.off[e];
-        if (MX || empty) {
-          if (p.do_row && p.row_ts) p.row_ts[e] = 1.0f;
-          if (p.do_col && p.col_ts) p.col_ts[e] = 1.0f;
-        }
-      }
-    }
-  }
-  if (!T.active) return;  // uniform per workgroup
-  const LaneGeom L = lane_geom(p, T);
-  constexpr float qmax = grid_qmax<GRID>();
-  TensorScale tsr{1.0f, qmax, 1.0f / qmax, false}, tsc = tsr;
-  // Phase-A partials of the segment: the first 4 per thread are requested
-  // before the tile, so their latency overlaps the tile loads.  The loads are
-  // unconditional (clamped index, result selected afterwards), so they issue
-  // back to back; a dense tensor's partials are contiguous.
-  const uint32_t t0 = p.offsets ? (uint32_t)g.tpre[T.seg] : 0u;
-  const uint32_t nt = p.offsets ? (uint32_t)(g.tpre[T.seg + 1] - g.tpre[T.seg]) : (uint32_t)p.n_tiles;
-  const uint32_t cnt = MX ? 0u : nt * (uint32_t)p.n_band;
-  auto part_index = [&](uint32_t j) -> uint32_t {
-    return p.offsets ? (j / nt) * (uint32_t)p.n_tiles + t0 + j % nt : j;
-  };
-  float2 pre[4];
-  if (!MX) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t i = threadIdx.x + q * kThreads;
-      pre[q] = p.ws_part[part_index(i < cnt ? i : cnt - 1u)];
-    }
-  }
-  // The first four rows are requested before the prologue and the rest after
-  // it: with fewer requests ahead of them in the memory queues, the rows the
-  // first group needs arrive sooner.
-  uint32_t w[16][4];
-  load_rows<0, 4, true>(p, T, L, w);
-  if (!MX) {
-    // per-tensor maximum of the segment from the phase-A partials
-    float r = 0.0f, c = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool in = threadIdx.x + q * kThreads < cnt;
-      r = fmaxf(r, in ? pre[q].x : 0.0f);
-      c = fmaxf(c, in ? pre[q].y : 0.0f);
-    }
-    for (uint32_t i = threadIdx.x + 4 * kThreads; i < cnt; i += kThreads) {
-      const float2 q = p.ws_part[part_index(i)];
-      r = fmaxf(r, q.x);
-      c = fmaxf(c, q.y);
-    }
-    r = wave_max(r);
-    c = wave_max(c);
-    if ((threadIdx.x & 63) == 0) {
-      red[0][threadIdx.x >> 6] = r;
-      red[1][threadIdx.x >> 6] = c;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kThreads / 64; ++i) {
-      r = fmaxf(r, red[0][i]);
-      c = fmaxf(c, red[1][i]);
-    }
-    tsr = make_tensor_scale<RHT>(r, qmax);
-    tsc = make_tensor_scale<RHT>(c, qmax);
-    {
-      const int t = threadIdx.x, l = t >> 7, cc = t & 127;
-      const float S = l ? tsc.S : tsr.S;
-      const float d = (cc == 127) ? 0.0f : e4m3_decode_pos((uint32_t)cc) * S;
-      lut[l][cc] = (d == 0.0f) ? 0.0f : 1.0f / d;  // inverse dequantization factor per code
-    }
-    if (threadIdx.x == 0 && T.band == 0 && T.m0 == 0) {
-      if (p.do_row && p.row_ts) p.row_ts[T.seg] = tsr.S;
-      if (p.do_col && p.col_ts) p.col_ts[T.seg] = tsc.S;
-    }
-    __syncthreads();
-  }
-  load_rows<4, 16, true>(p, T, L, w);
+// Quantize one tile whose rows are loaded (or in flight, in load order) in
+// w, given the per-tensor scales of the two layouts and their inverse
+// block-factor tables: row-wise codes and scales straight to memory,
+// column-wise ones through the LDS staging area.  KEEP: the rows are
+// unpacked once and kept unpacked for the column-wise pass (fewer
+// instructions); otherwise they are unpacked again there (fewer registers).
+template <int GRID, bool SR, bool MX, bool RHT, bool KEEP = true>
+__device__ __forceinline__ void quant_tile(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
+                                           const uint32_t (&w)[16][4], const TensorScale& tsr,
+                                           const TensorScale& tsc, const float (&lut)[2][128], ColStage& cst) {
 
   // The sub-tile is unpacked once (row by row, in load order, inside the
   // row-wise pass) and kept for the column-wise pass.
   float xf[16][8];
-  if (!p.do_row) {
+  if (KEEP && !p.do_row) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
 #pragma unroll
@@ -596,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
           xf[i][2 * k + 1] = bf_hi(w[i][k]);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[r][j] = xf[i][j];
+        for (int j = 0; j < 8; ++j) v[r][j] = xf[i][j];  // (without KEEP, xf is dead beyond this row)
         if (RHT) {
           fwht8_half(v[r], rs.h);
           cross_stage8(v[r], rs.s4);
@@ -682,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
       for (int r = 0; r < 2; ++r) {
         const int k = 2 * g2 + r;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[r][i] = xf[i][k];
+        for (int i = 0; i < 16; ++i) v[r][i] = KEEP ? xf[i][k] : ((k & 1) ? bf_hi(w[i][k >> 1]) : bf_lo(w[i][k >> 1]));
         if (RHT) fwht16_inlane(v[r], p.sg);
         float m = 0.0f;
 #pragma unroll
@@ -773,6 +715,327 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
       const int col = q / per, b = q % per;
       if (col < ncols && b < nsc) cs[(int64_t)col * (Rp / B) + b] = cst.scales[MX ? 2 * b : b][col];
     }
+  }
+}
+
+template <int GRID, bool SR, bool MX, bool RHT>
+__global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
+  __shared__ GroupLds g;
+  __shared__ float lut[2][128];
+  __shared__ float red[2][kThreads / 64];
+  __shared__ ColStage cst;
+  const TileInfo T = tile_info(p, g);
+  if (blockIdx.x == 0) {
+    // tensor scales nobody else writes: MX32 (always 1) and empty segments
+    if (p.offsets && p.ws_status && threadIdx.x == 0) *p.ws_status = T.bad ? 6u : 0u;
+    if (p.offsets == nullptr || !T.bad) {
+      for (int e = threadIdx.x; e < p.num_groups; e += kThreads) {
+        const bool empty = p.offsets != nullptr && g.off[e + 1] == g.off[e];
+        if (MX || empty) {
+          if (p.do_row && p.row_ts) p.row_ts[e] = 1.0f;
+          if (p.do_col && p.col_ts) p.col_ts[e] = 1.0f;
+        }
+      }
+    }
+  }
+  if (!T.active) return;  // uniform per workgroup
+  const LaneGeom L = lane_geom(p, T);
+  constexpr float qmax = grid_qmax<GRID>();
+  TensorScale tsr{1.0f, qmax, 1.0f / qmax, false}, tsc = tsr;
+  // Phase-A partials of the segment: the first 4 per thread are requested
+  // before the tile, so their latency overlaps the tile loads.  The loads are
+  // unconditional (clamped index, result selected afterwards), so they issue
+  // back to back; a dense tensor's partials are contiguous.
+  const uint32_t t0 = p.offsets ? (uint32_t)g.tpre[T.seg] : 0u;
+  const uint32_t nt = p.offsets ? (uint32_t)(g.tpre[T.seg + 1] - g.tpre[T.seg]) : (uint32_t)p.n_tiles;
+  const uint32_t cnt = MX ? 0u : nt * (uint32_t)p.n_band;
+  auto part_index = [&](uint32_t j) -> uint32_t {
+    return p.offsets ? (j / nt) * (uint32_t)p.n_tiles + t0 + j % nt : j;
+  };
+  float2 pre[4];
+  if (!MX) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t i = threadIdx.x + q * kThreads;
+      pre[q] = p.ws_part[part_index(i < cnt ? i : cnt - 1u)];
+    }
+  }
+  // The first four rows are requested before the prologue and the rest after
+  // it: with fewer requests ahead of them in the memory queues, the rows the
+  // first group needs arrive sooner.
+  uint32_t w[16][4];
+  load_rows<0, 4, true>(p, T, L, w);
+  if (!MX) {
+    // per-tensor maximum of the segment from the phase-A partials
+    float r = 0.0f, c = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool in = threadIdx.x + q * kThreads < cnt;
+      r = fmaxf(r, in ? pre[q].x : 0.0f);
+      c = fmaxf(c, in ? pre[q].y : 0.0f);
+    }
+    for (uint32_t i = threadIdx.x + 4 * kThreads; i < cnt; i += kThreads) {
+      const float2 q = p.ws_part[part_index(i)];
+      r = fmaxf(r, q.x);
+      c = fmaxf(c, q.y);
+    }
+    r = wave_max(r);
+    c = wave_max(c);
+    if ((threadIdx.x & 63) == 0) {
+      red[0][threadIdx.x >> 6] = r;
+      red[1][threadIdx.x >> 6] = c;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) {
+      r = fmaxf(r, red[0][i]);
+      c = fmaxf(c, red[1][i]);
+    }
+    tsr = make_tensor_scale<RHT>(r, qmax);
+    tsc = make_tensor_scale<RHT>(c, qmax);
+    {
+      const int t = threadIdx.x, l = t >> 7, cc = t & 127;
+      const float S = l ? tsc.S : tsr.S;
+      const float d = (cc == 127) ? 0.0f : e4m3_decode_pos((uint32_t)cc) * S;
+      lut[l][cc] = (d == 0.0f) ? 0.0f : 1.0f / d;  // inverse dequantization factor per code
+    }
+    if (threadIdx.x == 0 && T.band == 0 && T.m0 == 0) {
+      if (p.do_row && p.row_ts) p.row_ts[T.seg] = tsr.S;
+      if (p.do_col && p.col_ts) p.col_ts[T.seg] = tsc.S;
+    }
+    __syncthreads();
+  }
+  load_rows<4, 16, true>(p, T, L, w);
+  quant_tile<GRID, SR, MX, RHT>(p, T, L, w, tsr, tsc, lut, cst);
+}
+
+// ------------------------------------------------------- single pass
+// One kernel for a dense NV16 tensor whose tiles the device can hold at
+// once: each workgroup loads its tile, computes the tile maxima (phase A),
+// keeps the tile in registers while the maxima of all tiles are exchanged
+// through generation-tagged words in the workspace, then quantizes it
+// (phase B) without reading it again.
+//
+// No workgroup waits for one that has not started: before publishing its
+// maxima, a workgroup checks that every tile's start word carries this call's
+// generation.  If some tile has not started within kGraceTicks, the device
+// cannot hold all tiles at once (other work occupies it, or the grid is too
+// large); the workgroup then publishes its maxima marked "left", and exits.
+// Every started workgroup publishes without waiting, so every partial word
+// is eventually written and the exchange completes.  The workgroups that stay
+// see the same final words, so they agree on which tiles were left and share
+// them out by rank, reloading each such tile.  The last workgroup to start
+// always finds every tile started, so at least one stays.
+constexpr uint64_t kGraceTicks = 10000;      // 100 us of the 100 MHz real-time counter
+constexpr uint64_t kStuckTicks = 200000000;  // 2 s: only a device fault gets here
+constexpr int kWatch = kMaxFusedTiles / kThreads;  // tiles watched per thread
+
+__device__ __forceinline__ uint64_t ld_agent(uint64_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* a, uint64_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The generation tag: the low half of a tagged word.
+__device__ __forceinline__ uint32_t ld_tag(uint64_t* a) {
+  return __hip_atomic_load(reinterpret_cast<uint32_t*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t rt_now() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Per-tensor scales of both layouts from the tensor maxima, the inverse
+// block-factor tables built from them (ends with a workgroup barrier).
+template <bool RHT>
+__device__ __forceinline__ void tensor_setup(float r, float c, float qmax, TensorScale& tsr, TensorScale& tsc,
+                                             float (&lut)[2][128]) {
+  tsr = make_tensor_scale<RHT>(r, qmax);
+  tsc = make_tensor_scale<RHT>(c, qmax);
+  const int t = threadIdx.x, l = t >> 7, cc = t & 127;
+  const float S = l ? tsc.S : tsr.S;
+  const float d = (cc == 127) ? 0.0f : e4m3_decode_pos((uint32_t)cc) * S;
+  lut[l][cc] = (d == 0.0f) ? 0.0f : 1.0f / d;  // inverse dequantization factor per code
+  __syncthreads();
+}
+
+// LDS of the single-pass kernel: the tile's raw rows, kept from phase A to
+// phase B (register room goes to phase A's column butterflies), share their
+// space with the column-wise staging area, which is used only after the rows
+// are back in registers.
+constexpr size_t kFusedTileLds = 16 * kThreads * sizeof(uint4);
+static_assert(sizeof(ColStage) <= kFusedTileLds, "staging area fits the tile buffer");
+
+template <int GRID, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads, 2) void ufp4_fused_kernel(QuantParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t big[kFusedTileLds];
+  __shared__ float lut[2][128];
+  __shared__ float red[2][kThreads / 64];
+  __shared__ uint64_t left_mask[kMaxFusedTiles / 64];
+  __shared__ int32_t pick;
+  uint4 (&wl)[16][kThreads] = *reinterpret_cast<uint4 (*)[16][kThreads]>(big);
+  ColStage& cst = *reinterpret_cast<ColStage*>(big);
+  const TileInfo T = dense_tile(p, remap_xcd((int32_t)blockIdx.x, (int32_t)gridDim.x));
+  if (!T.active) return;  // uniform per workgroup; owns no tile
+  const uint64_t t_begin = rt_now();
+  const int32_t n = p.n_work;
+  uint64_t* const w_start = p.fs_words;
+  uint64_t* const w_row = w_start + n;
+  uint64_t* const w_col = w_row + n;
+  uint32_t tag = __hip_atomic_load(p.fs_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  tag = tag ? tag : 1u;
+  if (threadIdx.x == 0) st_agent(&w_start[T.work], tag);
+  const LaneGeom L = lane_geom(p, T);
+  uint32_t w[16][4];
+  load_rows<0, 16, true>(p, T, L, w);
+
+  // Phase A on the tile; the start words are read half-way through, when
+  // every workgroup that can start has long since written its own.
+  uint32_t sw[kWatch];
+  const float2 m = tile_amax<RHT>(p, L, w, red, [&] {
+#pragma unroll
+    for (int k = 0; k < kWatch; ++k) {
+      const int32_t i = (int32_t)threadIdx.x + k * kThreads;
+      sw[k] = i < n ? ld_tag(&w_start[i]) : tag;
+    }
+  }, [&](int i) { wl[i][threadIdx.x] = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]); });
+  bool ok = true;
+#pragma unroll
+  for (int k = 0; k < kWatch; ++k) ok = ok && sw[k] == tag;
+  bool all = __syncthreads_and(ok) != 0;
+  bool left = p.fs_orphan_stride > 1 && T.work % p.fs_orphan_stride != 0;
+  while (!all && !left) {
+    if (__syncthreads_or(rt_now() - t_begin > kGraceTicks)) {
+      left = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    ok = true;
+#pragma unroll
+    for (int k = 0; k < kWatch; ++k) {
+      const int32_t i = (int32_t)threadIdx.x + k * kThreads;
+      if (i < n && ld_tag(&w_start[i]) != tag) ok = false;
+    }
+    all = __syncthreads_and(ok) != 0;
+  }
+  if (threadIdx.x == 0) {
+    st_agent(&w_col[T.work], (uint64_t)tag | ((uint64_t)__float_as_uint(m.y) << 32));
+    st_agent(&w_row[T.work], (uint64_t)tag | ((uint64_t)(__float_as_uint(m.x) | (left ? 0x80000000u : 0u)) << 32));
+  }
+  if (left) return;
+
+  // Exchange: every thread watches its tiles until both words of each carry
+  // this call's generation.
+  float r = 0.0f, c = 0.0f;
+  uint32_t have = 0u, need = 0u, lbits = 0u;
+#pragma unroll
+  for (int k = 0; k < kWatch; ++k)
+    if ((int32_t)threadIdx.x + k * kThreads < n) need |= 1u << k;
+  for (;;) {
+#pragma unroll
+    for (int k = 0; k < kWatch; ++k) {
+      if ((need & ~have) & (1u << k)) {
+        const int32_t i = (int32_t)threadIdx.x + k * kThreads;
+        const uint64_t a = ld_agent(&w_row[i]), b = ld_agent(&w_col[i]);
+        if ((uint32_t)a == tag && (uint32_t)b == tag) {
+          const uint32_t hi = (uint32_t)(a >> 32);
+          have |= 1u << k;
+          lbits |= (hi >> 31) << k;
+          r = fmaxf(r, __uint_as_float(hi & 0x7FFFFFFFu));
+          c = fmaxf(c, __uint_as_float((uint32_t)(b >> 32)));
+        }
+      }
+    }
+    if (__syncthreads_and(have == need)) break;
+    if (__syncthreads_or(rt_now() - t_begin > kStuckTicks)) {
+      if (threadIdx.x == 0 && p.ws_status) *p.ws_status = 7u;
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  r = wave_max(r);
+  c = wave_max(c);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < kWatch; ++k) {
+    const uint64_t bits = __ballot((lbits >> k) & 1u);
+    if (lane == 0) left_mask[k * (kThreads / 64) + wave] = bits;
+  }
+  if (lane == 0) {
+    red[0][wave] = r;
+    red[1][wave] = c;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    r = fmaxf(r, red[0][i]);
+    c = fmaxf(c, red[1][i]);
+  }
+  // the same in every lane: keep the tensor quantities in scalar registers
+  r = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r)));
+  c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));
+  constexpr float qmax = grid_qmax<GRID>();
+  TensorScale tsr, tsc;
+  tensor_setup<RHT>(r, c, qmax, tsr, tsc, lut);
+  // every workgroup has read the generation word by now
+  if (threadIdx.x == 0) __hip_atomic_store(p.fs_gen, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // The workgroup's own tile first (already in registers); then the tiles
+  // that were left, the q-th (by index) going to the staying tile of rank
+  // q mod (number staying).
+  int32_t n_left = 0, below = 0;
+  for (int j = 0; j < (n + 63) / 64; ++j) {
+    const uint64_t mk = left_mask[j];
+    n_left += __popcll(mk);
+    if (64 * j + 63 < T.work) below += __popcll(mk);
+    else if (64 * j < T.work) below += __popcll(mk & ((1ull << (T.work - 64 * j)) - 1ull));
+  }
+  const int32_t n_stay = n - n_left;
+  int32_t q = T.work - below;  // rank among the staying tiles
+  {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 u = wl[i][threadIdx.x];
+      w[i][0] = u.x;
+      w[i][1] = u.y;
+      w[i][2] = u.z;
+      w[i][3] = u.w;
+    }
+    __syncthreads();  // the staging area reuses the rows' space
+    if (threadIdx.x == 0 && T.band == 0 && T.m0 == 0) {
+      if (p.do_row && p.row_ts) p.row_ts[0] = tsr.S;
+      if (p.do_col && p.col_ts) p.col_ts[0] = tsc.S;
+    }
+    quant_tile<GRID, SR, false, RHT>(p, T, L, w, tsr, tsc, lut, cst);
+  }
+  for (; q < n_left; q += n_stay) {
+    if (threadIdx.x == 0) {
+      int32_t want = q, o = -1;
+      for (int j = 0; j < (n + 63) / 64 && o < 0; ++j) {
+        uint64_t mk = left_mask[j];
+        const int cnt = __popcll(mk);
+        if (want < cnt) {
+          for (; want > 0; --want) mk &= mk - 1ull;
+          o = 64 * j + (int)__builtin_ctzll(mk);
+        } else {
+          want -= cnt;
+        }
+      }
+      pick = o;
+    }
+    __syncthreads();  // also: the previous tile's write-out has read the staging area
+    const TileInfo U = dense_tile(p, pick);
+    if (!U.active) break;  // (not reached: the q-th left tile exists for q < n_left)
+    // Lane geometry re-derived through an opaque copy, so the compiler
+    // recomputes the lane-dependent values inside this rarely used loop
+    // instead of holding them in registers across the own tile's pass.
+    LaneGeom LU = lane_geom(p, U);
+    asm volatile("" : "+v"(LU.lc), "+v"(LU.lane), "+v"(LU.half), "+v"(LU.wave));
+    LU.m_h0 = U.m0 + 32 * LU.wave + 16 * LU.half;
+    LU.c0 = (int64_t)U.band * kBandCols + 8 * LU.lc;
+    LU.lane_ok = LU.c0 < p.cols;
+    load_rows<0, 16, true>(p, U, LU, w);
+    if (threadIdx.x == 0 && U.band == 0 && U.m0 == 0) {
+      if (p.do_row && p.row_ts) p.row_ts[0] = tsr.S;
+      if (p.do_col && p.col_ts) p.col_ts[0] = tsc.S;
+    }
+    quant_tile<GRID, SR, false, RHT, false>(p, U, LU, w, tsr, tsc, lut, cst);
   }
 }
 
@@ -888,6 +1151,33 @@ hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s, hipEv
     case kGridINT4: return launch_quant_mx<kGridINT4>(p, grid, sr, s, t0, t1);
     case kGridE2M1: return launch_quant_mx<kGridE2M1>(p, grid, sr, s, t0, t1);
     case kGridE2M1C: return launch_quant_mx<kGridE2M1C>(p, grid, sr, s, t0, t1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int GRID, bool SR>
+static void launch_fused_rht(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (p.rht)
+    launch(ufp4_fused_kernel<GRID, SR, true>, p, grid, s, t0, t1);
+  else
+    launch(ufp4_fused_kernel<GRID, SR, false>, p, grid, s, t0, t1);
+}
+
+template <int GRID>
+static hipError_t launch_fused_grid(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (p.sr)
+    launch_fused_rht<GRID, true>(p, grid, s, t0, t1);
+  else
+    launch_fused_rht<GRID, false>(p, grid, s, t0, t1);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  switch (p.grid) {
+    case kGridE1M2: return launch_fused_grid<kGridE1M2>(p, grid, s, t0, t1);
+    case kGridINT4: return launch_fused_grid<kGridINT4>(p, grid, s, t0, t1);
+    case kGridE2M1: return launch_fused_grid<kGridE2M1>(p, grid, s, t0, t1);
+    case kGridE2M1C: return launch_fused_grid<kGridE2M1C>(p, grid, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -68,7 +68,10 @@ enum ufp4_status {
   UFP4_ERR_ALIGNMENT = 3,        /* a pointer or leading dimension is misaligned */
   UFP4_ERR_WORKSPACE = 4,        /* workspace null or smaller than required */
   UFP4_ERR_HIP = 5,              /* a HIP runtime call failed */
-  UFP4_ERR_OFFSETS = 6           /* grouped offsets were found invalid on the device */
+  UFP4_ERR_OFFSETS = 6,          /* grouped offsets were found invalid on the device */
+  UFP4_ERR_SYNC = 7              /* a single-pass call's device-wide exchange did not
+                                    complete within 2 s (a device fault); its outputs
+                                    are incomplete and the workspace must be re-initialized */
 };
 
 /* Code layouts: E1M2, E2M1 and E2M1C store sign | magnitude index (index 0..7,
@@ -133,12 +136,14 @@ const char* ufp4_status_string(int status);
  * with `num_groups` segments (1 for dense tensors). */
 size_t ufp4_workspace_size(int64_t rows, int64_t cols, int32_t num_groups);
 
-/* Prepare a workspace before its first use (zeroes its synchronization words
- * with a fill kernel).  Every later call leaves it ready for the next one. */
+/* Prepare a workspace before its first use (zeroes all ws_bytes with a fill
+ * kernel: the status word and the synchronization words of the single-pass
+ * schedule).  Every later call leaves it ready for the next one. */
 int ufp4_workspace_init(void* ws, size_t ws_bytes, ufp4_stream_t stream);
 
 /* After a grouped call: writes UFP4_OK or UFP4_ERR_OFFSETS (the device found
- * the offsets invalid and wrote no output).  Synchronizes the stream. */
+ * the offsets invalid and wrote no output); UFP4_ERR_SYNC after a single-pass
+ * call whose exchange timed out.  Synchronizes the stream. */
 int ufp4_workspace_status(const void* ws, size_t ws_bytes, int* status_out, ufp4_stream_t stream);
 
 /* Row-wise quantization of x[rows][ld] (bf16 bit patterns), blocks along each
@@ -196,6 +201,37 @@ int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_
                const float* tensor_scale, void* ws, size_t ws_bytes, ufp4_stats_t* host_out,
                ufp4_stream_t stream);
 
+/* --- schedule ------------------------------------------------------------ */
+
+/* Dense NV16 calls need the tensor maximum before any code is written.
+ * UFP4_SCHEDULE_TWO_PASS runs two kernels: tile maxima, then quantization
+ * (the input is read twice).  UFP4_SCHEDULE_SINGLE_PASS runs one kernel
+ * whose workgroups keep their tile on chip while the tile maxima are
+ * exchanged through the workspace, so the input is read once; it applies to
+ * tensors of at most 1024 tiles of 128 x 256 elements (others take two
+ * passes).  It wants every tile resident at once; a workgroup that finds
+ * some tile not started within 100 us leaves its tile to the workgroups that
+ * did start, which reload and quantize it, so the call always completes
+ * (slowly when the device is shared).  UFP4_SCHEDULE_AUTO (the default)
+ * takes the two-pass schedule, the faster one on MI355X for every tensor
+ * measured.  Results are bit-identical in every schedule.  Process-wide
+ * setting. */
+enum ufp4_schedule { UFP4_SCHEDULE_AUTO = 0, UFP4_SCHEDULE_TWO_PASS = 1, UFP4_SCHEDULE_SINGLE_PASS = 2 };
+
+/* Select the schedule.  left_stride (test hook, single-pass schedule only):
+ * when > 1, every tile whose index is not a multiple of it is left to the
+ * others as if it had found the device full; 0 or 1 leaves none.
+ * UFP4_ERR_INVALID_ARGUMENT for an unknown schedule or a negative stride. */
+int ufp4_set_schedule(int32_t schedule, int32_t left_stride);
+
+/* The schedule a quantization call on a tensor of rows x cols with
+ * num_groups segments and this configuration takes on the current device
+ * under the current setting: UFP4_SCHEDULE_SINGLE_PASS or
+ * UFP4_SCHEDULE_TWO_PASS (also for MX32, grouped and empty tensors, which
+ * need no separate maxima pass or have their own).  Host only. */
+int ufp4_schedule_of(int64_t rows, int64_t cols, int32_t num_groups, const ufp4_config* cfg,
+                     int32_t* schedule_out);
+
 /* --- diagnostic hooks (not on the hot path) ------------------------------ */
 
 /* codes_dev[i] = 4-bit code (one per byte) of y_dev[i] rounded at unit scale
@@ -205,11 +241,12 @@ int ufp4_round_f32(const float* y_dev, int64_t n, int32_t grid, int32_t rounding
                    uint64_t sr_seed, uint8_t* codes_dev, ufp4_stream_t stream);
 
 /* Measurement hook (not part of the quantization path): one
- * ufp4_quantize_rowcol call with NV16 scaling on `stream`, whose two kernels
- * (tensor maximum, then quantization) are launched with start/stop hipEvents
- * that the runtime stamps with each kernel's own start and end.  Synchronizes
- * the stream and writes the two kernel durations in milliseconds to host
- * memory.  Other arguments and outputs exactly as ufp4_quantize_rowcol.
+ * ufp4_quantize_rowcol call with NV16 scaling on `stream`, whose kernels are
+ * launched with start/stop hipEvents that the runtime stamps with each
+ * kernel's own start and end.  Synchronizes the stream and writes the kernel
+ * durations in milliseconds to host memory: the tensor-maximum kernel's in
+ * *ms_amax_host and the quantization kernel's in *ms_quant_host (under the
+ * single-pass schedule, 0 and the one kernel's).  Other arguments and outputs exactly as ufp4_quantize_rowcol.
  * rows or cols of 0, MX32 scaling or a null duration pointer give
  * UFP4_ERR_INVALID_ARGUMENT.  Not for use under stream capture. */
 int ufp4_time_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,

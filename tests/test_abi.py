@@ -56,6 +56,15 @@ def test_workspace_size(F):
     assert F.lib.ufp4_workspace_size(65536, 4096, 64) >= F.lib.ufp4_workspace_size(65536, 4096, 1)
 
 
+def test_set_schedule_arguments(F):
+    assert F.lib.ufp4_set_schedule(3, 0) == 1
+    assert F.lib.ufp4_set_schedule(-1, 0) == 1
+    assert F.lib.ufp4_set_schedule(2, -1) == 1
+    for mode in (1, 2, 0):
+        assert F.lib.ufp4_set_schedule(mode, 0) == 0
+    assert F.lib.ufp4_set_schedule(0, 0) == 0
+
+
 # Argument errors are detected on the host before anything is enqueued, so
 # these calls are safe with fake (never dereferenced) pointers and no GPU.
 FAKE = 1 << 40  # 16-byte aligned, never touched

@@ -17,6 +17,7 @@ E1M2, INT4, E2M1, E2M1C = 0, 1, 2, 3
 RTNE, SR = 0, 1
 NV16, MX32 = 0, 1
 ROW, COL = 0, 1
+AUTO, TWO_PASS, SINGLE_PASS = 0, 1, 2
 
 
 def say(msg):
@@ -33,6 +34,18 @@ def env():
     import oracle
     oracle.lib()
     return torch, F, oracle
+
+
+@pytest.fixture
+def schedule(env):
+    """Set the process-wide schedule for one test; restored to AUTO after."""
+    _, F, _ = env
+
+    def set_(mode, left_stride=0):
+        F.ufp4_set_schedule(mode, left_stride)
+
+    yield set_
+    F.ufp4_set_schedule(AUTO, 0)
 
 
 def to_dev(torch, xb):
@@ -126,15 +139,18 @@ def test_tiny_config_row(env):
 SHAPES = [(384, 320), (160, 512), (32, 2048)]
 
 
+@pytest.mark.parametrize("sched", [TWO_PASS, SINGLE_PASS])
 @pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
 @pytest.mark.parametrize("rounding", [RTNE, SR])
 @pytest.mark.parametrize("scaling", [NV16, MX32])
 @pytest.mark.parametrize("rht", [1, 0])
-def test_rowcol_variants(env, grid, rounding, scaling, rht):
+def test_rowcol_variants(env, schedule, sched, grid, rounding, scaling, rht):
+    # (MX32 has no tensor maximum: both schedules run its one kernel)
     torch, F, orc = env
+    schedule(sched)
     for shape in SHAPES:
         R, C = shape
-        say(f"[rowcol] {R}x{C} grid={grid} rnd={rounding} scl={scaling} rht={rht}")
+        say(f"[rowcol] {R}x{C} grid={grid} rnd={rounding} scl={scaling} rht={rht} sched={sched}")
         xb = synth.activation(R, C, seed=R + C + grid)
         fc, oc = cfgs(F, orc, grid, rounding, scaling, rht, rht_seed=3, sr_seed=11)
         row, col = gpu_rowcol(env, xb, fc)
@@ -196,19 +212,77 @@ def test_deterministic_repeat(env):
         assert torch.equal(qa.codes, qb.codes) and torch.equal(qa.scales, qb.scales)
 
 
-def test_timing_hook_matches_plain_call(env):
+@pytest.mark.parametrize("sched", [TWO_PASS, SINGLE_PASS])
+def test_timing_hook_matches_plain_call(env, schedule, sched):
     torch, F, orc = env
+    schedule(sched)
     xb = synth.activation(384, 512, seed=9)
     fc, oc = cfgs(F, orc, E1M2, RTNE, NV16, 1, 9, 9)
     x = to_dev(torch, xb)
     row, col = F.alloc_layout(384, 512, NV16), F.alloc_layout(512, 384, NV16)
     ms_a, ms_q = F.ufp4_time_rowcol(x, fc, row, col, F.Workspace(384, 512))
-    assert ms_a > 0.0 and ms_q > 0.0
+    # the single pass has no separate maxima kernel (an empty interval)
+    assert ms_q > 0.0 and (ms_a > 0.0 if sched == TWO_PASS else ms_a >= 0.0)
     for name, qt, layout in (("row", row, ROW), ("col", col, COL)):
         c, s_, t = orc.quantize(xb, oc, layout)
         assert np.array_equal(qt.codes.cpu().numpy(), c), name
         assert np.array_equal(qt.scales.cpu().numpy(), s_), name
         assert qt.tensor_scale.cpu().numpy().view(np.uint32)[0] == t.view(np.uint32)[0], name
+
+
+# -------------------------------------------------------------- single pass
+@pytest.mark.parametrize("stride", [2, 3, 7])
+@pytest.mark.parametrize("rounding", [RTNE, SR])
+def test_single_pass_left_tiles(env, schedule, stride, rounding):
+    # tiles whose workgroup leaves them (forced from the host) are reloaded
+    # and quantized by the workgroups that stay: bit for bit the same output
+    torch, F, orc = env
+    schedule(SINGLE_PASS, stride)
+    R, C = 1040, 1024  # 4 bands x 9 row tiles, the last one ragged
+    say(f"[single pass] {R}x{C} left stride={stride} rnd={rounding}")
+    xb = synth.activation(R, C, seed=40 + stride)
+    fc, oc = cfgs(F, orc, E1M2, rounding, NV16, 1, 5, 6)
+    row, col = gpu_rowcol(env, xb, fc)
+    assert_layout_equal(row, orc.quantize(xb, oc, ROW), f"row stride {stride}")
+    assert_layout_equal(col, orc.quantize(xb, oc, COL), f"col stride {stride}")
+
+
+def test_single_pass_more_tiles_than_the_device_holds(env, schedule):
+    # 16384 x 2048 is 1024 tiles, twice what the device holds at once: the
+    # first workgroups find tiles not started, leave theirs after the grace
+    # period and exit; the later ones find every tile started and quantize
+    # the left tiles too
+    torch, F, orc = env
+    schedule(SINGLE_PASS)
+    R, C = 16384, 2048
+    say(f"[single pass] {R}x{C} oversubscribed")
+    xb = synth.activation(R, C, seed=44)
+    fc, oc = cfgs(F, orc, E1M2, RTNE, NV16, 1, 2, 2)
+    row, col = gpu_rowcol(env, xb, fc)
+    assert_layout_equal(row, orc.quantize(xb, oc, ROW), "row")
+    assert_layout_equal(col, orc.quantize(xb, oc, COL), "col")
+
+
+def test_single_pass_workspace_reuse_across_shapes(env, schedule):
+    # one workspace, calls on different shapes and layouts in turn: each
+    # call's exchange words carry its own generation
+    torch, F, orc = env
+    schedule(SINGLE_PASS)
+    ws = F.Workspace(1024, 1024)
+    for R, C, seed in ((512, 512, 1), (256, 1024, 2), (1024, 768, 3), (512, 512, 4)):
+        say(f"[single pass] reuse {R}x{C}")
+        xb = synth.activation(R, C, seed=seed)
+        fc, oc = cfgs(F, orc, E1M2, RTNE, NV16, 1, seed, seed)
+        x = to_dev(torch, xb)
+        row, col = F.alloc_layout(R, C, NV16), F.alloc_layout(C, R, NV16)
+        F.ufp4_quantize_rowcol(x, fc, row, col, ws)
+        rq = F.alloc_layout(R, C, NV16)
+        F.ufp4_quantize(x, fc, rq, ws)
+        torch.cuda.synchronize()
+        assert_layout_equal(row, orc.quantize(xb, oc, ROW), f"row {R}x{C}")
+        assert_layout_equal(col, orc.quantize(xb, oc, COL), f"col {R}x{C}")
+        assert_layout_equal(rq, orc.quantize(xb, oc, ROW), f"row only {R}x{C}")
+    assert ws.status() == 0
 
 
 # ------------------------------------------------------------------ grouped
