@@ -92,6 +92,9 @@ def lib():
         L.orc_round_f32.argtypes = [P, i64, i32, i32, u64, P]
         L.orc_quantize.restype = ctypes.c_int
         L.orc_quantize.argtypes = [P, i64, i64, i64, ctypes.POINTER(Config), i32, P, P, P]
+        L.orc_quantize_given_amax.restype = ctypes.c_int
+        L.orc_quantize_given_amax.argtypes = [P, i64, i64, i64, ctypes.POINTER(Config), i32, ctypes.c_float,
+                                              P, P, P, P]
         L.orc_grouped_col_offsets.restype = ctypes.c_int
         L.orc_grouped_col_offsets.argtypes = [P, i32, i32, P]
         L.orc_quantize_grouped.restype = ctypes.c_int
@@ -228,6 +231,23 @@ def grouped_col_offsets(offsets, block: int) -> np.ndarray:
     if rc:
         raise ValueError("bad offsets")
     return col
+
+
+def quantize_given_amax(x_bf16: np.ndarray, cfg: Config, layout: int, amax_given: float):
+    """Delayed scaling (NV16): quantize with the tensor scale taken from
+    amax_given.  Returns (codes, scales, tensor_scale, amax_seen)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    cshape, sshape = out_shapes(rows, cols, layout, cfg.scaling)
+    codes = np.zeros(cshape, dtype=np.uint8)
+    scales = np.zeros(sshape, dtype=np.uint8)
+    ts = np.zeros(1, dtype=np.float32)
+    seen = np.zeros(1, dtype=np.float32)
+    rc = lib().orc_quantize_given_amax(_ptr(x), rows, cols, cols, ctypes.byref(cfg), int(layout),
+                                       float(amax_given), _ptr(codes), _ptr(scales), _ptr(ts), _ptr(seen))
+    if rc:
+        raise ValueError(f"orc_quantize_given_amax failed ({rc})")
+    return codes, scales, ts, float(seen[0])
 
 
 def quantize_grouped(x_bf16: np.ndarray, offsets, cfg: Config, row=True, col=True):

@@ -364,13 +364,23 @@ static uint8_t get_nibble(const uint8_t* codes, int64_t o) {
 }
 
 /* Quantize a lineset: pass 1 finds the tensor amax, pass 2 scales, rounds
- * and packs every block (recomputing the transform).                       */
-static float quantize_lineset(const lineset* L, const orc_config* cfg, uint8_t* codes,
-                              uint8_t* scales) {
+ * and packs every block (recomputing the transform).  With amax_given, the
+ * tensor scale comes from that maximum instead (delayed scaling): blocks
+ * whose maximum exceeds it saturate, their E4M3 scale at 448 and their
+ * codes at +-Qmax.  *amax_seen (if given) receives the lineset's own
+ * maximum either way.                                                       */
+static float quantize_lineset_amax(const lineset* L, const orc_config* cfg, uint8_t* codes,
+                                   uint8_t* scales, const float* amax_given, float* amax_seen) {
   int8_t signs[16];
   orc_rht_signs(cfg->rht_seed, signs);
   float amax_t = lineset_amax(L, cfg, signs);
-  float S_t = tensor_scale_from_amax(cfg, amax_t);
+  if (amax_seen) *amax_seen = amax_t;
+  float amax_s = amax_t;
+  if (amax_given) {
+    /* a provided maximum that is not a positive finite number counts as 0 */
+    amax_s = (*amax_given > 0.0f && !isinf(*amax_given)) ? *amax_given : 0.0f;
+  }
+  float S_t = tensor_scale_from_amax(cfg, amax_s);
   int B = block_len(cfg);
   float v[32];
   for (int64_t l = 0; l < L->lines; ++l) {
@@ -393,6 +403,11 @@ static float quantize_lineset(const lineset* L, const orc_config* cfg, uint8_t* 
   return S_t;
 }
 
+static float quantize_lineset(const lineset* L, const orc_config* cfg, uint8_t* codes,
+                              uint8_t* scales) {
+  return quantize_lineset_amax(L, cfg, codes, scales, NULL, NULL);
+}
+
 static int check_cfg(const orc_config* cfg) {
   if (!cfg) return 1;
   if (cfg->grid < 0 || cfg->grid > 3) return 1;
@@ -401,9 +416,9 @@ static int check_cfg(const orc_config* cfg) {
   return 0;
 }
 
-int orc_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
-                 const orc_config* cfg, int32_t layout,
-                 uint8_t* codes, uint8_t* scales, float* tensor_scale) {
+static int quantize_layout(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                           const orc_config* cfg, int32_t layout, const float* amax_given,
+                           uint8_t* codes, uint8_t* scales, float* tensor_scale, float* amax_seen) {
   if (check_cfg(cfg) || rows < 0 || cols < 0 || ld < cols) return 1;
   int B = block_len(cfg);
   lineset L;
@@ -418,8 +433,22 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
   } else {
     return 1;
   }
-  *tensor_scale = quantize_lineset(&L, cfg, codes, scales);
+  *tensor_scale = quantize_lineset_amax(&L, cfg, codes, scales, amax_given, amax_seen);
   return 0;
+}
+
+int orc_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                 const orc_config* cfg, int32_t layout,
+                 uint8_t* codes, uint8_t* scales, float* tensor_scale) {
+  return quantize_layout(x, rows, cols, ld, cfg, layout, NULL, codes, scales, tensor_scale, NULL);
+}
+
+int orc_quantize_given_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                            const orc_config* cfg, int32_t layout, float amax_given,
+                            uint8_t* codes, uint8_t* scales, float* tensor_scale, float* amax_seen) {
+  if (cfg && cfg->scaling != ORC_SCALE_NV16) return 1;
+  return quantize_layout(x, rows, cols, ld, cfg, layout, &amax_given, codes, scales, tensor_scale,
+                         amax_seen);
 }
 
 int orc_grouped_col_offsets(const int64_t* offsets, int32_t num_groups, int32_t block,

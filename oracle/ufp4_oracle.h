@@ -85,6 +85,16 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
 
 /* Padded column offsets of a grouped (per-expert) tensor: exclusive scan of
  * each segment's row count rounded up to the scale block. */
+/* Delayed scaling (NV16 only): as orc_quantize, but the tensor scale comes
+ * from amax_given, a maximum of the layout's transformed values supplied by
+ * the caller (for instance the previous step's), instead of from this
+ * tensor.  A given maximum that is not a positive finite number counts as
+ * zero (S_t = 1).  Blocks above it saturate.  *amax_seen receives this
+ * tensor's own maximum for the layout.  Returns 1 for MX32. */
+int orc_quantize_given_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                            const orc_config* cfg, int32_t layout, float amax_given,
+                            uint8_t* codes, uint8_t* scales, float* tensor_scale, float* amax_seen);
+
 int orc_grouped_col_offsets(const int64_t* offsets, int32_t num_groups, int32_t block,
                             int64_t* col_offsets);
 

@@ -319,3 +319,86 @@ def test_int4_dequantizes_identically_to_e1m2(orc, rounding, scaling):
     e, i = unpack(out[E1M2][0]), unpack(out[INT4][0])
     sm_to_tc = np.array([0, 1, 2, 3, 4, 5, 6, 7, 0, 15, 14, 13, 12, 11, 10, 9], np.uint8)
     np.testing.assert_array_equal(sm_to_tc[e], i)
+
+
+# ------------------------------------------- delayed scaling (given maximum)
+@pytest.mark.parametrize("rounding", [RTNE, SR])
+@pytest.mark.parametrize("layout", [ROW, COL])
+def test_given_own_maximum_reproduces_exact_path(orc, rounding, layout):
+    # the tensor's own maximum as the provided one: the same scales and codes
+    xb = synth.activation(96, 128, 11)
+    for grid in (E1M2, INT4, E2M1, E2M1_CLAMP):
+        cfg = orc.config(grid=grid, rounding=rounding, rht=1, rht_seed=5, sr_seed=6)
+        c, s, t = orc.quantize(xb, cfg, layout)
+        _, _, _, seen = orc.quantize_given_amax(xb, cfg, layout, 1.0)
+        c2, s2, t2, seen2 = orc.quantize_given_amax(xb, cfg, layout, seen)
+        assert seen2 == seen
+        assert t2[0] == t[0]
+        np.testing.assert_array_equal(s2, s)
+        np.testing.assert_array_equal(c2, c)
+
+
+def test_given_maximum_power_of_two_shifts_only_the_scale_exponent(orc):
+    # Every block maximum lies in [amax/2, amax], so with the provided maximum
+    # 2^k times the tensor's own (k = 1, 2, 3) every E4M3 block scale stays
+    # normal and unsaturated: S_t grows by exactly 2^k, each scale byte's
+    # exponent field drops by k (byte - 8k) and d_b = s_b S_t, hence every
+    # code, is unchanged.
+    rng = np.random.default_rng(12)
+    R, C = 64, 128
+    x = rng.uniform(-1.0, 1.0, size=(R, C)).astype(np.float32)
+    blk = x.reshape(R, C // 16, 16)
+    idx = rng.integers(0, 16, size=(R, C // 16))
+    mag = rng.uniform(0.5, 1.0, size=(R, C // 16)).astype(np.float32)
+    np.put_along_axis(blk, idx[..., None], (mag * np.sign(rng.standard_normal((R, C // 16))))[..., None], axis=2)
+    np.clip(blk, -np.abs(np.take_along_axis(blk, idx[..., None], 2)), np.abs(np.take_along_axis(blk, idx[..., None], 2)),
+            out=blk)
+    xb = synth.f32_to_bf16(blk.reshape(R, C))
+    cfg = orc.config(grid=E1M2, rht=0)
+    c, s, t = orc.quantize(xb, cfg, ROW)
+    _, _, _, seen = orc.quantize_given_amax(xb, cfg, ROW, 1.0)
+    for k in (1, 2, 3):
+        c2, s2, t2, _ = orc.quantize_given_amax(xb, cfg, ROW, seen * 2.0 ** k)
+        assert t2[0] == t[0] * np.float32(2.0 ** k)
+        np.testing.assert_array_equal(s2.astype(np.int32), s.astype(np.int32) - 8 * k)
+        np.testing.assert_array_equal(c2, c)
+
+
+def test_given_small_maximum_saturates_numpy(orc):
+    # Provided maximum a quarter of the tensor's own (RHT off): S_t, every
+    # block scale (saturated at 448 = byte 0x7E) and every code recomputed
+    # in numpy float32 with a brute-force E4M3 encode and the printed grid.
+    torch = pytest.importorskip("torch")
+    xb = synth.activation(64, 256, 13)
+    xf = synth.bf16_to_f32(xb)
+    cfg = orc.config(grid=E1M2, rht=0)
+    _, _, _, seen = orc.quantize_given_amax(xb, cfg, ROW, 1.0)
+    given = np.float32(seen) / np.float32(4)
+    codes, scales, ts, _ = orc.quantize_given_amax(xb, cfg, ROW, float(given))
+    S_t = given / np.float32(3.5 * 448)
+    assert ts[0] == S_t
+    amax_b = np.abs(xf.reshape(64, 16, 16)).max(axis=2).astype(np.float32)
+    q = (amax_b / (np.float32(3.5) * S_t)).astype(np.float32)
+    sb = torch.from_numpy(np.minimum(q, np.float32(448)).copy()).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(scales, sb.view(torch.uint8).numpy())
+    assert (scales == 0x7E).any()
+    d = (sb.to(torch.float32).numpy() * S_t).astype(np.float32)
+    inv = np.where(d == 0, np.float32(0), (np.float32(1) / d)).astype(np.float32)
+    y = (xf.reshape(64, 16, 16) * inv[..., None]).astype(np.float32)
+    # E1M2 {0, .5, ..., 3.5}: index = 2|y| rounded half to even, at most 7
+    k = np.rint(np.minimum(2.0 * np.abs(y.astype(np.float64)), 7.0)).astype(np.int64)
+    want = np.where(k == 0, 0, k | np.where(y < 0, 8, 0)).astype(np.uint8).reshape(64, 256)
+    np.testing.assert_array_equal(unpack(codes), want)
+    assert (unpack(codes)[np.abs(xf) == amax_b.max()] & 7 == 7).all()
+
+
+def test_given_maximum_not_positive_finite_counts_as_zero(orc):
+    xb = synth.activation(32, 64, 14)
+    cfg = orc.config(grid=E1M2, rht=1, rht_seed=3)
+    ref = orc.quantize_given_amax(xb, cfg, ROW, 0.0)
+    assert ref[2][0] == 1.0
+    for g in (-1.0, float("inf"), float("-inf"), float("nan")):
+        c, s, t, _ = orc.quantize_given_amax(xb, cfg, ROW, g)
+        assert t[0] == 1.0
+        np.testing.assert_array_equal(s, ref[1])
+        np.testing.assert_array_equal(c, ref[0])
