@@ -333,6 +333,22 @@ def main():
         per_kernel.append(F.ufp4_time_rowcol(x, cfg, row, col, ws, stream))
     k_amax = np.array([a for a, _ in per_kernel])
     k_quant = np.array([b for _, b in per_kernel])
+    # delayed scaling (a different numerics mode, reported beside, never as
+    # the value): each call reads the previous call's tile maxima
+    n_amax = F.ufp4_amax_tiles(ROWS, COLS)
+    amax = [torch.tensor([[3.0, 5.0]], dtype=torch.float32, device=dev).repeat(n_amax, 1) for _ in sets]
+    dfns = []
+    for i, (x, row, col, ws) in enumerate(sets):
+        a = (ctypes.c_void_p(x.data_ptr()), ROWS, COLS, COLS, ctypes.byref(cfg),
+             ctypes.c_void_p(amax[i - 1].data_ptr()), n_amax, ctypes.c_void_p(amax[i].data_ptr()),
+             row.c(), col.c(), sptr)
+
+        def dfn(a=a):
+            rc = F.lib.ufp4_quantize_delayed(*a)
+            if rc:
+                raise F.Ufp4Error("ufp4_quantize_delayed", rc)
+        dfns.append(dfn)
+    ms_delayed, _ = time_graph(torch, dfns, args.steps - args.steps % len(sets) or len(sets), args.warmup, stream)
     # the other schedule on the same buffers, for comparison
     other = "two_pass" if single else "single_pass"
     F.ufp4_set_schedule(F.SCHEDULE_TWO_PASS if single else F.SCHEDULE_SINGLE_PASS)
@@ -397,6 +413,8 @@ def main():
     }
     if two:
         line["extra"].update(two)
+    line["extra"]["delayed_scaling_ms"] = round(ms_delayed, 6)
+    line["extra"]["delayed_scaling_gbps"] = round(nbytes / (ms_delayed * 1e-3) / 1e9, 2)
     if ms_warm is not None:
         line["extra"]["warm_same_buffer_ms"] = round(ms_warm, 6)
         line["extra"]["warm_same_buffer_gbps"] = round(nbytes / (ms_warm * 1e-3) / 1e9, 2)

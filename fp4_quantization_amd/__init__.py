@@ -18,7 +18,7 @@ from ._lib import (GRID_E1M2, GRID_E2M1, GRID_E2M1C, GRID_INT4, LIB_PATH, ROUND_
 
 __all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "GRID_E2M1C", "ROUND_RTNE", "ROUND_STOCHASTIC", "SCALE_NV16",
            "SCALE_MX32", "SCHEDULE_AUTO", "SCHEDULE_TWO_PASS", "SCHEDULE_SINGLE_PASS", "ufp4_set_schedule",
-           "ufp4_schedule_of", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
+           "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
            "ufp4_quantize", "ufp4_quantize_rowcol", "ufp4_quantize_grouped", "ufp4_dequantize",
            "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol",
            "block_len"]
@@ -129,6 +129,28 @@ def ufp4_set_schedule(schedule: int, left_stride: int = 0) -> None:
     _SINGLE_PASS); left_stride > 1 makes the single pass leave every tile whose
     index is not a multiple of it to the other workgroups (test hook)."""
     check("ufp4_set_schedule", lib.ufp4_set_schedule(int(schedule), int(left_stride)))
+
+
+def ufp4_amax_tiles(rows: int, cols: int) -> int:
+    """Pairs of tile maxima a delayed call on rows x cols writes."""
+    return int(lib.ufp4_amax_tiles(int(rows), int(cols)))
+
+
+def ufp4_quantize_delayed(x: torch.Tensor, cfg: ufp4_config, amax_in: torch.Tensor, amax_out,
+                          row_out: QTensor, col_out: QTensor | None = None, stream=None) -> None:
+    """Delayed scaling: tensor scales from amax_in (float32 [n, 2] on the
+    device: row-wise, column-wise maxima); this call's tile maxima go to
+    amax_out (float32 [ufp4_amax_tiles(rows, cols), 2], or None)."""
+    rows, cols, ld = _bf16_view(x)
+    assert amax_in.dtype == torch.float32 and amax_in.is_contiguous() and amax_in.numel() % 2 == 0
+    if amax_out is not None:
+        assert amax_out.dtype == torch.float32 and amax_out.is_contiguous()
+        assert amax_out.numel() >= 2 * ufp4_amax_tiles(rows, cols)
+    col = col_out.c() if col_out is not None else ufp4_qtensor(None, None, None)
+    check("ufp4_quantize_delayed",
+          lib.ufp4_quantize_delayed(_ptr(x), rows, cols, ld, ctypes.byref(cfg), _ptr(amax_in),
+                                    amax_in.numel() // 2, _ptr(amax_out) if amax_out is not None else None,
+                                    row_out.c(), col, _stream(stream)))
 
 
 def ufp4_schedule_of(rows: int, cols: int, cfg: ufp4_config, num_groups: int = 1) -> int:

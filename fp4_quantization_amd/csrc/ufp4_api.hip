@@ -162,6 +162,67 @@ int ufp4_workspace_init(void* ws, size_t ws_bytes, ufp4_stream_t stream) {
   return UFP4_OK;
 }
 
+int64_t ufp4_amax_tiles(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 0;
+  int32_t nb, nt;
+  grid_size_quant(rows, cols, 1, 16, &nb, &nt);
+  return (int64_t)nb * nt;
+}
+
+int ufp4_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const ufp4_config* cfg,
+                          const float* amax_in, int32_t n_in, float* amax_out, ufp4_qtensor row_out,
+                          ufp4_qtensor col_out, ufp4_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->scaling != UFP4_SCALE_NV16) return UFP4_ERR_INVALID_ARGUMENT;
+  if (rows < 0 || cols < 0 || ld < cols || !amax_in || n_in < 1) return UFP4_ERR_INVALID_ARGUMENT;
+  const bool do_col = col_out.tensor_scale != nullptr;
+  if (cols % 16 || (do_col && rows % 16)) return UFP4_ERR_SHAPE;
+  const bool empty = rows == 0 || cols == 0;
+  if ((rc = check_qtensor(row_out, empty))) return rc;
+  if (do_col && (rc = check_qtensor(col_out, empty))) return rc;
+  if (!aligned(amax_in, 8) || !aligned(amax_out, 8)) return UFP4_ERR_ALIGNMENT;
+  if (!empty) {
+    if (!x) return UFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || ld % 8) return UFP4_ERR_ALIGNMENT;
+  }
+  const int64_t n_out = ufp4_amax_tiles(rows, cols);
+  if (amax_out && n_out > 0) {
+    // the kernel reads every provided maximum while it writes its own
+    const uintptr_t a0 = (uintptr_t)amax_in, a1 = a0 + (uintptr_t)n_in * 2 * sizeof(float);
+    const uintptr_t b0 = (uintptr_t)amax_out, b1 = b0 + (uintptr_t)n_out * 2 * sizeof(float);
+    if (a0 < b1 && b0 < a1) return UFP4_ERR_INVALID_ARGUMENT;
+  }
+  QuantParams p;
+  base_params(p, x, rows, cols, ld, cfg, nullptr);
+  p.do_row = 1;
+  p.do_col = do_col;
+  p.row_codes = row_out.codes;
+  p.row_scales = row_out.scales;
+  p.row_ts = row_out.tensor_scale;
+  if (do_col) {
+    p.col_codes = col_out.codes;
+    p.col_scales = col_out.scales;
+    p.col_ts = col_out.tensor_scale;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (empty) {
+    if (launch_fill(reinterpret_cast<uint32_t*>(p.row_ts), 1, 0x3F800000u, s) != hipSuccess) return UFP4_ERR_HIP;
+    if (do_col && launch_fill(reinterpret_cast<uint32_t*>(p.col_ts), 1, 0x3F800000u, s) != hipSuccess)
+      return UFP4_ERR_HIP;
+    return UFP4_OK;
+  }
+  if (cols >= kMaxDim || rows >= kMaxDim) return UFP4_ERR_SHAPE;
+  const int64_t grid = grid_size_quant(rows, cols, 1, 16, &p.n_band, &p.n_tiles);
+  p.n_work = p.n_band * p.n_tiles;
+  if (grid > 0x7FFFFFFF) return UFP4_ERR_SHAPE;
+  p.amax_in = reinterpret_cast<const float2*>(amax_in);
+  p.n_in = n_in;
+  p.amax_out = reinterpret_cast<float2*>(amax_out);
+  if (launch_delayed(p, grid, s) != hipSuccess) return UFP4_ERR_HIP;
+  return UFP4_OK;
+}
+
 int ufp4_schedule_of(int64_t rows, int64_t cols, int32_t num_groups, const ufp4_config* cfg,
                      int32_t* schedule_out) {
   if (check_cfg(cfg) || !schedule_out || rows < 0 || cols < 0 || num_groups < 1)

@@ -44,6 +44,10 @@ struct QuantParams {
   // workspace
   uint32_t* ws_status;  // grouped calls: 0, or UFP4_ERR_OFFSETS
   float2* ws_part;      // [n_work]: per tile, max |transform| (row-wise, column-wise)
+  // delayed scaling: provided maxima in, this call's tile maxima out
+  const float2* amax_in;  // [n_in] (row-wise, column-wise) maxima of the transformed values
+  int32_t n_in;
+  float2* amax_out;       // [n_work], or null
   // single-pass schedule
   uint32_t* fs_gen;          // call generation, advanced once per call
   uint64_t* fs_words;        // [3][n_work] generation-tagged words: start, row-wise and column-wise partial
@@ -72,6 +76,9 @@ hipError_t launch_amax(const QuantParams& p, int64_t grid, hipStream_t s, hipEve
                        hipEvent_t t1 = nullptr);
 hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0 = nullptr,
                         hipEvent_t t1 = nullptr);
+// Delayed scaling (dense NV16): one kernel, tensor scales from p.amax_in.
+hipError_t launch_delayed(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0 = nullptr,
+                          hipEvent_t t1 = nullptr);
 // The single-pass schedule (dense NV16 tensors of at most kMaxFusedTiles
 // tiles): one kernel, every tile kept in registers across a device-wide
 // exchange of the tile maxima.

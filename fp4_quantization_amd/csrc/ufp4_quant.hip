@@ -431,7 +431,9 @@ __device__ __forceinline__ TensorScale make_tensor_scale(float raw, float qmax) 
 // MX32: a power-of-two scale.  Returns true when every block of the
 // wavefront allows the exact fast rounding (normal block scale, no tiny
 // nonzero maximum); blocks outside the data hold zeros and always allow it.
-template <int GRID, bool MX, bool RHT, int NB>
+// Under a provided (delayed) tensor maximum a block maximum may exceed it:
+// DELAYED clamps the converter input at 448, where E4M3 saturates.
+template <int GRID, bool MX, bool RHT, int NB, bool DELAYED = false>
 __device__ __forceinline__ bool block_scales(const float raw[NB], const TensorScale& ts, bool fast_u,
                                              const float* lut_l, uint32_t sbyte[NB], float inv[NB]) {
   constexpr float kThr = RHT ? 0x1p-98f : 0x1p-100f;  // raw maxima whose 1/4 keeps codes exact
@@ -450,7 +452,7 @@ __device__ __forceinline__ bool block_scales(const float raw[NB], const TensorSc
     if (fast_u) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float q = raw[b] * ts.R4;
+        const float q = DELAYED ? fminf(raw[b] * ts.R4, 448.0f) : raw[b] * ts.R4;
         const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q * 0x1.fffffp-1f,   // q (1 - 2^-21)
                                                                        q * 0x1.000004p+0f,  // q (1 + 2^-21)
                                                                        0, false);
@@ -485,10 +487,14 @@ struct ColStage {
 // column-wise ones through the LDS staging area.  KEEP: the rows are
 // unpacked once and kept unpacked for the column-wise pass (fewer
 // instructions); otherwise they are unpacked again there (fewer registers).
-template <int GRID, bool SR, bool MX, bool RHT, bool KEEP = true>
-__device__ __forceinline__ void quant_tile(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
-                                           const uint32_t (&w)[16][4], const TensorScale& tsr,
-                                           const TensorScale& tsc, const float (&lut)[2][128], ColStage& cst) {
+template <int GRID, bool SR, bool MX, bool RHT, bool KEEP = true, bool DELAYED = false>
+__device__ __forceinline__ float2 quant_tile(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
+                                             const uint32_t (&w)[16][4], const TensorScale& tsr,
+                                             const TensorScale& tsc, const float (&lut)[2][128], ColStage& cst) {
+  // DELAYED: the tensor scales come from provided maxima, so a block may
+  // exceed them; scales and codes saturate, and the lane's largest block
+  // maxima (before the final 1/4) are returned for the next call.
+  float tile_r = 0.0f, tile_c = 0.0f;
 
   // The sub-tile is unpacked once (row by row, in load order, inside the
   // row-wise pass) and kept for the column-wise pass.
@@ -510,7 +516,8 @@ __device__ __forceinline__ void quant_tile(const QuantParams& p, const TileInfo&
   const RowLaneSigns rs = row_lane_signs<RHT>(p, parity);
   const int64_t C = p.cols;
   // RTNE onto E1M2/INT4 has an exact fast form; it needs no clamp when the
-  // block scale is a normal E4M3 value (then |y| <= 1.0625 Qmax).
+  // block scale is a normal E4M3 value (then |y| <= 1.0625 Qmax) and the
+  // tensor maximum is the tensor's own (otherwise it clamps to +-Qmax).
   constexpr bool kFastGrid = !SR && GRID != kGridE2M1;  // uniform grids
   constexpr float kGridMul = GRID == kGridINT4 ? 1.0f : 2.0f;  // grid step -> integer
   constexpr float kTop = (float)grid_top<GRID>();              // MX32 clamp, in grid steps
@@ -550,7 +557,8 @@ __device__ __forceinline__ void quant_tile(const QuantParams& p, const TileInfo&
         if (MX) m = fmaxf(m, dpp_xor2(m));
         raw[r] = m;
       }
-      const bool ok = block_scales<GRID, MX, RHT, 4>(raw, tsr, fast_r, lut[0], sbyte, inv);
+      const bool ok = block_scales<GRID, MX, RHT, 4, DELAYED>(raw, tsr, fast_r, lut[0], sbyte, inv);
+      if (DELAYED) tile_r = fmaxf(tile_r, fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])));
       uint32_t packed[4] = {0u, 0u, 0u, 0u};
       if (kFastGrid && ok) {
         // t = y / (grid step) as one product: an exact power-of-two rescaling
@@ -562,7 +570,7 @@ __device__ __forceinline__ void quant_tile(const QuantParams& p, const TileInfo&
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             float t = v[r][j] * mult;
-            if (MX) t = __builtin_amdgcn_fmed3f(t, -kTop, kTop);
+            if (MX || DELAYED) t = __builtin_amdgcn_fmed3f(t, -kTop, kTop);
             acc = push_nibble(__float_as_uint(t + kMagic), acc);
           }
           packed[r] = GRID == kGridINT4 ? acc : tc_to_signmag8(acc);
@@ -632,7 +640,8 @@ __device__ __forceinline__ void quant_tile(const QuantParams& p, const TileInfo&
         if (MX) m = fmaxf(m, __shfl_xor(m, 32));
         raw[r] = m;
       }
-      const bool ok = block_scales<GRID, MX, RHT, 2>(raw, tsc, fast_c, lut[1], sbyte, inv);
+      const bool ok = block_scales<GRID, MX, RHT, 2, DELAYED>(raw, tsc, fast_c, lut[1], sbyte, inv);
+      if (DELAYED) tile_c = fmaxf(tile_c, fmaxf(raw[0], raw[1]));
       uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
       if (kFastGrid && ok) {
 #pragma unroll
@@ -642,7 +651,7 @@ __device__ __forceinline__ void quant_tile(const QuantParams& p, const TileInfo&
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             float t0 = v[r][j] * mult, t1 = v[r][8 + j] * mult;
-            if (MX) {
+            if (MX || DELAYED) {
               t0 = __builtin_amdgcn_fmed3f(t0, -kTop, kTop);
               t1 = __builtin_amdgcn_fmed3f(t1, -kTop, kTop);
             }
@@ -716,6 +725,7 @@ __device__ __forceinline__ void quant_tile(const QuantParams& p, const TileInfo&
       if (col < ncols && b < nsc) cs[(int64_t)col * (Rp / B) + b] = cst.scales[MX ? 2 * b : b][col];
     }
   }
+  return make_float2(tile_r, tile_c);
 }
 
 template <int GRID, bool SR, bool MX, bool RHT>
@@ -807,6 +817,91 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
   }
   load_rows<4, 16, true>(p, T, L, w);
   quant_tile<GRID, SR, MX, RHT>(p, T, L, w, tsr, tsc, lut, cst);
+}
+
+// ------------------------------------------------------------ delayed
+// One kernel for a dense NV16 tensor whose per-tensor scales come from
+// provided maxima (delayed scaling): the input is read once.  The provided
+// maxima are p.amax_in[0 .. n_in), pairs (row-wise, column-wise) of maxima of
+// the transformed values, reduced here (a value that is not a positive
+// finite number counts as zero).  The kernel writes its own tile maxima, in
+// the same units, to p.amax_out[T.work] for the next call.
+__device__ __forceinline__ float given_max(float m) { return (m > 0.0f && m <= 3.4028235e38f) ? m : 0.0f; }
+
+template <bool RHT>
+__device__ __forceinline__ TensorScale given_tensor_scale(float a, float qmax) {
+  TensorScale ts;
+  ts.S = (a > 0.0f) ? a / (qmax * 448.0f) : 1.0f;
+  ts.D = qmax * ts.S;
+  const float R = 1.0f / ts.D;
+  ts.R4 = RHT ? R * 0.25f : R;
+  ts.fast = ts.D >= 0x1p-126f && ts.D <= 0x1p+120f && a < 0x1p+119f;
+  return ts;
+}
+
+template <int GRID, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void ufp4_delayed_kernel(QuantParams p) {
+  __shared__ float lut[2][128];
+  __shared__ float red[2][kThreads / 64];
+  __shared__ ColStage cst;
+  const TileInfo T = dense_tile(p, remap_xcd((int32_t)blockIdx.x, (int32_t)gridDim.x));
+  if (!T.active) return;  // uniform per workgroup
+  const LaneGeom L = lane_geom(p, T);
+  constexpr float qmax = grid_qmax<GRID>();
+  const uint32_t cnt = (uint32_t)p.n_in;
+  float2 pre = make_float2(0.0f, 0.0f);
+  if (threadIdx.x < cnt) pre = p.amax_in[threadIdx.x];
+  uint32_t w[16][4];
+  load_rows<0, 4, true>(p, T, L, w);
+  float r = given_max(pre.x), c = given_max(pre.y);
+  for (uint32_t i = threadIdx.x + kThreads; i < cnt; i += kThreads) {
+    const float2 q = p.amax_in[i];
+    r = fmaxf(r, given_max(q.x));
+    c = fmaxf(c, given_max(q.y));
+  }
+  r = wave_max(r);
+  c = wave_max(c);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = r;
+    red[1][threadIdx.x >> 6] = c;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    r = fmaxf(r, red[0][i]);
+    c = fmaxf(c, red[1][i]);
+  }
+  const TensorScale tsr = given_tensor_scale<RHT>(r, qmax), tsc = given_tensor_scale<RHT>(c, qmax);
+  {
+    const int t = threadIdx.x, l = t >> 7, cc = t & 127;
+    const float S = l ? tsc.S : tsr.S;
+    const float d = (cc == 127) ? 0.0f : e4m3_decode_pos((uint32_t)cc) * S;
+    lut[l][cc] = (d == 0.0f) ? 0.0f : 1.0f / d;  // inverse dequantization factor per code
+  }
+  if (threadIdx.x == 0 && T.band == 0 && T.m0 == 0) {
+    if (p.do_row && p.row_ts) p.row_ts[0] = tsr.S;
+    if (p.do_col && p.col_ts) p.col_ts[0] = tsc.S;
+  }
+  __syncthreads();  // also: every thread has read red
+  load_rows<4, 16, true>(p, T, L, w);
+  float2 m = quant_tile<GRID, SR, false, RHT, true, true>(p, T, L, w, tsr, tsc, lut, cst);
+  m.x = wave_max(m.x);
+  m.y = wave_max(m.y);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = m.x;
+    red[1][threadIdx.x >> 6] = m.y;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && p.amax_out) {
+    float a = red[0][0], b = red[1][0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) {
+      a = fmaxf(a, red[0][i]);
+      b = fmaxf(b, red[1][i]);
+    }
+    // maxima of the transformed values: the final 1/4 is exact
+    p.amax_out[T.work] = RHT ? make_float2(a * 0.25f, b * 0.25f) : make_float2(a, b);
+  }
 }
 
 // ------------------------------------------------------- single pass
@@ -1170,6 +1265,34 @@ static hipError_t launch_fused_grid(const QuantParams& p, int64_t grid, hipStrea
   else
     launch_fused_rht<GRID, false>(p, grid, s, t0, t1);
   return hipGetLastError();
+}
+
+template <int GRID, bool SR>
+static void launch_delayed_rht(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (p.rht)
+    launch(ufp4_delayed_kernel<GRID, SR, true>, p, grid, s, t0, t1);
+  else
+    launch(ufp4_delayed_kernel<GRID, SR, false>, p, grid, s, t0, t1);
+}
+
+template <int GRID>
+static hipError_t launch_delayed_grid(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0,
+                                      hipEvent_t t1) {
+  if (p.sr)
+    launch_delayed_rht<GRID, true>(p, grid, s, t0, t1);
+  else
+    launch_delayed_rht<GRID, false>(p, grid, s, t0, t1);
+  return hipGetLastError();
+}
+
+hipError_t launch_delayed(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  switch (p.grid) {
+    case kGridE1M2: return launch_delayed_grid<kGridE1M2>(p, grid, s, t0, t1);
+    case kGridINT4: return launch_delayed_grid<kGridINT4>(p, grid, s, t0, t1);
+    case kGridE2M1: return launch_delayed_grid<kGridE2M1>(p, grid, s, t0, t1);
+    case kGridE2M1C: return launch_delayed_grid<kGridE2M1C>(p, grid, s, t0, t1);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_fused(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {

@@ -201,6 +201,37 @@ int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_
                const float* tensor_scale, void* ws, size_t ws_bytes, ufp4_stats_t* host_out,
                ufp4_stream_t stream);
 
+/* --- delayed scaling ------------------------------------------------------ */
+
+/* Pairs of maxima a delayed call on a rows x cols tensor writes to amax_out
+ * (one per 128 x 256 tile; 0 for an empty tensor). */
+int64_t ufp4_amax_tiles(int64_t rows, int64_t cols);
+
+/* Delayed-scaling quantization (NV16 only): as ufp4_quantize_rowcol (or
+ * ufp4_quantize when col_out.tensor_scale is NULL), but the per-tensor
+ * scales come from provided maxima instead of this tensor's own, so the
+ * input is read once by one kernel.
+ *   amax_in: device, n_in >= 1 pairs (row-wise, column-wise), each a maximum
+ *     of |transformed value| (after the RHT's 1/4; of |x| without the RHT)
+ *     for that layout.  The effective maximum of a layout is the largest
+ *     entry, an entry that is not a positive finite number counting as zero
+ *     (then S_t = 1).  S_t = max / (Qmax * 448).
+ *   amax_out: device, ufp4_amax_tiles(rows, cols) pairs, or NULL: this
+ *     call's exact tile maxima in the same units, to pass as the next call's
+ *     amax_in (their largest entries are this tensor's maxima).  It must not
+ *     overlap amax_in (UFP4_ERR_INVALID_ARGUMENT).
+ *   Blocks whose maximum exceeds the provided one saturate: E4M3 scale 448,
+ *   codes at +-Qmax.  With a provided maximum equal to the tensor's own the
+ *   outputs equal ufp4_quantize_rowcol's bit for bit.
+ * Shapes, alignment and layouts as ufp4_quantize_rowcol (rows % 16 == 0 only
+ * with the column-wise layout); amax_in and amax_out 8-byte aligned.  No
+ * workspace.  MX32 gives UFP4_ERR_INVALID_ARGUMENT (it has no tensor
+ * scale).  This is a numerics choice (delayed scaling), not the pages'
+ * recipe, which takes each tensor's own maximum. */
+int ufp4_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                          const ufp4_config* cfg, const float* amax_in, int32_t n_in, float* amax_out,
+                          ufp4_qtensor row_out, ufp4_qtensor col_out, ufp4_stream_t stream);
+
 /* --- schedule ------------------------------------------------------------ */
 
 /* Dense NV16 calls need the tensor maximum before any code is written.

@@ -56,6 +56,26 @@ def test_workspace_size(F):
     assert F.lib.ufp4_workspace_size(65536, 4096, 64) >= F.lib.ufp4_workspace_size(65536, 4096, 1)
 
 
+def test_delayed_arguments(F):
+    # host-side checks only (fake device pointers are never dereferenced)
+    cfg = F.config()
+    mx = F.config(scaling=F.SCALE_MX32)
+    q = F.ufp4_qtensor(ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(12288))
+    none = F.ufp4_qtensor(None, None, None)
+    x, a_in, a_out = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21), ctypes.c_void_p(1 << 22)
+    call = F.lib.ufp4_quantize_delayed
+    assert F.lib.ufp4_amax_tiles(8192, 2048) == 512
+    assert F.lib.ufp4_amax_tiles(0, 2048) == 0
+    assert call(x, 64, 64, 64, ctypes.byref(mx), a_in, 1, a_out, q, q, None) == 1    # MX32
+    assert call(x, 64, 64, 64, ctypes.byref(cfg), None, 1, a_out, q, q, None) == 1   # no maxima
+    assert call(x, 64, 64, 64, ctypes.byref(cfg), a_in, 0, a_out, q, q, None) == 1   # n_in 0
+    assert call(x, 64, 40, 64, ctypes.byref(cfg), a_in, 1, a_out, q, q, None) == 2   # cols % 16
+    assert call(x, 40, 64, 64, ctypes.byref(cfg), a_in, 1, a_out, q, q, None) == 2   # rows % 16, col layout
+    assert call(x, 64, 64, 64, ctypes.byref(cfg), ctypes.c_void_p((1 << 21) + 4), 1, a_out, q, q, None) == 3
+    assert call(x, 64, 64, 64, ctypes.byref(cfg), a_in, 1, a_in, q, q, None) == 1    # overlap
+    assert call(x, 64, 64, 64, ctypes.byref(cfg), a_in, 1, a_out, none, q, None) == 1  # row output needed
+
+
 def test_set_schedule_arguments(F):
     assert F.lib.ufp4_set_schedule(3, 0) == 1
     assert F.lib.ufp4_set_schedule(-1, 0) == 1

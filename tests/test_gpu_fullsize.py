@@ -68,9 +68,23 @@ def test_activation_rowcol_8192x2048(env):
     F.ufp4_quantize_rowcol(x, fc, row, col, F.Workspace(8192, 2048))
     torch.cuda.synchronize()
     t = time.time()
-    check_layout("row", row, orc.quantize(xb, oc, ROW))
-    check_layout("col", col, orc.quantize(xb, oc, COL))
+    ref_row, ref_col = orc.quantize(xb, oc, ROW), orc.quantize(xb, oc, COL)
+    check_layout("row", row, ref_row)
+    check_layout("col", col, ref_col)
     say(f"  oracle+compare {time.time() - t:.1f}s")
+    # delayed scaling, chained as in training: a first call under a stale
+    # maximum, then a call under the first one's tile maxima = the exact path
+    say("[full] activation 8192x2048 delayed, chained")
+    n = F.ufp4_amax_tiles(8192, 2048)
+    a1 = torch.full((n, 2), -1.0, dtype=torch.float32, device="cuda")
+    a2 = torch.full((n, 2), -1.0, dtype=torch.float32, device="cuda")
+    stale = torch.tensor([[3.0, 5.0]], dtype=torch.float32, device="cuda")
+    F.ufp4_quantize_delayed(x, fc, stale, a1, row, col)
+    F.ufp4_quantize_delayed(x, fc, a1, a2, row, col)
+    torch.cuda.synchronize()
+    check_layout("delayed row", row, ref_row)
+    check_layout("delayed col", col, ref_col)
+    assert torch.equal(a1, a2) and bool((a1 >= 0).all())
 
 
 def test_weight_grid_sweep_2048x8192(env):

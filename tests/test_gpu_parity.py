@@ -230,6 +230,92 @@ def test_timing_hook_matches_plain_call(env, schedule, sched):
         assert qt.tensor_scale.cpu().numpy().view(np.uint32)[0] == t.view(np.uint32)[0], name
 
 
+# ------------------------------------------------------------------ delayed
+def gpu_delayed(env, xb, fc, amax_in, col=True):
+    """One delayed call; amax_in: float32 array of (row, col) pairs, or a
+    device tensor.  Returns (row, col, tile maxima as numpy [n, 2])."""
+    torch, F, _ = env
+    R, C = xb.shape
+    x = to_dev(torch, xb)
+    row = F.alloc_layout(R, C, NV16)
+    colq = F.alloc_layout(C, R, NV16) if col else None
+    if isinstance(amax_in, torch.Tensor):
+        a_in = amax_in
+    else:
+        a_in = torch.from_numpy(np.asarray(amax_in, np.float32).reshape(-1, 2).copy()).cuda()
+    n = F.ufp4_amax_tiles(R, C)
+    a_out = torch.full((n, 2), -1.0, dtype=torch.float32, device="cuda")
+    F.ufp4_quantize_delayed(x, fc, a_in, a_out, row, colq)
+    torch.cuda.synchronize()
+    return row, colq, a_out
+
+
+def own_maxima(orc, xb, oc):
+    r = orc.quantize_given_amax(xb, oc, ROW, 1.0)[3]
+    c = orc.quantize_given_amax(xb, oc, COL, 1.0)[3]
+    return np.float32(r), np.float32(c)
+
+
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
+@pytest.mark.parametrize("rounding", [RTNE, SR])
+@pytest.mark.parametrize("rht", [1, 0])
+def test_delayed_matches_oracle(env, grid, rounding, rht):
+    # provided maxima at, below (saturating) and above the tensor's own
+    torch, F, orc = env
+    for R, C in ((384, 320), (160, 512)):
+        xb = synth.activation(R, C, seed=R + grid + 7)
+        fc, oc = cfgs(F, orc, grid, rounding, NV16, rht, 3, 11)
+        mr, mc = own_maxima(orc, xb, oc)
+        for factor in (1.0, 0.25, 3.0):
+            gr, gc = np.float32(mr * np.float32(factor)), np.float32(mc * np.float32(factor))
+            say(f"[delayed] {R}x{C} grid={grid} rnd={rounding} rht={rht} x{factor}")
+            row, col, a_out = gpu_delayed(env, xb, fc, [gr, gc])
+            want_r = orc.quantize_given_amax(xb, oc, ROW, float(gr))
+            want_c = orc.quantize_given_amax(xb, oc, COL, float(gc))
+            assert_layout_equal(row, want_r[:3], f"row x{factor}")
+            assert_layout_equal(col, want_c[:3], f"col x{factor}")
+            if factor == 1.0:
+                assert_layout_equal(row, orc.quantize(xb, oc, ROW), "row = exact path")
+                assert_layout_equal(col, orc.quantize(xb, oc, COL), "col = exact path")
+            t = a_out.cpu().numpy()
+            assert (t >= 0).all(), "every tile maximum written"
+            assert t[:, 0].max() == mr and t[:, 1].max() == mc
+
+
+def test_delayed_chain_reaches_exact_path(env):
+    # a first call with an arbitrary provided maximum; its tile maxima, passed
+    # as they are, make the second call the exact (own-maximum) quantization
+    torch, F, orc = env
+    R, C = 1040, 1024
+    xb = synth.activation(R, C, seed=50)
+    fc, oc = cfgs(F, orc, E1M2, RTNE, NV16, 1, 4, 4)
+    _, _, a1 = gpu_delayed(env, xb, fc, [1.0, 1.0])
+    row, col, a2 = gpu_delayed(env, xb, fc, a1)
+    assert_layout_equal(row, orc.quantize(xb, oc, ROW), "row")
+    assert_layout_equal(col, orc.quantize(xb, oc, COL), "col")
+    assert torch.equal(a1, a2)
+
+
+def test_delayed_row_only_nonfinite_and_many_entries(env):
+    torch, F, orc = env
+    R, C = 200, 256
+    xb = synth.output_grad(R, C, seed=51)
+    fc, oc = cfgs(F, orc, E1M2, SR, NV16, 1, 6, 6)
+    # entries that are not positive finite numbers count as zero: S_t = 1
+    row, _, _ = gpu_delayed(env, xb, fc, [np.nan, np.inf, -1.0, 0.0, -np.inf, np.nan], col=False)
+    assert_layout_equal(row, orc.quantize_given_amax(xb, oc, ROW, 0.0)[:3], "non-finite")
+    # 700 entries (more than one per thread); the largest row-wise entry decides
+    mr = np.float32(orc.quantize_given_amax(xb, oc, ROW, 1.0)[3])  # (200 rows: no column layout)
+    ent = np.zeros((700, 2), np.float32)
+    ent[:, 0] = np.linspace(0, 0.5, 700, dtype=np.float32) * mr
+    ent[650, 0] = mr * np.float32(0.75)
+    ent[:, 1] = np.nan
+    row, _, a_out = gpu_delayed(env, xb, fc, ent, col=False)
+    assert_layout_equal(row, orc.quantize_given_amax(xb, oc, ROW, float(ent[:, 0].max()))[:3], "700 entries")
+    t = a_out.cpu().numpy()
+    assert t[:, 0].max() == mr and (t[:, 1] == 0).all()
+
+
 # -------------------------------------------------------------- single pass
 @pytest.mark.parametrize("stride", [2, 3, 7])
 @pytest.mark.parametrize("rounding", [RTNE, SR])
