@@ -233,6 +233,16 @@ def grouped_col_offsets(offsets, block: int) -> np.ndarray:
     return col
 
 
+def gemm_nt_reference(a, b, cfg: Config, M: int, N: int, K: int) -> np.ndarray:
+    """The product the consumer GEMM computes, in float64: each operand
+    (codes, scales, tensor_scale) of an M x K / N x K row-wise layout is
+    dequantized by the oracle (no inverse transform), then
+    C = A_hat @ B_hat^T.  Returns (C, |A_hat| @ |B_hat|^T) for error bounds."""
+    ah = dequantize(a[0], a[1], a[2], M, K, cfg).astype(np.float64)
+    bh = dequantize(b[0], b[1], b[2], N, K, cfg).astype(np.float64)
+    return ah @ bh.T, np.abs(ah) @ np.abs(bh).T
+
+
 def quantize_given_amax(x_bf16: np.ndarray, cfg: Config, layout: int, amax_given: float):
     """Delayed scaling (NV16): quantize with the tensor scale taken from
     amax_given.  Returns (codes, scales, tensor_scale, amax_seen)."""

@@ -402,3 +402,30 @@ def test_given_maximum_not_positive_finite_counts_as_zero(orc):
         assert t[0] == 1.0
         np.testing.assert_array_equal(s, ref[1])
         np.testing.assert_array_equal(c, ref[0])
+
+
+# ------------------------------------------------------ consumer GEMM reference
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1_CLAMP])
+def test_gemm_reference_is_the_product_of_exactly_quantized_inputs(orc, grid):
+    # Grid-valued blocks with their maximum at +-Qmax 2^k quantize exactly
+    # (RHT off), so the reference must equal X @ W^T of the inputs themselves;
+    # a transposed operand or a lost tensor scale fails it.
+    rng = np.random.default_rng(30 + grid)
+    mags = value_table(orc, grid)
+    top = 4 if grid == E2M1_CLAMP else 7
+
+    def exact_matrix(rows, cols, scale):
+        k = rng.integers(0, top + 1, size=(rows, cols))
+        neg = rng.integers(0, 2, size=(rows, cols)).astype(bool) & (k > 0)
+        c = np.where(neg, ((16 - k) % 16) if grid == INT4 else (8 | k), k).astype(np.uint8)
+        c[:, ::16] = top
+        return (mags[c] * scale).astype(np.float32)
+
+    M, N, K = 24, 40, 64
+    x, w = exact_matrix(M, K, 4.0), exact_matrix(N, K, 0.5)
+    cfg = orc.config(grid=grid, rht=0)
+    a = orc.quantize(synth.f32_to_bf16(x), cfg, ROW)
+    b = orc.quantize(synth.f32_to_bf16(w), cfg, ROW)
+    c, mag = orc.gemm_nt_reference(a, b, cfg, M, N, K)
+    np.testing.assert_array_equal(c, x.astype(np.float64) @ w.astype(np.float64).T)
+    assert (mag >= np.abs(c)).all()
