@@ -349,6 +349,18 @@ def main():
                 raise F.Ufp4Error("ufp4_quantize_delayed", rc)
         dfns.append(dfn)
     ms_delayed, _ = time_graph(torch, dfns, args.steps - args.steps % len(sets) or len(sets), args.warmup, stream)
+    # consumer GEMM (reported beside): the activation's row-wise codes times a
+    # quantized 8192 x 2048 weight's, C = X W^T of 8192 x 8192 (fwd_y), K = 2048
+    wq = F.alloc_layout(ROWS, COLS, F.SCALE_NV16, device=dev)
+    wx = torch.from_numpy(synth.weight(ROWS, COLS, seed=2).view(np.int16)).to(dev)
+    F.ufp4_quantize(wx, cfg, wq, sets[0][3])
+    gc = torch.empty((ROWS, ROWS), dtype=torch.float32, device=dev)
+    xq = sets[0][1]
+    gemm_fns = [lambda: F.ufp4_gemm_nt(cfg, xq, wq, ROWS, ROWS, COLS, gc, stream)]
+    gemm_steps = 20
+    ms_gemm, _ = time_graph(torch, gemm_fns, gemm_steps, 3, stream)
+    gemm_tflops = 2.0 * ROWS * ROWS * COLS / (ms_gemm * 1e-3) / 1e12
+    del gc
     # the other schedule on the same buffers, for comparison
     other = "two_pass" if single else "single_pass"
     F.ufp4_set_schedule(F.SCHEDULE_TWO_PASS if single else F.SCHEDULE_SINGLE_PASS)
@@ -413,6 +425,9 @@ def main():
     }
     if two:
         line["extra"].update(two)
+    line["extra"]["gemm_8192x8192x2048_ms"] = round(ms_gemm, 6)
+    line["extra"]["gemm_tflops"] = round(gemm_tflops, 1)
+    line["extra"]["gemm_frac_of_bf16_mfma_peak"] = round(gemm_tflops / 2500.0, 4)
     line["extra"]["delayed_scaling_ms"] = round(ms_delayed, 6)
     line["extra"]["delayed_scaling_gbps"] = round(nbytes / (ms_delayed * 1e-3) / 1e9, 2)
     if ms_warm is not None:

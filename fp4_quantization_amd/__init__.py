@@ -18,7 +18,7 @@ from ._lib import (GRID_E1M2, GRID_E2M1, GRID_E2M1C, GRID_INT4, LIB_PATH, ROUND_
 
 __all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "GRID_E2M1C", "ROUND_RTNE", "ROUND_STOCHASTIC", "SCALE_NV16",
            "SCALE_MX32", "SCHEDULE_AUTO", "SCHEDULE_TWO_PASS", "SCHEDULE_SINGLE_PASS", "ufp4_set_schedule",
-           "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
+           "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "ufp4_gemm_nt", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
            "ufp4_quantize", "ufp4_quantize_rowcol", "ufp4_quantize_grouped", "ufp4_dequantize",
            "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol",
            "block_len"]
@@ -129,6 +129,15 @@ def ufp4_set_schedule(schedule: int, left_stride: int = 0) -> None:
     _SINGLE_PASS); left_stride > 1 makes the single pass leave every tile whose
     index is not a multiple of it to the other workgroups (test hook)."""
     check("ufp4_set_schedule", lib.ufp4_set_schedule(int(schedule), int(left_stride)))
+
+
+def ufp4_gemm_nt(cfg: ufp4_config, a: QTensor, b: QTensor, M: int, N: int, K: int, c: torch.Tensor,
+                 stream=None) -> None:
+    """c[m][n] = sum_k deq(a)[m][k] deq(b)[n][k] for NV16 row-wise layouts of
+    an M x K and an N x K matrix; c float32 [M][ldc >= N] on the device."""
+    assert c.dtype == torch.float32 and c.dim() == 2 and c.stride(1) == 1
+    check("ufp4_gemm_nt", lib.ufp4_gemm_nt(ctypes.byref(cfg), int(M), int(N), int(K), a.c(), b.c(), _ptr(c),
+                                           c.stride(0), _stream(stream)))
 
 
 def ufp4_amax_tiles(rows: int, cols: int) -> int:

@@ -26,7 +26,7 @@ EXPORTED = ["ufp4_status_string", "ufp4_workspace_size", "ufp4_workspace_init",
             "ufp4_workspace_status", "ufp4_quantize", "ufp4_quantize_rowcol",
             "ufp4_quantize_grouped", "ufp4_dequantize", "ufp4_stats", "ufp4_round_f32",
             "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol", "ufp4_set_schedule",
-            "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed"]
+            "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "ufp4_gemm_nt"]
 
 
 class Ufp4Error(RuntimeError):
@@ -96,6 +96,8 @@ def _load():
     L.ufp4_grouped_col_offsets.argtypes = [P, i32, i32, P]
     L.ufp4_set_schedule.restype = ctypes.c_int
     L.ufp4_set_schedule.argtypes = [i32, i32]
+    L.ufp4_gemm_nt.restype = ctypes.c_int
+    L.ufp4_gemm_nt.argtypes = [cfgp, i64, i64, i64, ufp4_qtensor, ufp4_qtensor, P, i64, P]
     L.ufp4_amax_tiles.restype = i64
     L.ufp4_amax_tiles.argtypes = [i64, i64]
     L.ufp4_quantize_delayed.restype = ctypes.c_int

@@ -162,6 +162,37 @@ int ufp4_workspace_init(void* ws, size_t ws_bytes, ufp4_stream_t stream) {
   return UFP4_OK;
 }
 
+int ufp4_gemm_nt(const ufp4_config* cfg, int64_t M, int64_t N, int64_t K, ufp4_qtensor a, ufp4_qtensor b,
+                 float* c, int64_t ldc, ufp4_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->scaling != UFP4_SCALE_NV16) return UFP4_ERR_INVALID_ARGUMENT;
+  if (M < 0 || N < 0 || K < 0 || ldc < N) return UFP4_ERR_INVALID_ARGUMENT;
+  if (K % 32) return UFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return UFP4_OK;
+  if (!c || !a.tensor_scale || !b.tensor_scale) return UFP4_ERR_INVALID_ARGUMENT;
+  if (K > 0 && (!a.codes || !a.scales || !b.codes || !b.scales)) return UFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(a.codes, 16) || !aligned(b.codes, 16) || !aligned(c, 4) || !aligned(a.tensor_scale, 4) ||
+      !aligned(b.tensor_scale, 4))
+    return UFP4_ERR_ALIGNMENT;
+  if ((M + 127) / 128 > 0xFFFF || (N + 127) / 128 > 0x7FFFFFFF) return UFP4_ERR_SHAPE;
+  GemmParams p;
+  p.a_codes = a.codes;
+  p.a_scales = a.scales;
+  p.a_ts = a.tensor_scale;
+  p.b_codes = b.codes;
+  p.b_scales = b.scales;
+  p.b_ts = b.tensor_scale;
+  p.c = c;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.ldc = ldc;
+  p.grid = cfg->grid;
+  if (launch_gemm(p, (hipStream_t)stream) != hipSuccess) return UFP4_ERR_HIP;
+  return UFP4_OK;
+}
+
 int64_t ufp4_amax_tiles(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0) return 0;
   int32_t nb, nt;

@@ -114,4 +114,19 @@ hipError_t launch_stats(const StatsParams& p, hipStream_t s);
 hipError_t launch_round(const float* y, int64_t n, int32_t grid, int32_t rounding, uint64_t seed,
                         uint8_t* codes, hipStream_t s);
 
+// Consumer GEMM of two NV16 row-wise layouts along K (codes [rows][K/2],
+// scales [rows][K/16], one tensor scale each); C row-major with stride ldc.
+struct GemmParams {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_ts;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const float* b_ts;
+  float* c;
+  int64_t M, N, K, ldc;
+  int32_t grid;
+};
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
 }  // namespace ufp4

@@ -201,6 +201,24 @@ int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_
                const float* tensor_scale, void* ws, size_t ws_bytes, ufp4_stats_t* host_out,
                ufp4_stream_t stream);
 
+/* --- consumer GEMM -------------------------------------------------------- */
+
+/* c[m][n] = sum_k xa[m][k] * xb[n][k] (fp32, row-major with stride ldc), where
+ * xa and xb are the dequantized values of a and b: NV16 row-wise layouts of
+ * an M x K and an N x K matrix (codes [rows][K/2], scales [rows][K/16], one
+ * tensor scale), blocks along K, the reduction dimension of the training
+ * GEMMs ("Shrinkage Bias: The Hidden Geometric Trap in FP4 Training"
+ * (zhichai.net), "Key points": the fix quantizes the operands of all three).
+ * Operands quantized with the same RHT signs give the product of the
+ * untransformed matrices (the transform is orthonormal).  Each dequantized
+ * value is exact in bf16; the products are summed on the bf16 MFMA in fp32,
+ * so c differs from the exact sum only by fp32 accumulation order.
+ * cfg: grid of both operands; NV16 only.  K % 32 == 0 (UFP4_ERR_SHAPE);
+ * ldc >= N; codes 16-byte aligned.  M or N of 0 writes nothing; K of 0
+ * writes zeros. */
+int ufp4_gemm_nt(const ufp4_config* cfg, int64_t M, int64_t N, int64_t K, ufp4_qtensor a, ufp4_qtensor b,
+                 float* c, int64_t ldc, ufp4_stream_t stream);
+
 /* --- delayed scaling ------------------------------------------------------ */
 
 /* Pairs of maxima a delayed call on a rows x cols tensor writes to amax_out

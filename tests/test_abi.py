@@ -76,6 +76,21 @@ def test_delayed_arguments(F):
     assert call(x, 64, 64, 64, ctypes.byref(cfg), a_in, 1, a_out, none, q, None) == 1  # row output needed
 
 
+def test_gemm_arguments(F):
+    cfg, mx = F.config(), F.config(scaling=F.SCALE_MX32)
+    q = F.ufp4_qtensor(ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(12288))
+    c = ctypes.c_void_p(1 << 20)
+    g = F.lib.ufp4_gemm_nt
+    assert g(ctypes.byref(mx), 16, 16, 32, q, q, c, 16, None) == 1    # MX32
+    assert g(ctypes.byref(cfg), 16, 16, 48, q, q, c, 16, None) == 2   # K % 32
+    assert g(ctypes.byref(cfg), 16, 16, 32, q, q, c, 8, None) == 1    # ldc < N
+    assert g(ctypes.byref(cfg), -1, 16, 32, q, q, c, 16, None) == 1
+    assert g(ctypes.byref(cfg), 16, 16, 32, q, q, None, 16, None) == 1
+    bad = F.ufp4_qtensor(ctypes.c_void_p(4100), ctypes.c_void_p(8192), ctypes.c_void_p(12288))
+    assert g(ctypes.byref(cfg), 16, 16, 32, bad, q, c, 16, None) == 3
+    assert g(ctypes.byref(cfg), 0, 16, 32, q, q, c, 16, None) == 0    # nothing to do
+
+
 def test_set_schedule_arguments(F):
     assert F.lib.ufp4_set_schedule(3, 0) == 1
     assert F.lib.ufp4_set_schedule(-1, 0) == 1

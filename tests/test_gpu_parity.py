@@ -316,6 +316,73 @@ def test_delayed_row_only_nonfinite_and_many_entries(env):
     assert t[:, 0].max() == mr and (t[:, 1] == 0).all()
 
 
+# ------------------------------------------------------------ consumer GEMM
+def upload(torch, F, q, rows, cols):
+    """An oracle-quantized row-wise layout as a device QTensor."""
+    qt = F.alloc_layout(rows, cols, NV16)
+    qt.codes.copy_(torch.from_numpy(np.ascontiguousarray(q[0])))
+    qt.scales.copy_(torch.from_numpy(np.ascontiguousarray(q[1])))
+    qt.tensor_scale.copy_(torch.from_numpy(np.ascontiguousarray(q[2])))
+    return qt
+
+
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
+def test_gemm_matches_oracle_reference(env, grid):
+    # operands quantized by the oracle; the GEMM against the float64 product
+    # of the oracle's dequantized operands, within the fp32 accumulation bound
+    torch, F, orc = env
+    for M, N, K in ((256, 384, 512), (130, 70, 96), (1, 1, 32), (300, 129, 2048)):
+        say(f"[gemm] grid={grid} {M}x{N}x{K}")
+        fc, oc = cfgs(F, orc, grid, RTNE, NV16, 1, 7, 7)
+        a = orc.quantize(synth.activation(M, K, seed=M + K), oc, ROW)
+        b = orc.quantize(synth.weight(N, K, seed=N + K), oc, ROW)
+        ref, mag = orc.gemm_nt_reference(a, b, oc, M, N, K)
+        c = torch.full((M, N + 3), np.nan, dtype=torch.float32, device="cuda")[:, :N]
+        F.ufp4_gemm_nt(fc, upload(torch, F, a, M, K), upload(torch, F, b, N, K), M, N, K, c)
+        torch.cuda.synchronize()
+        got = c.cpu().numpy().astype(np.float64)
+        bound = (K + 4) * 2.0 ** -24 * mag + 1e-30
+        err = np.abs(got - ref)
+        assert (err <= bound).all(), f"max err/bound {float((err / bound).max()):.3g}"
+
+
+def test_gemm_exact_on_exactly_representable_products(env):
+    # integer-valued operands (INT4 codes, unit block scales, unit tensor
+    # scales) with small sums: every partial sum is an integer below 2^24,
+    # so the fp32 MFMA result is exact
+    torch, F, orc = env
+    rng = np.random.default_rng(40)
+    M, N, K = 64, 96, 256
+    fc, oc = cfgs(F, orc, INT4, RTNE, NV16, 0, 0, 0)
+
+    def layout(rows):
+        k = rng.integers(-7, 8, size=(rows, K))
+        nib = (k & 15).astype(np.uint8)
+        codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+        scales = np.full((rows, K // 16), 0x38, np.uint8)  # E4M3 1.0
+        return (codes, scales, np.ones(1, np.float32)), k.astype(np.float64)
+
+    (a, ka), (b, kb) = layout(M), layout(N)
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    F.ufp4_gemm_nt(fc, upload(torch, F, a, M, K), upload(torch, F, b, N, K), M, N, K, c)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c.cpu().numpy().astype(np.float64), ka @ kb.T)
+    ref, _ = orc.gemm_nt_reference(a, b, oc, M, N, K)
+    np.testing.assert_array_equal(ref, ka @ kb.T)
+
+
+def test_gemm_degenerate_shapes(env):
+    torch, F, orc = env
+    fc, oc = cfgs(F, orc)
+    a = F.alloc_layout(16, 32, NV16)
+    a.tensor_scale.fill_(1.0)
+    c = torch.full((16, 16), 5.0, dtype=torch.float32, device="cuda")
+    F.ufp4_gemm_nt(fc, a, a, 16, 16, 0, c)  # K = 0: zeros
+    F.ufp4_gemm_nt(fc, a, a, 0, 16, 32, c)  # M = 0: nothing written
+    torch.cuda.synchronize()
+    assert bool((c == 0).all())
+
+
 # -------------------------------------------------------------- single pass
 @pytest.mark.parametrize("stride", [2, 3, 7])
 @pytest.mark.parametrize("rounding", [RTNE, SR])
