@@ -77,6 +77,7 @@ def counter_traffic(single: bool):
 
 
 FUSED_KERNEL = "ufp4_fused_kernel<0, false, true>"
+DELAYED_KERNEL = "ufp4_delayed_kernel<0, false, true>"
 AMAX_KERNEL = "ufp4_amax_kernel<true>"
 QUANT_KERNEL = "ufp4_quant_kernel<0, false, false, true>"
 
@@ -133,14 +134,17 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
     _, wf_ = pick(write, FUSED_KERNEL)
     _, wa = pick(write, AMAX_KERNEL)
     _, wq = pick(write, QUANT_KERNEL)
+    kd, fd = pick(fetch, DELAYED_KERNEL)
+    _, wd = pick(write, DELAYED_KERNEL)
+    delayed = (fd * ff + wd * wf) * 1024
     fused = (ff_ * ff + wf_ * wf) * 1024
     quant = (fq * ff + wq * wf) * 1024
     call = quant + (fa * ff + wa * wf) * 1024
-    out = {"fetch_kib_raw": {kf: ff_, ka: fa, kq: fq}, "write_kib_raw": {kf: wf_, ka: wa, kq: wq},
+    out = {"fetch_kib_raw": {kf: ff_, ka: fa, kq: fq, kd: fd}, "write_kib_raw": {kf: wf_, ka: wa, kq: wq, kd: wd},
            "copy_calibration": {"copy_bytes": copy_kib * 1024, "fetch_kib_raw": copy_fetch,
                                 "write_kib_raw": copy_write, "fetch_factor": ff, "write_factor": wf},
            "hbm_bytes": {"single_pass_kernel": round(fused), "two_pass_quant_kernel": round(quant),
-                         "two_pass_call": round(call)},
+                         "two_pass_call": round(call), "delayed_kernel": round(delayed)},
            "algorithmic_bytes_per_call": algorithmic_bytes(ROWS, COLS),
            "kernel_source_sha256": kernel_source_sha(), "commands": commands,
            "note": "KiB per dispatch, mean over dispatches; bytes = (fetch * fetch_factor + "
