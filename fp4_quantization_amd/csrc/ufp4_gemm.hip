@@ -8,45 +8,79 @@
 // same RHT signs multiply to the product of the untransformed matrices, the
 // transform being orthonormal.
 //
-// Dequantization is exact in bf16: a grid value (at most 3 significant
+// Dequantization is exact in fp16: a grid value (at most 3 significant
 // bits: k/2, k or an E2M1 value) times an E4M3 block scale (4 significant
-// bits) needs at most 7 bits, within bf16's 8.  So each workgroup expands its
-// operand tiles to bf16 in LDS, multiplies them on the bf16 MFMA with fp32
-// accumulation, and applies the two tensor scales in the epilogue.  Results
-// differ from an exact sum only by the fp32 accumulation order.
+// bits) needs at most 7 bits and lies in [2^-10, 2688], inside fp16's normal
+// range.  So each workgroup expands its operand tiles to fp16 in LDS,
+// multiplies them on the fp16 MFMA with fp32 accumulation (the products are
+// exact), and applies the two tensor scales in the epilogue.  Results differ
+// from an exact sum only by the fp32 accumulation order.
+//
+// The expansion is byte arithmetic: every grid value's fp16 encoding has a
+// zero low byte, so one byte permute looks the high bytes of four codes up in
+// an 8-entry table, an OR adds their signs, a second permute interleaves the
+// zero low bytes, and a packed fp16 multiply applies the block scale.
 #include <hip/hip_runtime.h>
 
 #include "ufp4_internal.hpp"
 
 namespace ufp4 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t g32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t g32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmM = 128, kGemmN = 128, kGemmK = 32;
-constexpr int kGemmLd = kGemmK + 8;  // bf16 per LDS row: 80 bytes, 16-byte aligned rows
+constexpr int kGemmLd = kGemmK + 8;  // fp16 per LDS row: 80 bytes, 16-byte aligned rows
 
-// Two dequantized values as one bf16 pair (exact: at most 7 significant bits).
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
+// High bytes of the fp16 encodings of the grid magnitudes by magnitude
+// index (low word: indices 0..3, high word: 4..7).
+template <int GRID>
+__device__ __forceinline__ uint32_t f16_hi_lo() {
+  return GRID == kGridINT4 ? 0x42403C00u : 0x3E3C3800u;  // {0, 1, 2, 3} / {0, .5, 1, 1.5}
+}
+template <int GRID>
+__device__ __forceinline__ uint32_t f16_hi_hi() {
+  return GRID == kGridE1M2 ? 0x43424140u    // 2, 2.5, 3, 3.5
+         : GRID == kGridINT4 ? 0x47464544u  // 4, 5, 6, 7
+                             : 0x46444240u; // 2, 3, 4, 6 (E2M1; the clamped grid uses 0..4)
 }
 
-// One 16-element block: 8 code bytes (element 2i in the low nibble of byte
-// i) and its E4M3 scale byte, to 16 bf16 values at dst (16-byte aligned).
+// Two's-complement nibbles -> sign-magnitude nibbles, eight at a time (for
+// a negative nibble n, |n| = (n ^ 7) + 1 with the sign bit kept).
+__device__ __forceinline__ uint32_t signmag8(uint32_t P) {
+  const uint32_t A = P & 0x88888888u, S = A >> 3;
+  return (P ^ (A - S)) + S;
+}
+
+// Eight codes (element 2i in the low nibble of byte i) to four fp16 pairs
+// times the block scale d2 = (d, d).
 template <int GRID>
-__device__ __forceinline__ void dequant16(g32x2 codes, uint32_t sbyte, __bf16* dst) {
-  const float d = e4m3_decode_pos(sbyte & 0x7Fu);
+__device__ __forceinline__ void expand8(uint32_t word, f16x2 d2, uint32_t out[4]) {
+  if (GRID == kGridINT4) word = signmag8(word);
+  const uint32_t lo = f16_hi_lo<GRID>(), hi = f16_hi_hi<GRID>();
+  // high bytes of the even (low-nibble) and odd (high-nibble) elements
+  const uint32_t he = __builtin_amdgcn_perm(hi, lo, word & 0x07070707u) | ((word << 4) & 0x80808080u);
+  const uint32_t ho = __builtin_amdgcn_perm(hi, lo, (word >> 4) & 0x07070707u) | (word & 0x80808080u);
+  // (element 2i, element 2i+1) = (0x00, he.byte i, 0x00, ho.byte i); selector
+  // 0x0C gives a zero byte, 0..3 the bytes of he, 4..7 those of ho
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(ho, he, 0x040C000Cu)) * d2);
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(ho, he, 0x050C010Cu)) * d2);
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(ho, he, 0x060C020Cu)) * d2);
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(ho, he, 0x070C030Cu)) * d2);
+}
+
+// One 16-element block: 8 code bytes and its E4M3 scale byte, to 16 fp16
+// values at dst (16-byte aligned).
+template <int GRID>
+__device__ __forceinline__ void dequant16(g32x2 codes, uint32_t sbyte, _Float16* dst) {
+  const _Float16 d = (_Float16)e4m3_decode_pos(sbyte & 0x7Fu);  // exact: E4M3 values are fp16 values
+  const f16x2 d2 = {d, d};
   uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t word = i < 4 ? codes.x : codes.y;
-    const uint32_t c0 = (word >> (8 * (i & 3))) & 15u, c1 = (word >> (8 * (i & 3) + 4)) & 15u;
-    o[i] = pack_bf16(code_value<GRID>(c0) * d, code_value<GRID>(c1) * d);
-  }
+  expand8<GRID>(codes.x, d2, o);
+  expand8<GRID>(codes.y, d2, o + 4);
   g32x4* p = reinterpret_cast<g32x4*>(dst);
   p[0] = g32x4{o[0], o[1], o[2], o[3]};
   p[1] = g32x4{o[4], o[5], o[6], o[7]};
@@ -59,8 +93,8 @@ __device__ __forceinline__ void dequant16(g32x2 codes, uint32_t sbyte, __bf16* d
 // while the current step multiplies.
 template <int GRID>
 __global__ __launch_bounds__(kThreads) void ufp4_gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 As[kGemmM][kGemmLd];
-  __shared__ __attribute__((aligned(16))) __bf16 Bs[kGemmN][kGemmLd];
+  __shared__ __attribute__((aligned(16))) _Float16 As[kGemmM][kGemmLd];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[kGemmN][kGemmLd];
   const int64_t m0 = (int64_t)blockIdx.y * kGemmM, n0 = (int64_t)blockIdx.x * kGemmN;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
@@ -102,16 +136,16 @@ __global__ __launch_bounds__(kThreads) void ufp4_gemm_kernel(GemmParams p) {
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 fa[2], fb[2];
+      f16x8 fa[2], fb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        fa[i] = *reinterpret_cast<const bf16x8*>(&As[wm + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
-        fb[i] = *reinterpret_cast<const bf16x8*>(&Bs[wn + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+        fa[i] = *reinterpret_cast<const f16x8*>(&As[wm + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+        fb[i] = *reinterpret_cast<const f16x8*>(&Bs[wn + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
   }
   const float s = p.a_ts[0] * p.b_ts[0];
