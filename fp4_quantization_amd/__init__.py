@@ -12,7 +12,9 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import (GRID_E1M2, GRID_E2M1, GRID_E2M1C, GRID_INT4, LIB_PATH, ROUND_RTNE, ROUND_STOCHASTIC,
+from ._lib import (GEMM_BWD_DW, GEMM_BWD_DX, GEMM_FWD_Y, OPERAND_A, OPERAND_B, RECIPE_NVFP4, RECIPE_UFP4,
+                   RECIPE_UFP4_INT4, TENSOR_DY, TENSOR_W, TENSOR_X,
+                   GRID_E1M2, GRID_E2M1, GRID_E2M1C, GRID_INT4, LIB_PATH, ROUND_RTNE, ROUND_STOCHASTIC,
                    SCALE_MX32, SCALE_NV16, SCHEDULE_AUTO, SCHEDULE_SINGLE_PASS, SCHEDULE_TWO_PASS, Ufp4Error, check, lib, ufp4_config, ufp4_qtensor,
                    ufp4_stats_t)
 
@@ -21,7 +23,9 @@ __all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "GRID_E2M1C", "ROUND_RTNE", "R
            "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "ufp4_gemm_nt", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
            "ufp4_quantize", "ufp4_quantize_rowcol", "ufp4_quantize_grouped", "ufp4_dequantize",
            "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol",
-           "block_len"]
+           "block_len", "ufp4_recipe_config", "RECIPE_UFP4", "RECIPE_UFP4_INT4", "RECIPE_NVFP4",
+           "GEMM_FWD_Y", "GEMM_BWD_DX", "GEMM_BWD_DW", "OPERAND_A", "OPERAND_B", "TENSOR_X", "TENSOR_W",
+           "TENSOR_DY"]
 
 
 def config(grid: int = GRID_E1M2, rounding: int = ROUND_RTNE, scaling: int = SCALE_NV16,
@@ -223,3 +227,14 @@ def ufp4_grouped_col_offsets(offsets, block: int) -> np.ndarray:
           lib.ufp4_grouped_col_offsets(off.ctypes.data_as(ctypes.c_void_p), off.size - 1, int(block),
                                        out.ctypes.data_as(ctypes.c_void_p)))
     return out
+
+
+def ufp4_recipe_config(recipe: int, gemm: int, operand: int, rht_seed: int = 0, sr_seed: int = 0):
+    """(config, layout, tensor) of one operand of one training GEMM under a
+    recipe: layout 0 row-wise / 1 column-wise, tensor TENSOR_X/W/DY."""
+    cfg = ufp4_config()
+    layout, tensor = ctypes.c_int32(), ctypes.c_int32()
+    check("ufp4_recipe_config", lib.ufp4_recipe_config(int(recipe), int(gemm), int(operand), int(rht_seed),
+                                                       int(sr_seed), ctypes.byref(cfg), ctypes.byref(layout),
+                                                       ctypes.byref(tensor)))
+    return cfg, layout.value, tensor.value

@@ -21,12 +21,17 @@ GRID_E1M2, GRID_INT4, GRID_E2M1, GRID_E2M1C = 0, 1, 2, 3
 ROUND_RTNE, ROUND_STOCHASTIC = 0, 1
 SCALE_NV16, SCALE_MX32 = 0, 1
 SCHEDULE_AUTO, SCHEDULE_TWO_PASS, SCHEDULE_SINGLE_PASS = 0, 1, 2
+RECIPE_UFP4, RECIPE_UFP4_INT4, RECIPE_NVFP4 = 0, 1, 2
+GEMM_FWD_Y, GEMM_BWD_DX, GEMM_BWD_DW = 0, 1, 2
+OPERAND_A, OPERAND_B = 0, 1
+TENSOR_X, TENSOR_W, TENSOR_DY = 0, 1, 2
 
 EXPORTED = ["ufp4_status_string", "ufp4_workspace_size", "ufp4_workspace_init",
             "ufp4_workspace_status", "ufp4_quantize", "ufp4_quantize_rowcol",
             "ufp4_quantize_grouped", "ufp4_dequantize", "ufp4_stats", "ufp4_round_f32",
             "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol", "ufp4_set_schedule",
-            "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "ufp4_gemm_nt"]
+            "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "ufp4_gemm_nt",
+            "ufp4_recipe_config"]
 
 
 class Ufp4Error(RuntimeError):
@@ -102,6 +107,8 @@ def _load():
     L.ufp4_amax_tiles.argtypes = [i64, i64]
     L.ufp4_quantize_delayed.restype = ctypes.c_int
     L.ufp4_quantize_delayed.argtypes = [P, i64, i64, i64, cfgp, P, i32, P, ufp4_qtensor, ufp4_qtensor, P]
+    L.ufp4_recipe_config.restype = ctypes.c_int
+    L.ufp4_recipe_config.argtypes = [i32, i32, i32, u64, u64, cfgp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ufp4_schedule_of.restype = ctypes.c_int
     L.ufp4_schedule_of.argtypes = [i64, i64, i32, cfgp, ctypes.POINTER(i32)]
     return L

@@ -516,6 +516,33 @@ int ufp4_round_f32(const float* y_dev, int64_t n, int32_t grid, int32_t rounding
              : UFP4_ERR_HIP;
 }
 
+int ufp4_recipe_config(int32_t recipe, int32_t gemm, int32_t operand, uint64_t rht_seed, uint64_t sr_seed,
+                       ufp4_config* cfg_out, int32_t* layout_out, int32_t* tensor_out) {
+  if (!cfg_out || !layout_out || !tensor_out) return UFP4_ERR_INVALID_ARGUMENT;
+  if (recipe < UFP4_RECIPE_UFP4 || recipe > UFP4_RECIPE_NVFP4 || gemm < UFP4_GEMM_FWD_Y ||
+      gemm > UFP4_GEMM_BWD_DW || (operand != UFP4_OPERAND_A && operand != UFP4_OPERAND_B))
+    return UFP4_ERR_INVALID_ARGUMENT;
+  // operand tensors and layouts: the reduction dimension of each product
+  // runs along the quantization blocks
+  static const int32_t kTensor[3][2] = {{UFP4_TENSOR_X, UFP4_TENSOR_W},
+                                        {UFP4_TENSOR_DY, UFP4_TENSOR_W},
+                                        {UFP4_TENSOR_DY, UFP4_TENSOR_X}};
+  static const int32_t kLayout[3][2] = {{0, 0}, {0, 1}, {1, 1}};
+  const int32_t tensor = kTensor[gemm][operand];
+  ufp4_config c;
+  c.grid = recipe == UFP4_RECIPE_UFP4 ? UFP4_GRID_E1M2 : recipe == UFP4_RECIPE_UFP4_INT4 ? UFP4_GRID_INT4
+                                                                                          : UFP4_GRID_E2M1;
+  c.scaling = UFP4_SCALE_NV16;
+  c.rht = recipe == UFP4_RECIPE_NVFP4 ? (gemm == UFP4_GEMM_BWD_DW ? 1 : 0) : 1;
+  c.rounding = tensor == UFP4_TENSOR_DY ? UFP4_ROUND_STOCHASTIC : UFP4_ROUND_RTNE;
+  c.rht_seed = rht_seed;
+  c.sr_seed = c.rounding == UFP4_ROUND_STOCHASTIC ? sr_seed : 0u;
+  *cfg_out = c;
+  *layout_out = kLayout[gemm][operand];
+  *tensor_out = tensor;
+  return UFP4_OK;
+}
+
 int ufp4_rht_signs(uint64_t rht_seed, int8_t signs_host[16]) {
   if (!signs_host) return UFP4_ERR_INVALID_ARGUMENT;
   const uint32_t mask = rht_sign_mask(rht_seed);

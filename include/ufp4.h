@@ -281,6 +281,43 @@ int ufp4_set_schedule(int32_t schedule, int32_t left_stride);
 int ufp4_schedule_of(int64_t rows, int64_t cols, int32_t num_groups, const ufp4_config* cfg,
                      int32_t* schedule_out);
 
+/* --- training recipes ------------------------------------------------------ */
+
+/* The quantization of each operand of the three training GEMMs under a
+ * recipe.  The GEMMs of a linear layer Y = X W^T (X: tokens x in, W: out x in,
+ * dY: tokens x out) and the operands ufp4_gemm_nt takes for them (a: M x K,
+ * b: N x K, blocks along K, the reduction dimension):
+ *   fwd_y  Y  = X W^T : a = X  row-wise,    b = W  row-wise     (K = in)
+ *   bwd_dx dX = dY W  : a = dY row-wise,    b = W  column-wise  (K = out)
+ *   bwd_dw dW = dY^T X: a = dY column-wise, b = X  column-wise  (K = tokens)
+ * Recipes:
+ *   UFP4: E1M2 grid, NV16 scales, RHT on all three GEMMs, stochastic
+ *     rounding on dY only, RTNE elsewhere ("Shrinkage Bias: The Hidden
+ *     Geometric Trap in FP4 Training" (zhichai.net), "Key points", the fix;
+ *     "UFP4 Eliminates Shrinkage Bias ..." (autonainews.com), "The UFP4
+ *     Recipe"; hotpaper.ai summary, technical approach).
+ *   UFP4_INT4: the same with the symmetric INT4 grid (autonainews.com, "The
+ *     UFP4 Recipe": E1M2 or INT4).
+ *   NVFP4: the E2M1 baseline, RHT on bwd_dw only (zhichai.net, "Key points":
+ *     the RHT paradox; practitioners on E2M1-only hardware restrict RHT to
+ *     bwd_dw).  The pages do not say where the baseline rounds
+ *     stochastically; it keeps UFP4's choice (dY only), so the two presets
+ *     differ only in the grid and the RHT coverage.
+ * Both operands of one GEMM must share rht_seed (the signs must match along
+ * K); sr_seed is used only where the preset rounds stochastically (0 is
+ * written otherwise).  Host only; UFP4_ERR_INVALID_ARGUMENT for an unknown
+ * enum value or a null output. */
+enum ufp4_recipe { UFP4_RECIPE_UFP4 = 0, UFP4_RECIPE_UFP4_INT4 = 1, UFP4_RECIPE_NVFP4 = 2 };
+enum ufp4_gemm_path { UFP4_GEMM_FWD_Y = 0, UFP4_GEMM_BWD_DX = 1, UFP4_GEMM_BWD_DW = 2 };
+enum ufp4_operand { UFP4_OPERAND_A = 0, UFP4_OPERAND_B = 1 };
+enum ufp4_tensor_role { UFP4_TENSOR_X = 0, UFP4_TENSOR_W = 1, UFP4_TENSOR_DY = 2 };
+
+/* Writes the configuration, the layout (0 row-wise, 1 column-wise) and the
+ * tensor (enum ufp4_tensor_role) of operand `operand` of GEMM `gemm` under
+ * `recipe`. */
+int ufp4_recipe_config(int32_t recipe, int32_t gemm, int32_t operand, uint64_t rht_seed, uint64_t sr_seed,
+                       ufp4_config* cfg_out, int32_t* layout_out, int32_t* tensor_out);
+
 /* --- diagnostic hooks (not on the hot path) ------------------------------ */
 
 /* codes_dev[i] = 4-bit code (one per byte) of y_dev[i] rounded at unit scale

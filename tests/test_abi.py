@@ -182,3 +182,45 @@ def test_other_entry_point_errors(F):
                           (cfg, 0, ctypes.byref(ms), ctypes.byref(ms))):
         assert F.lib.ufp4_time_rowcol(ctypes.c_void_p(FAKE), rows, 64, 64, ctypes.byref(c), q(F), q(F),
                                       ctypes.c_void_p(FAKE), 1 << 30, None, a, b) == 1
+
+
+# The recipes as the pages state them ("Shrinkage Bias: The Hidden Geometric
+# Trap in FP4 Training" (zhichai.net), "Key points"; "UFP4 Eliminates
+# Shrinkage Bias ..." (autonainews.com), "The UFP4 Recipe"): UFP4 puts the RHT
+# on all three GEMMs and rounds stochastically on dY only; the NVFP4 baseline
+# keeps the RHT to bwd_dw.
+RECIPE_EXPECT = {0: (0, {0, 1, 2}), 1: (1, {0, 1, 2}), 2: (2, {2})}  # recipe: (grid, GEMMs with RHT)
+
+
+def test_recipe_presets(F):
+    T, I, O = 48, 80, 112  # tokens, in, out: X [T][I], W [O][I], dY [T][O]
+    shape = {F.TENSOR_X: (T, I), F.TENSOR_W: (O, I), F.TENSOR_DY: (T, O)}
+    out_shape = {F.GEMM_FWD_Y: (T, O), F.GEMM_BWD_DX: (T, I), F.GEMM_BWD_DW: (O, I)}
+    for recipe, (grid, rht_gemms) in RECIPE_EXPECT.items():
+        for gemm in (F.GEMM_FWD_Y, F.GEMM_BWD_DX, F.GEMM_BWD_DW):
+            lines, lengths, seeds = [], [], set()
+            for operand in (F.OPERAND_A, F.OPERAND_B):
+                cfg, layout, tensor = F.ufp4_recipe_config(recipe, gemm, operand, rht_seed=77, sr_seed=5)
+                assert cfg.grid == grid and cfg.scaling == F.SCALE_NV16
+                assert cfg.rht == (1 if gemm in rht_gemms else 0)
+                sr = tensor == F.TENSOR_DY
+                assert cfg.rounding == (F.ROUND_STOCHASTIC if sr else F.ROUND_RTNE)
+                assert cfg.sr_seed == (5 if sr else 0)
+                seeds.add(cfg.rht_seed)
+                R, C = shape[tensor]
+                # the layout's lines and block length: row-wise R x C, column-wise C x R
+                ln, lg = (R, C) if layout == 0 else (C, R)
+                lines.append(ln)
+                lengths.append(lg)
+            # a: M x K, b: N x K, C = a b^T has the GEMM's output shape
+            assert lengths[0] == lengths[1], (recipe, gemm)
+            assert tuple(lines) == out_shape[gemm], (recipe, gemm)
+            assert seeds == {77}
+    # the reduction dimensions: in, out, tokens
+    for gemm, k in ((F.GEMM_FWD_Y, I), (F.GEMM_BWD_DX, O), (F.GEMM_BWD_DW, T)):
+        _, layout, tensor = F.ufp4_recipe_config(0, gemm, F.OPERAND_A)
+        R, C = shape[tensor]
+        assert (C if layout == 0 else R) == k
+    for bad in ((3, 0, 0), (-1, 0, 0), (0, 3, 0), (0, 0, 2)):
+        with pytest.raises(F.Ufp4Error):
+            F.ufp4_recipe_config(*bad)

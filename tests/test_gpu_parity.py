@@ -383,6 +383,45 @@ def test_gemm_degenerate_shapes(env):
     assert bool((c == 0).all())
 
 
+@pytest.mark.parametrize("recipe", [0, 1, 2])
+def test_training_gemms_under_recipes(env, recipe):
+    # each operand of fwd_y, bwd_dx and bwd_dw quantized on the GPU with the
+    # configuration and layout its recipe preset gives (bit-exact against the
+    # oracle with the same configuration), then multiplied by ufp4_gemm_nt
+    # (within the fp32 accumulation bound of the float64 product of the
+    # oracle's dequantized operands)
+    torch, F, orc = env
+    T, I, O = 256, 192, 160
+    tens = {F.TENSOR_X: synth.activation(T, I, seed=11), F.TENSOR_W: synth.weight(O, I, seed=12),
+            F.TENSOR_DY: synth.output_grad(T, O, seed=13)}
+    for gemm in (F.GEMM_FWD_Y, F.GEMM_BWD_DX, F.GEMM_BWD_DW):
+        say(f"[recipe] recipe={recipe} gemm={gemm}")
+        qs, oqs, dims = [], [], []
+        for operand in (F.OPERAND_A, F.OPERAND_B):
+            fc, layout, tensor = F.ufp4_recipe_config(recipe, gemm, operand, rht_seed=5, sr_seed=9)
+            oc = orc.config(fc.grid, fc.rounding, fc.scaling, fc.rht, fc.rht_seed, fc.sr_seed)
+            xb = tens[tensor]
+            row, col = gpu_rowcol(env, xb, fc)
+            q = row if layout == ROW else col
+            oq = orc.quantize(xb, oc, layout)
+            np.testing.assert_array_equal(q.codes.cpu().numpy(), oq[0])
+            np.testing.assert_array_equal(q.scales.cpu().numpy(), oq[1])
+            assert q.tensor_scale.cpu().numpy()[0] == oq[2][0]
+            R, C = xb.shape
+            qs.append(q)
+            oqs.append(oq)
+            dims.append((R, C) if layout == ROW else (C, R))
+        (M, K), (N, Kb) = dims
+        assert K == Kb
+        ref, mag = orc.gemm_nt_reference(oqs[0], oqs[1], oc, M, N, K)
+        c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        F.ufp4_gemm_nt(fc, qs[0], qs[1], M, N, K, c)
+        torch.cuda.synchronize()
+        err = np.abs(c.cpu().numpy().astype(np.float64) - ref)
+        bound = (K + 4) * 2.0 ** -24 * mag + 1e-30
+        assert (err <= bound).all(), f"max err/bound {float((err / bound).max()):.3g}"
+
+
 # -------------------------------------------------------------- single pass
 @pytest.mark.parametrize("stride", [2, 3, 7])
 @pytest.mark.parametrize("rounding", [RTNE, SR])
