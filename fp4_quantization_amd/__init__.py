@@ -25,7 +25,7 @@ __all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "GRID_E2M1C", "ROUND_RTNE", "R
            "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol",
            "block_len", "ufp4_recipe_config", "RECIPE_UFP4", "RECIPE_UFP4_INT4", "RECIPE_NVFP4",
            "GEMM_FWD_Y", "GEMM_BWD_DX", "GEMM_BWD_DW", "OPERAND_A", "OPERAND_B", "TENSOR_X", "TENSOR_W",
-           "TENSOR_DY"]
+           "TENSOR_DY", "ufp4_f32_to_bf16"]
 
 
 def config(grid: int = GRID_E1M2, rounding: int = ROUND_RTNE, scaling: int = SCALE_NV16,
@@ -238,3 +238,14 @@ def ufp4_recipe_config(recipe: int, gemm: int, operand: int, rht_seed: int = 0, 
                                                        int(sr_seed), ctypes.byref(cfg), ctypes.byref(layout),
                                                        ctypes.byref(tensor)))
     return cfg, layout.value, tensor.value
+
+
+def ufp4_f32_to_bf16(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 (as int16 bit patterns) of a contiguous float32 device tensor,
+    rounded to nearest even by the library's kernel."""
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 tensor")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.int16, device=x.device)
+    check("ufp4_f32_to_bf16", lib.ufp4_f32_to_bf16(_ptr(x), x.numel(), _ptr(out), _stream(stream)))
+    return out

@@ -31,7 +31,7 @@ EXPORTED = ["ufp4_status_string", "ufp4_workspace_size", "ufp4_workspace_init",
             "ufp4_quantize_grouped", "ufp4_dequantize", "ufp4_stats", "ufp4_round_f32",
             "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol", "ufp4_set_schedule",
             "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "ufp4_gemm_nt",
-            "ufp4_recipe_config"]
+            "ufp4_recipe_config", "ufp4_f32_to_bf16"]
 
 
 class Ufp4Error(RuntimeError):
@@ -107,6 +107,8 @@ def _load():
     L.ufp4_amax_tiles.argtypes = [i64, i64]
     L.ufp4_quantize_delayed.restype = ctypes.c_int
     L.ufp4_quantize_delayed.argtypes = [P, i64, i64, i64, cfgp, P, i32, P, ufp4_qtensor, ufp4_qtensor, P]
+    L.ufp4_f32_to_bf16.restype = ctypes.c_int
+    L.ufp4_f32_to_bf16.argtypes = [P, i64, P, P]
     L.ufp4_recipe_config.restype = ctypes.c_int
     L.ufp4_recipe_config.argtypes = [i32, i32, i32, u64, u64, cfgp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ufp4_schedule_of.restype = ctypes.c_int

@@ -543,6 +543,12 @@ int ufp4_recipe_config(int32_t recipe, int32_t gemm, int32_t operand, uint64_t r
   return UFP4_OK;
 }
 
+int ufp4_f32_to_bf16(const float* in_dev, int64_t n, uint16_t* out_dev, ufp4_stream_t stream) {
+  if (n < 0 || (n > 0 && (!in_dev || !out_dev))) return UFP4_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)in_dev % 4 || (uintptr_t)out_dev % 2) return UFP4_ERR_ALIGNMENT;
+  return launch_to_bf16(in_dev, n, out_dev, (hipStream_t)stream) == hipSuccess ? UFP4_OK : UFP4_ERR_HIP;
+}
+
 int ufp4_rht_signs(uint64_t rht_seed, int8_t signs_host[16]) {
   if (!signs_host) return UFP4_ERR_INVALID_ARGUMENT;
   const uint32_t mask = rht_sign_mask(rht_seed);

@@ -128,5 +128,6 @@ struct GemmParams {
   int32_t grid;
 };
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+hipError_t launch_to_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s);
 
 }  // namespace ufp4

@@ -1,4 +1,5 @@
-// ufp4_misc.hip -- dequantization, statistics and the unit-scale rounding hook
+// ufp4_misc.hip -- dequantization, statistics, the unit-scale rounding hook
+// and the fp32 -> bf16 conversion between the layers of a quantized chain
 // (gfx950).  None of these is on the quantization hot path.
 #include "ufp4_internal.hpp"
 
@@ -200,6 +201,40 @@ hipError_t launch_round(const float* y, int64_t n, int32_t grid, int32_t roundin
     case kGridE2M1C: launch_round_grid<kGridE2M1C>(y, n, sr, k0, k1, codes, blocks, s); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fp32 -> bf16
+// Round to nearest, ties to even, on the bit pattern; NaN stays a quiet NaN
+// with its sign.  Four values per thread (16-byte load, 8-byte store) when
+// both pointers allow it, one otherwise.
+__global__ __launch_bounds__(256) void ufp4_to_bf16_kernel(const float* in, int64_t n, uint16_t* out, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  auto rne = [](uint32_t u) -> uint32_t {
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  };
+  if (vec) {
+    const int64_t n4 = n / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+      const uint4 u = reinterpret_cast<const uint4*>(in)[i];
+      reinterpret_cast<uint2*>(out)[i] = make_uint2(rne(u.x) | (rne(u.y) << 16), rne(u.z) | (rne(u.w) << 16));
+    }
+    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+      out[i] = (uint16_t)rne(__float_as_uint(in[i]));
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+      out[i] = (uint16_t)rne(__float_as_uint(in[i]));
+  }
+}
+
+hipError_t launch_to_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int vec = ((uintptr_t)in % 16 == 0 && (uintptr_t)out % 8 == 0) ? 1 : 0;
+  int64_t blocks = ((vec ? n / 4 : n) + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(ufp4_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, in, n, out, vec);
   return hipGetLastError();
 }
 

@@ -320,6 +320,15 @@ int ufp4_recipe_config(int32_t recipe, int32_t gemm, int32_t operand, uint64_t r
 
 /* --- diagnostic hooks (not on the hot path) ------------------------------ */
 
+/* out_dev[i] = in_dev[i] rounded to bf16 (nearest, ties to even; NaN stays a
+ * quiet NaN): the conversion between the layers of a chain of quantized
+ * GEMMs, whose fp32 outputs feed the next layer's bf16 quantizer (the
+ * compounding of the GEMM gain through layers, "Shrinkage Bias: The Hidden
+ * Geometric Trap in FP4 Training" (zhichai.net), "Key points").  Device
+ * pointers, in_dev 4-byte and out_dev 2-byte aligned (UFP4_ERR_ALIGNMENT);
+ * n < 0 gives UFP4_ERR_INVALID_ARGUMENT. */
+int ufp4_f32_to_bf16(const float* in_dev, int64_t n, uint16_t* out_dev, ufp4_stream_t stream);
+
 /* codes_dev[i] = 4-bit code (one per byte) of y_dev[i] rounded at unit scale
  * onto `grid`, with the stochastic-rounding word of index i in stream 0.
  * +-inf saturates to +-Qmax; NaN gives code 0. */

@@ -309,3 +309,48 @@ def stats(x_bf16, layout: int, cfg: Config, codes, scales, tensor_scale) -> dict
     if rc:
         raise ValueError(f"orc_compute_stats failed ({rc})")
     return st.as_dict()
+
+
+def _f32_to_bf16_rne(y: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest, ties to even (finite input)."""
+    u = np.ascontiguousarray(y, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def shrinkage_chain(h0_bf16: np.ndarray, weights_bf16, cfg: Config) -> dict:
+    """Compounding of the quantized-GEMM gain through a chain of linear layers
+    ("Shrinkage Bias: The Hidden Geometric Trap in FP4 Training" (zhichai.net),
+    "Key points", compounding decay: a quantized operand is a scaled copy plus
+    an orthogonal residual, A_hat = alpha_A A + R_A, a GEMM's output is scaled
+    by eta ~ alpha_A alpha_B, and the gains multiply over layers).
+
+    Layer k: y_k = A_hat B_hat^T, the float64 product of the dequantized
+    row-wise layouts of its input h_{k-1} [T][D] and weight W_k [D'][D] (the
+    fwd_y GEMM; both quantized with cfg and one sign vector); its gain
+    eta_k = <y_k, y*_k> / <y*_k, y*_k> against the exact product
+    y*_k = h_{k-1} W_k^T of the same bf16 operands; alpha of both operands as
+    ufp4 statistics define it; the next input h_k = bf16(fp32(y_k)) (round to
+    nearest even twice, as a GEMM with an fp32 result feeding a bf16 layer).
+    The chain's gain G_k = <h_k, x*_k> / <x*_k, x*_k> is measured against the
+    unquantized chain x*_k = x*_{k-1} W_k^T, x*_0 = h_0, in float64.
+    Returns lists eta, alpha_a, alpha_b, gain (one entry per layer) and the
+    last input."""
+    h = np.ascontiguousarray(h0_bf16, dtype=np.uint16)
+    f64 = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+    xs = f64(h)
+    out = {"eta": [], "alpha_a": [], "alpha_b": [], "gain": []}
+    for w in weights_bf16:
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        T, D = h.shape
+        N = w.shape[0]
+        qa, qb = quantize(h, cfg, LAYOUT_ROW), quantize(w, cfg, LAYOUT_ROW)
+        out["alpha_a"].append(stats(h, LAYOUT_ROW, cfg, *qa)["alpha"])
+        out["alpha_b"].append(stats(w, LAYOUT_ROW, cfg, *qb)["alpha"])
+        y, _ = gemm_nt_reference(qa, qb, cfg, T, N, D)
+        ye = f64(h) @ f64(w).T
+        out["eta"].append(float(np.sum(y * ye) / np.sum(ye * ye)))
+        h = _f32_to_bf16_rne(y.astype(np.float32))
+        xs = xs @ f64(w).T
+        out["gain"].append(float(np.sum(f64(h) * xs) / np.sum(xs * xs)))
+    out["last_input"] = h
+    return out

@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["f32_to_bf16", "bf16_to_f32", "activation", "weight", "output_grad",
-           "moe_counts", "moe_activation", "tiny", "all_bf16_patterns", "Workload",
+           "moe_counts", "moe_activation", "orthogonal", "tiny", "all_bf16_patterns", "Workload",
            "workload", "sha256"]
 
 
@@ -144,6 +144,15 @@ def moe_activation(tokens: int, hidden: int, experts: int, top_k: int, seed: int
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     x = activation(int(offsets[-1]), hidden, seed + 1000)
     return x, offsets
+
+
+def orthogonal(n: int, seed: int) -> np.ndarray:
+    """A seeded random orthogonal n x n matrix (Q of the QR factorisation of a
+    standard normal matrix, column signs fixed by R's diagonal) as bf16
+    patterns: weights under which a chain of layers keeps its energy."""
+    g = _rng(seed).standard_normal((n, n))
+    q, r = np.linalg.qr(g)
+    return f32_to_bf16((q * np.sign(np.diag(r))).astype(np.float32))
 
 
 def all_bf16_patterns() -> np.ndarray:

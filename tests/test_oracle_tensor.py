@@ -463,3 +463,74 @@ def test_training_gemms_under_recipes_approximate_exact_products(orc):
             assert rel[recipe, g] < 0.2, (recipe, g, rel[recipe, g])
     for g in range(3):
         assert rel["ufp4", g] < rel["nvfp4", g], rel
+
+
+def _grid_input_and_block_permutations(T, D, layers, seed):
+    """A bf16 input whose 16-blocks are E1M2 grid values k * 7/16 with a
+    +-3.0625 in every block (so its tensor scale is 2^-9 and every block scale
+    448: quantization is exact), and weights that permute and negate
+    entries inside each 16-block (one +-1 per row).  Returns the integer
+    pattern k and the permutations for an independent expectation."""
+    rng = np.random.default_rng(seed)
+    k = rng.integers(-7, 8, size=(T, D))
+    k[:, ::16] = 7 * np.where(rng.random((T, D // 16)) < 0.5, -1, 1)
+    h = synth.f32_to_bf16((k * 0.4375).astype(np.float32))
+    Ws, perms = [], []
+    for _ in range(layers):
+        W = np.zeros((D, D), np.float32)
+        src, sgn = np.zeros(D, np.int64), np.zeros(D, np.int64)
+        for b in range(D // 16):
+            p = rng.permutation(16)
+            s = np.where(rng.random(16) < 0.5, -1, 1)
+            W[16 * b + np.arange(16), 16 * b + p] = s
+            src[16 * b:16 * b + 16], sgn[16 * b:16 * b + 16] = 16 * b + p, s
+        Ws.append(synth.f32_to_bf16(W))
+        perms.append((src, sgn))
+    return k, h, Ws, perms
+
+
+@pytest.mark.parametrize("grid", [E1M2, INT4])
+def test_shrinkage_chain_exact_case(orc, grid):
+    # Grid-valued input, RHT off, signed permutation weights: the input
+    # quantizes exactly and every layer only moves and negates values, so the
+    # chain reproduces the permuted input bit for bit, its gain is exactly 1,
+    # alpha_A is exactly 1 and eta differs from 1 only by the weight's fp32
+    # tensor scale (1/1568 is not a binary fraction): |eta - 1| <= 2^-23.  A
+    # transposed weight, a wrong layout or a wrong gain formula fails this.
+    T, D, L = 64, 64, 4
+    k, h, Ws, perms = _grid_input_and_block_permutations(T, D, L, seed=5)
+    r = orc.shrinkage_chain(h, Ws, orc.config(grid, RTNE, NV16, 0, 0, 0))
+    expect = k.copy()
+    for src, sgn in perms:
+        expect = expect[:, src] * sgn  # y = h W^T: y[:, i] = sgn[i] h[:, src[i]]
+    np.testing.assert_array_equal(synth.bf16_to_f32(r["last_input"]), (expect * 0.4375).astype(np.float32))
+    assert r["gain"] == [1.0] * L and r["alpha_a"] == [1.0] * L
+    assert all(abs(e - 1.0) <= 2.0 ** -23 for e in r["eta"]), r["eta"]
+    assert all(abs(a - 1.0) <= 2.0 ** -23 for a in r["alpha_b"]), r["alpha_b"]
+
+
+def test_shrinkage_chain_compounds(orc):
+    # The compounding decay the pages describe ("Shrinkage Bias: The Hidden
+    # Geometric Trap in FP4 Training" (zhichai.net), "Key points"): under
+    # E2M1 every layer's gain is below 1 on average and the chain's gain
+    # follows the product of the layer gains; the uniform E1M2 grid does not
+    # shrink.  Orthogonal weights keep the chain's energy, so the chain gain
+    # can be compared with prod eta without the noise a random product of
+    # matrices amplifies.  prod eta and exp(-sum delta) agree to second
+    # order: |ln prod eta + sum delta| <= sum delta^2.
+    T, D, L = 512, 256, 16
+    h0 = synth.activation(T, D, seed=21)
+    Ws = [synth.orthogonal(D, seed=100 + i) for i in range(L)]
+    prod = {}
+    for name, grid in (("e1m2", E1M2), ("e2m1", E2M1)):
+        r = orc.shrinkage_chain(h0, Ws, orc.config(grid, RTNE, NV16, 0, 3, 0))
+        eta = np.array(r["eta"])
+        prod[name] = float(np.prod(eta))
+        d = 1.0 - eta
+        assert abs(np.log(prod[name]) + d.sum()) <= (d * d).sum() + 1e-12
+        assert abs(r["gain"][-1] / prod[name] - 1.0) < 0.01, (name, r["gain"][-1], prod[name])
+        if name == "e2m1":
+            assert eta.mean() < 0.996 and (eta < 1.0).mean() > 0.9, eta
+        else:
+            assert abs(eta.mean() - 1.0) < 0.002, eta
+    assert prod["e2m1"] < 0.93 and prod["e2m1"] < prod["e1m2"] - 0.05, prod
