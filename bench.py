@@ -2,7 +2,7 @@
 activation on one MI355X, reported as HBM GB/s (algorithmic bytes / time).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--warm] [--copy]
-                [--schedule auto|two-pass|single-pass]
+                [--schedule auto|two-pass|single-pass] [--no-extra]
 
 A step is one ufp4_quantize_rowcol call (every stage of the hot path: load,
 random signs, 16-point Walsh-Hadamard transform, tensor and block maxima,
@@ -26,6 +26,14 @@ around that kernel alone, over calls that rotate through the buffer sets.
 
 The oracle leg (cpu_baseline) times the single-threaded CPU oracle on the same
 tensor (row-wise and column-wise), a reported baseline only.
+
+Reported beside the headline, under "extra" (never as the value): the RHT-off
+call, the other schedule, delayed scaling, the consumer GEMM, a streaming
+copy of 512 MiB on the same box, the weight workload's shrinkage sweep (SQNR,
+mean signed error in grid units and gain alpha per grid, RHT on and off),
+the output-gradient workload (stochastic rounding, row+col) and MoE workload
+(grouped, row+col) call times, and the compounding of the GEMM gain through
+16 quantized layers.
 """
 from __future__ import annotations
 
@@ -244,6 +252,98 @@ def copy_bench(torch, args):
                       "copy_gbps": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def extra_legs(torch, F, synth, np, dev, stream, steps):
+    """Measurements reported beside the headline: a streaming-copy reference
+    bandwidth; the weight workload's shrinkage sweep (SQNR, mean signed error
+    and gain alpha per grid, RHT on and off); the output-gradient workload
+    (SR, row+col) and the MoE workload (grouped, row+col) call times; and the
+    compounding of the GEMM gain through a chain of quantized layers."""
+    out = {}
+    # streaming copy of 512 MiB on the same box (read + write)
+    n = 512 * 1024 * 1024 // 4
+    a, b = torch.ones(n, dtype=torch.float32, device=dev), torch.empty(n, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        b.copy_(a)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(20):
+        b.copy_(a)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    out["copy_gbps"] = round(2 * n * 4 / (s0.elapsed_time(s1) / 20 * 1e-3) / 1e9, 1)
+    del a, b
+    # weight W 2048 x 8192, Student-t(4) tails: the shrinkage sweep per grid
+    wb = synth.weight(2048, 8192, seed=2)
+    w = torch.from_numpy(wb.view(np.int16)).to(dev)
+    ws = F.Workspace(2048, 8192, device=dev)
+    q = F.alloc_layout(2048, 8192, F.SCALE_NV16, device=dev)
+    sweep = {}
+    for gname, g in (("e1m2", F.GRID_E1M2), ("int4", F.GRID_INT4), ("e2m1", F.GRID_E2M1)):
+        for rht in (0, 1):
+            c = F.config(g, F.ROUND_RTNE, F.SCALE_NV16, rht=rht, rht_seed=2)
+            F.ufp4_quantize(w, c, q, ws, stream)
+            st = F.ufp4_stats(w, 0, c, q, ws, stream)
+            sweep[f"{gname}_rht{rht}"] = {"sqnr_db": round(st["sqnr_db"], 3),
+                                          "mean_signed_err_grid": round(st["mean_signed_err_grid"], 5),
+                                          "alpha": round(st["alpha"], 6)}
+    out["weight_2048x8192_sweep"] = sweep
+    del w, ws, q
+
+    def timed(fn, k):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    # output gradient dY 16384 x 4096, Laplace + outliers: RHT + E1M2 + SR, row+col
+    R, C = 16384, 4096
+    g = torch.from_numpy(synth.output_grad(R, C, seed=3).view(np.int16)).to(dev)
+    c = F.config(F.GRID_E1M2, F.ROUND_STOCHASTIC, F.SCALE_NV16, rht=1, rht_seed=3, sr_seed=3)
+    row, col, ws = (F.alloc_layout(R, C, F.SCALE_NV16, device=dev), F.alloc_layout(C, R, F.SCALE_NV16, device=dev),
+                    F.Workspace(R, C, device=dev))
+    ms = timed(lambda: F.ufp4_quantize_rowcol(g, c, row, col, ws, stream), max(10, steps // 10))
+    out["output_grad_16384x4096_sr_ms"] = round(ms, 6)
+    out["output_grad_16384x4096_sr_gbps"] = round((2 * R * C + R * C + 2 * R * C // 16 + 8) / (ms * 1e-3) / 1e9, 1)
+    del g, row, col, ws
+    # MoE 65536 x 4096 in 64 ragged expert segments: grouped RHT + E1M2, row+col
+    xm, off = synth.moe_activation(8192, 4096, 64, 8, seed=4)
+    Rm = xm.shape[0]
+    coff = F.ufp4_grouped_col_offsets(off, 16)
+    Rp = int(coff[-1])
+    x = torch.from_numpy(xm.view(np.int16)).to(dev)
+    offd = torch.from_numpy(off.astype(np.int64)).to(dev)
+    c = F.config(F.GRID_E1M2, F.ROUND_RTNE, F.SCALE_NV16, rht=1, rht_seed=4)
+    row = F.alloc_layout(Rm, 4096, F.SCALE_NV16, n_tensor_scales=64, device=dev)
+    col = F.alloc_layout(4096, Rp, F.SCALE_NV16, n_tensor_scales=64, device=dev)
+    ws = F.Workspace(Rm, 4096, 64, device=dev)
+    ms = timed(lambda: F.ufp4_quantize_grouped(x, offd, Rp, c, row, col, ws, stream), max(10, steps // 10))
+    moe_bytes = 2 * Rm * 4096 + Rm * 4096 // 2 + Rm * 4096 // 16 + 4096 * Rp // 2 + 4096 * Rp // 16 + 2 * 64 * 4
+    out["moe_65536x4096_grouped_ms"] = round(ms, 6)
+    out["moe_65536x4096_grouped_gbps"] = round(moe_bytes / (ms * 1e-3) / 1e9, 1)
+    del x, row, col, ws
+    # compounding of the GEMM gain: 16 layers, 8192 tokens x 1024, orthogonal weights
+    import fp4_quantization_amd.shrinkage as S
+    T, D, L = 8192, 1024, 16
+    h0 = torch.from_numpy(synth.activation(T, D, seed=21).view(np.int16)).to(dev)
+    Ws = [torch.from_numpy(synth.orthogonal(D, seed=100 + i).view(np.int16)).to(dev) for i in range(L)]
+    chain = {}
+    for gname, gg in (("e1m2", F.GRID_E1M2), ("e2m1", F.GRID_E2M1)):
+        for rht in (0, 1):
+            r = S.shrinkage_chain(h0, Ws, F.config(gg, F.ROUND_RTNE, F.SCALE_NV16, rht=rht, rht_seed=5), stream)
+            eta = np.array(r["eta"])
+            chain[f"{gname}_rht{rht}"] = {"mean_eta": round(float(eta.mean()), 6),
+                                          "prod_eta": round(float(eta.prod()), 5),
+                                          "exp_minus_sum_delta": round(float(np.exp(-(1.0 - eta).sum())), 5),
+                                          "chain_gain": round(r["gain"][-1], 5)}
+    out["shrinkage_chain_8192x1024_16_layers"] = chain
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +354,9 @@ def main():
                     help="also time repeated calls on one buffer set (input cache-resident)")
     ap.add_argument("--schedule", choices=("auto", "two-pass", "single-pass"), default="auto",
                     help="schedule of the timed calls (the other one is timed beside it)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the legs beyond the headline workload's own (the profiler runs use it: those "
+                         "legs launch the same kernels on other tensors)")
     ap.add_argument("--copy", action="store_true",
                     help="time a plain device copy of 512 MiB instead (bandwidth and counter calibration)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -265,9 +368,9 @@ def main():
         d = args.summarize_counters
         summarize_counters(*d, commands=[
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[0]} -o run -- "
-            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[1]} -o run -- "
-            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[2]} -o run -- "
             "python3 bench.py --copy --steps 5 --warmup 2",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[3]} -o run -- "
@@ -431,12 +534,16 @@ def main():
         line["extra"].update(two)
     line["extra"]["gemm_8192x8192x2048_ms"] = round(ms_gemm, 6)
     line["extra"]["gemm_tflops"] = round(gemm_tflops, 1)
-    line["extra"]["gemm_frac_of_bf16_mfma_peak"] = round(gemm_tflops / 2500.0, 4)
+    line["extra"]["gemm_frac_of_fp16_mfma_peak"] = round(gemm_tflops / 2500.0, 4)
     line["extra"]["delayed_scaling_ms"] = round(ms_delayed, 6)
     line["extra"]["delayed_scaling_gbps"] = round(nbytes / (ms_delayed * 1e-3) / 1e9, 2)
     if ms_warm is not None:
         line["extra"]["warm_same_buffer_ms"] = round(ms_warm, 6)
         line["extra"]["warm_same_buffer_gbps"] = round(nbytes / (ms_warm * 1e-3) / 1e9, 2)
+    if not args.no_extra:
+        line["extra"].update(extra_legs(torch, F, synth, np, dev, stream, args.steps))
+        line["extra"]["call_frac_of_copy"] = round(gbps / line["extra"]["copy_gbps"], 4)
+        line["extra"]["quant_kernel_frac_of_copy"] = round(quant_gbps / line["extra"]["copy_gbps"], 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(xb)
     print(json.dumps(line), flush=True)

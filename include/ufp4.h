@@ -211,7 +211,7 @@ int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_
  * (zhichai.net), "Key points": the fix quantizes the operands of all three).
  * Operands quantized with the same RHT signs give the product of the
  * untransformed matrices (the transform is orthonormal).  Each dequantized
- * value is exact in bf16; the products are summed on the bf16 MFMA in fp32,
+ * value is exact in fp16; the products are summed on the fp16 MFMA in fp32,
  * so c differs from the exact sum only by fp32 accumulation order.
  * cfg: grid of both operands; NV16 only.  K % 32 == 0 (UFP4_ERR_SHAPE);
  * ldc >= N; codes 16-byte aligned.  M or N of 0 writes nothing; K of 0
