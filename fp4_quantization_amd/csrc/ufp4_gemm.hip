@@ -16,6 +16,11 @@
 // exact), and applies the two tensor scales in the epilogue.  Results differ
 // from an exact sum only by the fp32 accumulation order.
 //
+// Tiles are 256 x 256 per workgroup of 8 waves, K steps of 32, with two LDS
+// buffers: a step multiplies from one while the next step's codes (requested
+// four steps ahead) are expanded in registers between the multiplies and
+// stored into the other, and ends in one barrier.
+//
 // The expansion is byte arithmetic: every grid value's fp16 encoding has a
 // zero low byte, so one byte permute looks the high bytes of four codes up in
 // an 8-entry table, an OR adds their signs, a second permute interleaves the
@@ -32,7 +37,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t g32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t g32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGemmM = 128, kGemmN = 128, kGemmK = 32;
+constexpr int kGemmM = 256, kGemmN = 256, kGemmK = 32;
 constexpr int kGemmLd = kGemmK + 8;  // fp16 per LDS row: 80 bytes, 16-byte aligned rows
 
 // High bytes of the fp16 encodings of the grid magnitudes by magnitude
@@ -73,31 +78,41 @@ __device__ __forceinline__ void expand8(uint32_t word, f16x2 d2, uint32_t out[4]
 }
 
 // One 16-element block: 8 code bytes and its E4M3 scale byte, to 16 fp16
-// values at dst (16-byte aligned).
+// values (eight words, element 2i in the low half of word i).
 template <int GRID>
-__device__ __forceinline__ void dequant16(g32x2 codes, uint32_t sbyte, _Float16* dst) {
+__device__ __forceinline__ void expand16(g32x2 codes, uint32_t sbyte, uint32_t o[8]) {
   const _Float16 d = (_Float16)e4m3_decode_pos(sbyte & 0x7Fu);  // exact: E4M3 values are fp16 values
   const f16x2 d2 = {d, d};
-  uint32_t o[8];
   expand8<GRID>(codes.x, d2, o);
   expand8<GRID>(codes.y, d2, o + 4);
+}
+
+// The 16 fp16 values of a block to dst (16-byte aligned).
+__device__ __forceinline__ void store16(const uint32_t o[8], _Float16* dst) {
   g32x4* p = reinterpret_cast<g32x4*>(dst);
   p[0] = g32x4{o[0], o[1], o[2], o[3]};
   p[1] = g32x4{o[4], o[5], o[6], o[7]};
 }
 
-// Grid: (ceil(N/128), ceil(M/128)); 256 threads.  Wave w computes the 64 x 64
-// sub-tile at rows 64 (w / 2), columns 64 (w % 2), as 2 x 2 MFMA tiles of
-// 32 x 32.  Per K step of 32 each thread expands one block of A (row t / 2,
-// block t % 2 of the step) and one of B; the next step's codes are loaded
-// while the current step multiplies.
+// Grid: (ceil(N/256), ceil(M/256)); 512 threads (8 waves).  Wave w computes
+// the 64 x 128 sub-tile at rows 64 (w / 2), columns 128 (w % 2), as 2 x 4
+// MFMA tiles of 32 x 32.  Per K step of 32 each thread expands one block of A
+// (row t / 2, block t % 2 of the step) and one of B.  The expanded tiles are
+// double-buffered in LDS: a step multiplies from one buffer while the next
+// step's codes, loaded from memory during the multiplies, are expanded into
+// the other, so each step ends in one barrier.  At this tile size the
+// expansion costs about half the MFMA time of a step per wave, and the two
+// waves of a SIMD overlap one's expansion with the other's multiplies.
+constexpr int kGemmThreads = 512;
+constexpr int kPrefetch = 4;  // steps between a code request and its use (even: buffer = step parity)
+
 template <int GRID>
-__global__ __launch_bounds__(kThreads) void ufp4_gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[kGemmM][kGemmLd];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[kGemmN][kGemmLd];
+__global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][kGemmM][kGemmLd];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kGemmN][kGemmLd];
   const int64_t m0 = (int64_t)blockIdx.y * kGemmM, n0 = (int64_t)blockIdx.x * kGemmN;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
   const int lr = t >> 1, lb = t & 1;
   const int64_t am = m0 + lr, bn = n0 + lr;
   const bool a_ok = am < p.M, b_ok = bn < p.N;
@@ -107,52 +122,96 @@ __global__ __launch_bounds__(kThreads) void ufp4_gemm_kernel(GemmParams p) {
   const uint8_t* as = p.a_scales + (a_ok ? am : 0) * ks + lb;
   const uint8_t* bc = p.b_codes + (b_ok ? bn : 0) * kc + 8 * lb;
   const uint8_t* bs = p.b_scales + (b_ok ? bn : 0) * ks + lb;
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  g32x2 na = {0u, 0u}, nb = {0u, 0u};
-  uint32_t nsa = 0u, nsb = 0u;
-  if (p.K > 0) {
-    na = *reinterpret_cast<const g32x2*>(ac);
-    nb = *reinterpret_cast<const g32x2*>(bc);
-    nsa = as[0];
-    nsb = bs[0];
-  }
-  for (int64_t k0 = 0; k0 < p.K; k0 += kGemmK) {
-    const g32x2 ca = a_ok ? na : g32x2{0u, 0u}, cb = b_ok ? nb : g32x2{0u, 0u};
-    const uint32_t sa = nsa, sb = nsb;
-    if (k0 + kGemmK < p.K) {
-      const int64_t k1 = k0 + kGemmK;
-      na = *reinterpret_cast<const g32x2*>(ac + k1 / 2);
-      nb = *reinterpret_cast<const g32x2*>(bc + k1 / 2);
-      nsa = as[k1 / 16];
-      nsb = bs[k1 / 16];
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  // Codes and scales of step k + kPrefetch are requested at step k, so a
+  // request has kPrefetch steps of multiplies to arrive in.  The ring index
+  // is static: the loop runs kPrefetch steps per iteration.
+  g32x2 ra[kPrefetch], rb[kPrefetch];
+  uint32_t rsa[kPrefetch], rsb[kPrefetch];
+  const int64_t nsteps = p.K / kGemmK;
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u) {
+    ra[u] = rb[u] = g32x2{0u, 0u};
+    rsa[u] = rsb[u] = 0u;
+    if (u < nsteps) {
+      ra[u] = *reinterpret_cast<const g32x2*>(ac + (int64_t)u * (kGemmK / 2));
+      rb[u] = *reinterpret_cast<const g32x2*>(bc + (int64_t)u * (kGemmK / 2));
+      rsa[u] = as[u * (kGemmK / 16)];
+      rsb[u] = bs[u * (kGemmK / 16)];
     }
-    __syncthreads();  // the previous step's fragments have been read
-    dequant16<GRID>(ca, sa, &As[lr][16 * lb]);
-    dequant16<GRID>(cb, sb, &Bs[lr][16 * lb]);
-    __syncthreads();
+  }
+  if (nsteps > 0) {
+    uint32_t ea[8], eb[8];
+    expand16<GRID>(a_ok ? ra[0] : g32x2{0u, 0u}, rsa[0], ea);
+    expand16<GRID>(b_ok ? rb[0] : g32x2{0u, 0u}, rsb[0], eb);
+    store16(ea, &As[0][lr][16 * lb]);
+    store16(eb, &Bs[0][lr][16 * lb]);
+  }
+  __syncthreads();
+  for (int64_t s0 = 0; s0 < nsteps; s0 += kPrefetch) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      f16x8 fa[2], fb[2];
+    for (int u = 0; u < kPrefetch; ++u) {
+      const int64_t st = s0 + u;  // this step; its tiles are in buffer u & 1
+      if (st < nsteps) {
+        const int cur = u & 1;
+        // slot u held this step's codes (already expanded); refill it with
+        // step st + kPrefetch's
+        if (st + kPrefetch < nsteps) {
+          const int64_t k1 = (st + kPrefetch) * kGemmK;
+          ra[u] = *reinterpret_cast<const g32x2*>(ac + k1 / 2);
+          rb[u] = *reinterpret_cast<const g32x2*>(bc + k1 / 2);
+          rsa[u] = as[k1 / 16];
+          rsb[u] = bs[k1 / 16];
+        }
+        f16x8 fa[2][2], fb[2][4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fa[i] = *reinterpret_cast<const f16x8*>(&As[wm + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
-        fb[i] = *reinterpret_cast<const f16x8*>(&Bs[wn + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            fa[kk][i] = *reinterpret_cast<const f16x8*>(&As[cur][wm + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            fb[kk][j] = *reinterpret_cast<const f16x8*>(&Bs[cur][wn + 32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+        }
+        // the next step's codes sit in slot (u + 1) % kPrefetch; they are
+        // expanded in registers while the multiplies run (after the last
+        // step the slot is stale and its expansion goes unread)
+        const int v = (u + 1) % kPrefetch;
+        uint32_t ea[8], eb[8];
+        expand16<GRID>(a_ok ? ra[v] : g32x2{0u, 0u}, rsa[v], ea);
+        expand16<GRID>(b_ok ? rb[v] : g32x2{0u, 0u}, rsb[v], eb);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+        // issue order: the fragment reads, then each multiply followed by a
+        // share of the expansion's arithmetic, so the VALU works while the
+        // matrix unit runs
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+        }
+        // the other buffer was last read before the previous step's barrier
+        store16(ea, &As[cur ^ 1][lr][16 * lb]);
+        store16(eb, &Bs[cur ^ 1][lr][16 * lb]);
+        __syncthreads();
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
   }
   const float s = p.a_ts[0] * p.b_ts[0];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -164,10 +223,10 @@ __global__ __launch_bounds__(kThreads) void ufp4_gemm_kernel(GemmParams p) {
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const dim3 grid((unsigned)((p.N + kGemmN - 1) / kGemmN), (unsigned)((p.M + kGemmM - 1) / kGemmM));
   switch (p.grid) {
-    case kGridE1M2: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridE1M2>, grid, dim3(kThreads), 0, s, p); break;
-    case kGridINT4: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridINT4>, grid, dim3(kThreads), 0, s, p); break;
-    case kGridE2M1: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridE2M1>, grid, dim3(kThreads), 0, s, p); break;
-    case kGridE2M1C: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridE2M1C>, grid, dim3(kThreads), 0, s, p); break;
+    case kGridE1M2: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridE1M2>, grid, dim3(kGemmThreads), 0, s, p); break;
+    case kGridINT4: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridINT4>, grid, dim3(kGemmThreads), 0, s, p); break;
+    case kGridE2M1: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridE2M1>, grid, dim3(kGemmThreads), 0, s, p); break;
+    case kGridE2M1C: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridE2M1C>, grid, dim3(kGemmThreads), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
