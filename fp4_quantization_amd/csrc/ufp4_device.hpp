@@ -32,11 +32,21 @@ struct Ctr4 {
   uint32_t x, y, z, w;
 };
 
+// Full 64-bit product of two 32-bit words in one v_mad_u64_u32 (the plain
+// C++ product compiles to a low and a high multiply: two quarter-rate
+// instructions instead of one).
+__device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t m) {
+  uint64_t r, carry;
+  asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(r), "=s"(carry) : "v"(a), "s"(m));
+  return r;
+}
+
 __device__ __forceinline__ Ctr4 philox10(Ctr4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = c.x * 0xD2511F53u, hi0 = __umulhi(c.x, 0xD2511F53u);
-    const uint32_t lo1 = c.z * 0xCD9E8D57u, hi1 = __umulhi(c.z, 0xCD9E8D57u);
+    const uint64_t p0 = mul_wide(c.x, 0xD2511F53u), p1 = mul_wide(c.z, 0xCD9E8D57u);
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     c = Ctr4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
