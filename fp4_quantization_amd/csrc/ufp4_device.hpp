@@ -47,7 +47,9 @@ __device__ __forceinline__ Ctr4 philox10(Ctr4 c, uint32_t k0, uint32_t k1) {
     const uint64_t p0 = mul_wide(c.x, 0xD2511F53u), p1 = mul_wide(c.z, 0xCD9E8D57u);
     const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
     const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
-    c = Ctr4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    // a ^ b ^ k as one three-input bitwise op (truth table 0x96)
+    c = Ctr4{(uint32_t)__builtin_amdgcn_bitop3_b32(hi1, c.y, k0, 0x96), lo1,
+             (uint32_t)__builtin_amdgcn_bitop3_b32(hi0, c.w, k1, 0x96), lo0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
