@@ -66,9 +66,13 @@ template <int GRID>
 __device__ __forceinline__ void expand8(uint32_t word, f16x2 d2, uint32_t out[4]) {
   if (GRID == kGridINT4) word = signmag8(word);
   const uint32_t lo = f16_hi_lo<GRID>(), hi = f16_hi_hi<GRID>();
-  // high bytes of the even (low-nibble) and odd (high-nibble) elements
-  const uint32_t he = __builtin_amdgcn_perm(hi, lo, word & 0x07070707u) | ((word << 4) & 0x80808080u);
-  const uint32_t ho = __builtin_amdgcn_perm(hi, lo, (word >> 4) & 0x07070707u) | (word & 0x80808080u);
+  // high bytes of the even (low-nibble) and odd (high-nibble) elements; the
+  // sign bits are merged by one three-input bitwise op, a | (b & c)
+  // (truth table 0xF8)
+  const uint32_t he = (uint32_t)__builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(hi, lo, word & 0x07070707u),
+                                                             word << 4, 0x80808080u, 0xF8);
+  const uint32_t ho = (uint32_t)__builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(hi, lo, (word >> 4) & 0x07070707u),
+                                                             word, 0x80808080u, 0xF8);
   // (element 2i, element 2i+1) = (0x00, he.byte i, 0x00, ho.byte i); selector
   // 0x0C gives a zero byte, 0..3 the bytes of he, 4..7 those of ho
   out[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(ho, he, 0x040C000Cu)) * d2);
@@ -81,7 +85,9 @@ __device__ __forceinline__ void expand8(uint32_t word, f16x2 d2, uint32_t out[4]
 // values (eight words, element 2i in the low half of word i).
 template <int GRID>
 __device__ __forceinline__ void expand16(g32x2 codes, uint32_t sbyte, uint32_t o[8]) {
-  const _Float16 d = (_Float16)e4m3_decode_pos(sbyte & 0x7Fu);  // exact: E4M3 values are fp16 values
+  // the hardware OCP E4M3 decode of the (non-negative) scale byte; exact,
+  // and every E4M3 value is an fp16 value
+  const _Float16 d = (_Float16)__builtin_amdgcn_cvt_pk_f32_fp8((int)(sbyte & 0x7Fu), false)[0];
   const f16x2 d2 = {d, d};
   expand8<GRID>(codes.x, d2, o);
   expand8<GRID>(codes.y, d2, o + 4);
