@@ -202,8 +202,14 @@ __device__ __forceinline__ uint32_t round_rtne(float y) {
   } else if (GRID == kGridINT4) {
     k = (uint32_t)__builtin_rintf(fminf(a, 7.0f));
   } else {
-    k = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-        (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    // E2M1: the hardware conversion (OCP E2M1, round to nearest even,
+    // saturating at +-6) writes sign | magnitude index, the layout of these
+    // codes; it matches the nearest-even search on every finite input
+    // except that it keeps the sign of a zero result, so a zero magnitude is
+    // mapped to code 0 here, and NaN is mapped to 0 before the conversion.
+    const uint32_t c =
+        (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, (a == a) ? y : 0.0f, 0.0f, 1.0f, 0) & 15u;
+    return (c & 7u) ? c : 0u;
   }
   k = (a == a) ? k : 0u;
   return k ? make_code<GRID>(k, y) : 0u;
