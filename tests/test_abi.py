@@ -224,3 +224,12 @@ def test_recipe_presets(F):
     for bad in ((3, 0, 0), (-1, 0, 0), (0, 3, 0), (0, 0, 2)):
         with pytest.raises(F.Ufp4Error):
             F.ufp4_recipe_config(*bad)
+
+
+def test_bench_algorithmic_bytes():
+    # bf16 read once (2 B), codes of both layouts (2 x 0.5 B) and E4M3 scales
+    # of both layouts (2 x 1/16 B) per element, plus two fp32 tensor scales
+    import bench
+    assert bench.algorithmic_bytes(8192, 2048) == 52_428_808
+    n = 8192 * 2048
+    assert bench.algorithmic_bytes(8192, 2048) == int(n * (2 + 0.5 + 0.5 + 1 / 16 + 1 / 16)) + 8
