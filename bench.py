@@ -28,7 +28,8 @@ The oracle leg (cpu_baseline) times the single-threaded CPU oracle on the same
 tensor (row-wise and column-wise), a reported baseline only.
 
 Reported beside the headline, under "extra" (never as the value): the RHT-off
-call, the other schedule, delayed scaling, the consumer GEMM, a streaming
+call, the E2M1, INT4 and MX32 variants of the call, the other schedule,
+delayed scaling, the consumer GEMM, a streaming
 copy of 512 MiB on the same box, the weight workload's shrinkage sweep (SQNR,
 mean signed error in grid units and gain alpha per grid, RHT on and off),
 the output-gradient workload (stochastic rounding, row+col) and MoE workload
@@ -250,6 +251,38 @@ def copy_bench(torch, args):
     ms = s.elapsed_time(e) / args.steps
     print(json.dumps({"copy_bytes_per_step": 2 * n * 4, "ms_per_step": round(ms, 6),
                       "copy_gbps": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def variant_legs(torch, F, sets, stream, steps):
+    """Call times of the comparator variants on the headline tensor and its
+    rotating buffer sets: the E2M1 and INT4 grids (NV16) and MX32 scaling
+    (one kernel: no tensor maximum), all with the RHT, row+col."""
+    import ctypes
+    out = {}
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    n = ROWS * COLS
+    for name, grid, scaling in (("e2m1_nv16", F.GRID_E2M1, F.SCALE_NV16), ("int4_nv16", F.GRID_INT4, F.SCALE_NV16),
+                                ("e1m2_mx32", F.GRID_E1M2, F.SCALE_MX32)):
+        cfg = F.config(grid, F.ROUND_RTNE, scaling, rht=1, rht_seed=1)
+        outs = [(x, F.alloc_layout(ROWS, COLS, scaling, device=x.device), F.alloc_layout(COLS, ROWS, scaling, device=x.device),
+                 ws) for x, _, _, ws in sets]
+        fns = []
+        for x, row, col, ws in outs:
+            a = (ctypes.c_void_p(x.data_ptr()), ROWS, COLS, COLS, ctypes.byref(cfg), row.c(), col.c(), ws.ptr, ws.nbytes,
+                 sptr)
+
+            def fn(a=a):
+                rc = F.lib.ufp4_quantize_rowcol(*a)
+                if rc:
+                    raise F.Ufp4Error("ufp4_quantize_rowcol", rc)
+            fns.append(fn)
+        ms, _ = time_graph(torch, fns, steps, 5, stream)
+        B = 32 if scaling == F.SCALE_MX32 else 16
+        nbytes = 2 * n + n + 2 * (n // B) + 8
+        out[f"{name}_rowcol_ms"] = round(ms, 6)
+        out[f"{name}_rowcol_gbps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        del outs, fns
+    return out
 
 
 def extra_legs(torch, F, synth, np, dev, stream, steps):
@@ -541,6 +574,7 @@ def main():
         line["extra"]["warm_same_buffer_ms"] = round(ms_warm, 6)
         line["extra"]["warm_same_buffer_gbps"] = round(nbytes / (ms_warm * 1e-3) / 1e9, 2)
     if not args.no_extra:
+        line["extra"].update(variant_legs(torch, F, sets, stream, args.steps))
         line["extra"].update(extra_legs(torch, F, synth, np, dev, stream, args.steps))
         line["extra"]["call_frac_of_copy"] = round(gbps / line["extra"]["copy_gbps"], 4)
         line["extra"]["quant_kernel_frac_of_copy"] = round(quant_gbps / line["extra"]["copy_gbps"], 4)
