@@ -233,3 +233,14 @@ def test_bench_algorithmic_bytes():
     assert bench.algorithmic_bytes(8192, 2048) == 52_428_808
     n = 8192 * 2048
     assert bench.algorithmic_bytes(8192, 2048) == int(n * (2 + 0.5 + 0.5 + 1 / 16 + 1 / 16)) + 8
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU only: --gpus 2 exits with status 2 and a message, before any
+    # device work
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
