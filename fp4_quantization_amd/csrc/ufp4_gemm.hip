@@ -16,14 +16,15 @@
 // exact), and applies the two tensor scales in the epilogue.  Results differ
 // from an exact sum only by the fp32 accumulation order.
 //
-// Tiles are 256 x 256 per workgroup of 8 waves, K steps of 32, with two LDS
+// Tiles are 256 x 256 per workgroup of 8 waves, K steps of 64, with two LDS
 // buffers: a step multiplies from one while the next step's codes (requested
-// four steps ahead) are expanded in registers between the multiplies and
+// two steps ahead) are expanded in registers between the multiplies and
 // stored into the other, and ends in one barrier.
 //
 // The expansion is byte arithmetic: every grid value's fp16 encoding has a
 // zero low byte, so one byte permute looks the high bytes of four codes up in
-// an 8-entry table, an OR adds their signs, a second permute interleaves the
+// an 8-entry table, a three-input bitwise op adds their signs, a second permute
+// interleaves the
 // zero low bytes, and a packed fp16 multiply applies the block scale.
 #include <hip/hip_runtime.h>
 
@@ -37,8 +38,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t g32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t g32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGemmM = 256, kGemmN = 256, kGemmK = 32;
-constexpr int kGemmLd = kGemmK + 8;  // fp16 per LDS row: 80 bytes, 16-byte aligned rows
+constexpr int kGemmM = 256, kGemmN = 256, kGemmK = 64;
+constexpr int kGemmLd = kGemmK + 8;  // fp16 per LDS row: 144 bytes, 16-byte aligned rows
 
 // High bytes of the fp16 encodings of the grid magnitudes by magnitude
 // index (low word: indices 0..3, high word: 4..7).
@@ -102,15 +103,16 @@ __device__ __forceinline__ void store16(const uint32_t o[8], _Float16* dst) {
 
 // Grid: (ceil(N/256), ceil(M/256)); 512 threads (8 waves).  Wave w computes
 // the 64 x 128 sub-tile at rows 64 (w / 2), columns 128 (w % 2), as 2 x 4
-// MFMA tiles of 32 x 32.  Per K step of 32 each thread expands one block of A
-// (row t / 2, block t % 2 of the step) and one of B.  The expanded tiles are
-// double-buffered in LDS: a step multiplies from one buffer while the next
-// step's codes, loaded from memory during the multiplies, are expanded into
-// the other, so each step ends in one barrier.  At this tile size the
-// expansion costs about half the MFMA time of a step per wave, and the two
-// waves of a SIMD overlap one's expansion with the other's multiplies.
+// MFMA tiles of 32 x 32.  Per K step of 64 each thread expands two adjacent
+// blocks of A (row t / 2, blocks 2 (t % 2) and 2 (t % 2) + 1 of the step: 16
+// code bytes, one load) and two of B.  At the 144-byte row pitch both the
+// fragment reads (consecutive rows) and these stores (two threads per row)
+// fall on distinct LDS banks.  The expanded tiles are double-buffered: a
+// step multiplies from one buffer while the next step's codes (requested
+// kPrefetch steps ahead) are expanded in registers between its multiplies
+// and stored into the other, so each step ends in one barrier.
 constexpr int kGemmThreads = 512;
-constexpr int kPrefetch = 4;  // steps between a code request and its use (even: buffer = step parity)
+constexpr int kPrefetch = 2;  // steps between a code request and its use (even: buffer = step parity)
 
 template <int GRID>
 __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
   const int64_t m0 = (int64_t)blockIdx.y * kGemmM, n0 = (int64_t)blockIdx.x * kGemmN;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
-  const int lr = t >> 1, lb = t & 1;
+  const int lr = t >> 1, lb = 2 * (t & 1);  // row, first of the thread's two blocks
   const int64_t am = m0 + lr, bn = n0 + lr;
   const bool a_ok = am < p.M, b_ok = bn < p.N;
   const int64_t kc = p.K / 2, ks = p.K / 16;
@@ -133,29 +135,36 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  // Codes and scales of step k + kPrefetch are requested at step k, so a
-  // request has kPrefetch steps of multiplies to arrive in.  The ring index
-  // is static: the loop runs kPrefetch steps per iteration.
-  g32x2 ra[kPrefetch], rb[kPrefetch];
-  uint32_t rsa[kPrefetch], rsb[kPrefetch];
-  const int64_t nsteps = p.K / kGemmK;
+  // Codes and scales of step k + kPrefetch are requested at step k.  The
+  // ring index is static: the loop runs kPrefetch steps per iteration.
+  g32x4 ra[kPrefetch], rb[kPrefetch];
+  uint32_t rsa[kPrefetch], rsb[kPrefetch];  // two scale bytes each
+  // K is a multiple of 32: a last step of 32 leaves blocks 2 and 3 empty
+  const int64_t nsteps = (p.K + kGemmK - 1) / kGemmK;
+  auto scale2 = [](const uint8_t* q) -> uint32_t { return (uint32_t)q[0] | ((uint32_t)q[1] << 8); };
+  auto has = [&](int64_t st) { return st * kGemmK + 16 * lb + 32 <= p.K; };  // the thread's blocks exist
 #pragma unroll
   for (int u = 0; u < kPrefetch; ++u) {
-    ra[u] = rb[u] = g32x2{0u, 0u};
+    ra[u] = rb[u] = g32x4{0u, 0u, 0u, 0u};
     rsa[u] = rsb[u] = 0u;
-    if (u < nsteps) {
-      ra[u] = *reinterpret_cast<const g32x2*>(ac + (int64_t)u * (kGemmK / 2));
-      rb[u] = *reinterpret_cast<const g32x2*>(bc + (int64_t)u * (kGemmK / 2));
-      rsa[u] = as[u * (kGemmK / 16)];
-      rsb[u] = bs[u * (kGemmK / 16)];
+    if (u < nsteps && has(u)) {
+      ra[u] = *reinterpret_cast<const g32x4*>(ac + (int64_t)u * (kGemmK / 2));
+      rb[u] = *reinterpret_cast<const g32x4*>(bc + (int64_t)u * (kGemmK / 2));
+      rsa[u] = scale2(as + u * (kGemmK / 16));
+      rsb[u] = scale2(bs + u * (kGemmK / 16));
     }
   }
+  // expand and store the two blocks of one operand row
+  auto put = [&](bool ok, g32x4 c, uint32_t sc, _Float16* dst) {
+    uint32_t e0[8], e1[8];
+    expand16<GRID>(ok ? g32x2{c.x, c.y} : g32x2{0u, 0u}, sc & 0xFFu, e0);
+    expand16<GRID>(ok ? g32x2{c.z, c.w} : g32x2{0u, 0u}, sc >> 8, e1);
+    store16(e0, dst);
+    store16(e1, dst + 16);
+  };
   if (nsteps > 0) {
-    uint32_t ea[8], eb[8];
-    expand16<GRID>(a_ok ? ra[0] : g32x2{0u, 0u}, rsa[0], ea);
-    expand16<GRID>(b_ok ? rb[0] : g32x2{0u, 0u}, rsb[0], eb);
-    store16(ea, &As[0][lr][16 * lb]);
-    store16(eb, &Bs[0][lr][16 * lb]);
+    put(a_ok, ra[0], rsa[0], &As[0][lr][16 * lb]);
+    put(b_ok, rb[0], rsb[0], &Bs[0][lr][16 * lb]);
   }
   __syncthreads();
   for (int64_t s0 = 0; s0 < nsteps; s0 += kPrefetch) {
@@ -168,47 +177,55 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
         // step st + kPrefetch's
         if (st + kPrefetch < nsteps) {
           const int64_t k1 = (st + kPrefetch) * kGemmK;
-          ra[u] = *reinterpret_cast<const g32x2*>(ac + k1 / 2);
-          rb[u] = *reinterpret_cast<const g32x2*>(bc + k1 / 2);
-          rsa[u] = as[k1 / 16];
-          rsb[u] = bs[k1 / 16];
-        }
-        f16x8 fa[2][2], fb[2][4];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            fa[kk][i] = *reinterpret_cast<const f16x8*>(&As[cur][wm + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            fb[kk][j] = *reinterpret_cast<const f16x8*>(&Bs[cur][wn + 32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+          const bool h = has(st + kPrefetch);
+          ra[u] = h ? *reinterpret_cast<const g32x4*>(ac + k1 / 2) : g32x4{0u, 0u, 0u, 0u};
+          rb[u] = h ? *reinterpret_cast<const g32x4*>(bc + k1 / 2) : g32x4{0u, 0u, 0u, 0u};
+          rsa[u] = h ? scale2(as + k1 / 16) : 0u;
+          rsb[u] = h ? scale2(bs + k1 / 16) : 0u;
         }
         // the next step's codes sit in slot (u + 1) % kPrefetch; they are
         // expanded in registers while the multiplies run (after the last
         // step the slot is stale and its expansion goes unread)
         const int v = (u + 1) % kPrefetch;
-        uint32_t ea[8], eb[8];
-        expand16<GRID>(a_ok ? ra[v] : g32x2{0u, 0u}, rsa[v], ea);
-        expand16<GRID>(b_ok ? rb[v] : g32x2{0u, 0u}, rsb[v], eb);
+        uint32_t ea[2][8], eb[2][8];
+        expand16<GRID>(a_ok ? g32x2{ra[v].x, ra[v].y} : g32x2{0u, 0u}, rsa[v] & 0xFFu, ea[0]);
+        expand16<GRID>(a_ok ? g32x2{ra[v].z, ra[v].w} : g32x2{0u, 0u}, rsa[v] >> 8, ea[1]);
+        expand16<GRID>(b_ok ? g32x2{rb[v].x, rb[v].y} : g32x2{0u, 0u}, rsb[v] & 0xFFu, eb[0]);
+        expand16<GRID>(b_ok ? g32x2{rb[v].z, rb[v].w} : g32x2{0u, 0u}, rsb[v] >> 8, eb[1]);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int half = 0; half < 2; ++half) {
+          f16x8 fa[2][2], fb[2][4];
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int q = 0; q < 2; ++q) {
+            const int kk = 2 * half + q;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              fa[q][i] = *reinterpret_cast<const f16x8*>(&As[cur][wm + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
-        // issue order: the fragment reads, then each multiply followed by a
-        // share of the expansion's arithmetic, so the VALU works while the
-        // matrix unit runs
-        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
+              fb[q][j] = *reinterpret_cast<const f16x8*>(&Bs[cur][wn + 32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+          }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[q][i], fb[q][j], acc[i][j], 0, 0, 0);
+          // issue order: the fragment reads, then each multiply followed by
+          // a share of the expansion's arithmetic
+          __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+          }
         }
         // the other buffer was last read before the previous step's barrier
-        store16(ea, &As[cur ^ 1][lr][16 * lb]);
-        store16(eb, &Bs[cur ^ 1][lr][16 * lb]);
+        store16(ea[0], &As[cur ^ 1][lr][16 * lb]);
+        store16(ea[1], &As[cur ^ 1][lr][16 * lb + 16]);
+        store16(eb[0], &Bs[cur ^ 1][lr][16 * lb]);
+        store16(eb[1], &Bs[cur ^ 1][lr][16 * lb + 16]);
         __syncthreads();
       }
     }
