@@ -23,9 +23,9 @@
 //
 // The expansion is byte arithmetic: every grid value's fp16 encoding has a
 // zero low byte, so one byte permute looks the high bytes of four codes up in
-// an 8-entry table, a three-input bitwise op adds their signs, a second permute
-// interleaves the
-// zero low bytes, and a packed fp16 multiply applies the block scale.
+// an 8-entry table, a three-input bitwise op adds their signs, a second
+// permute interleaves the zero low bytes, and a packed fp16 multiply applies
+// the block scale.
 #include <hip/hip_runtime.h>
 
 #include "ufp4_internal.hpp"
