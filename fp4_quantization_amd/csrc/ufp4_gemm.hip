@@ -239,7 +239,8 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int64_t col = n0 + wn + 32 * j + (lane & 31);
-        if (row < p.M && col < p.N) p.c[row * p.ldc + col] = acc[i][j][r] * s;
+        // written once, never read here: a non-temporal store
+        if (row < p.M && col < p.N) __builtin_nontemporal_store(acc[i][j][r] * s, &p.c[row * p.ldc + col]);
       }
 }
 
