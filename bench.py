@@ -1,7 +1,7 @@
 """Benchmark: fused RHT + E1M2 row+column quantization of an 8192x2048 bf16
 activation on one MI355X, reported as HBM GB/s (algorithmic bytes / time).
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--warm] [--copy]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-warm] [--copy]
                 [--schedule auto|two-pass|single-pass] [--no-extra]
 
 A step is one ufp4_quantize_rowcol call (every stage of the hot path: load,
@@ -383,8 +383,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--warm", action="store_true",
-                    help="also time repeated calls on one buffer set (input cache-resident)")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm figure (repeated calls on one buffer set, input cache-resident)")
     ap.add_argument("--schedule", choices=("auto", "two-pass", "single-pass"), default="auto",
                     help="schedule of the timed calls (the other one is timed beside it)")
     ap.add_argument("--no-extra", action="store_true",
@@ -401,9 +401,9 @@ def main():
         d = args.summarize_counters
         summarize_counters(*d, commands=[
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[0]} -o run -- "
-            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
+            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --no-warm",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[1]} -o run -- "
-            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra",
+            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --no-warm",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[2]} -o run -- "
             "python3 bench.py --copy --steps 5 --warmup 2",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[3]} -o run -- "
@@ -464,7 +464,7 @@ def main():
     ms, graph = time_graph(torch, on, args.steps, args.warmup, stream)
     ms_off, _ = time_graph(torch, off, args.steps, args.warmup, stream)
     ms_eager = time_eager(torch, on, args.steps, args.warmup, stream)
-    ms_warm = time_graph(torch, on[:1], args.steps, args.warmup, stream)[0] if args.warm else None
+    ms_warm = None if args.no_warm else time_graph(torch, on[:1], args.steps, args.warmup, stream)[0]
     # per-kernel durations: hipEvents around each kernel of one call, on the
     # launch stream, over calls that rotate through the buffer sets
     per_kernel = []
