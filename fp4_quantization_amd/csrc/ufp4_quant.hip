@@ -1069,8 +1069,6 @@ __global__ __launch_bounds__(kThreads, 2) void ufp4_fused_kernel(QuantParams p) 
   constexpr float qmax = grid_qmax<GRID>();
   TensorScale tsr, tsc;
   tensor_setup<RHT>(r, c, qmax, tsr, tsc, lut);
-  // every workgroup has read the generation word by now
-  if (threadIdx.x == 0) __hip_atomic_store(p.fs_gen, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // The workgroup's own tile first (already in registers); then the tiles
   // that were left, the q-th (by index) going to the staying tile of rank
   // q mod (number staying).
@@ -1083,6 +1081,11 @@ __global__ __launch_bounds__(kThreads, 2) void ufp4_fused_kernel(QuantParams p) 
   }
   const int32_t n_stay = n - n_left;
   int32_t q = T.work - below;  // rank among the staying tiles
+  // Every workgroup has read the generation word by now, so one writer
+  // suffices: the staying tile of rank 0 (at least one tile always stays).
+  // (Stores from all workgroups to this one word serialize at the memory
+  // and hold up each writer's following stores by microseconds.)
+  if (threadIdx.x == 0 && q == 0) __hip_atomic_store(p.fs_gen, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
