@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int m = 0; m < 16; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU (best of 2..8 measured)
           }
         }
         // the other buffer was last read before the previous step's barrier
