@@ -7,7 +7,7 @@ import subprocess
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = [os.path.join(_HERE, "csrc", f)
-           for f in ("ufp4_quant.hip", "ufp4_misc.hip", "ufp4_gemm.hip", "ufp4_api.hip")]
+           for f in ("ufp4_quant.hip", "ufp4_misc.hip", "ufp4_gemm.hip", "ufp4_host.hip", "ufp4_api.hip")]
 OUT = os.path.join(_HERE, "libufp4.so")
 
 # -ffp-contract=off: no implicit fused multiply-add (every rounding step is

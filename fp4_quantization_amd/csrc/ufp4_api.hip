@@ -175,7 +175,8 @@ int ufp4_gemm_nt(const ufp4_config* cfg, int64_t M, int64_t N, int64_t K, ufp4_q
   if (!aligned(a.codes, 16) || !aligned(b.codes, 16) || !aligned(c, 4) || !aligned(a.tensor_scale, 4) ||
       !aligned(b.tensor_scale, 4))
     return UFP4_ERR_ALIGNMENT;
-  if ((M + 127) / 128 > 0xFFFF || (N + 127) / 128 > 0x7FFFFFFF) return UFP4_ERR_SHAPE;
+  // grid: (N / 256) x (M / 256) workgroups of 256 x 256 output tiles
+  if ((M + 255) / 256 > 0xFFFF || (N + 255) / 256 > 0x7FFFFFFF) return UFP4_ERR_SHAPE;
   GemmParams p;
   p.a_codes = a.codes;
   p.a_scales = a.scales;
@@ -281,7 +282,11 @@ int ufp4_workspace_status(const void* ws, size_t ws_bytes, int* status_out, ufp4
                      (hipStream_t)stream) != hipSuccess)
     return UFP4_ERR_HIP;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return UFP4_ERR_HIP;
-  *status_out = st ? UFP4_ERR_OFFSETS : UFP4_OK;
+  // the device writes 0, UFP4_ERR_OFFSETS (grouped offsets rejected) or
+  // UFP4_ERR_SYNC (a single-pass exchange that did not complete); any other
+  // word means the workspace was never initialized or was overwritten
+  *status_out = (st == 0u || st == (uint32_t)UFP4_ERR_OFFSETS || st == (uint32_t)UFP4_ERR_SYNC) ? (int)st
+                                                                                             : UFP4_ERR_WORKSPACE;
   return UFP4_OK;
 }
 

@@ -71,7 +71,8 @@ enum ufp4_status {
   UFP4_ERR_OFFSETS = 6,          /* grouped offsets were found invalid on the device */
   UFP4_ERR_SYNC = 7              /* a single-pass call's device-wide exchange did not
                                     complete within 2 s (a device fault); its outputs
-                                    are incomplete and the workspace must be re-initialized */
+                                    are incomplete; the workspace stays usable (the
+                                    failed call advanced its generation) */
 };
 
 /* Code layouts: E1M2, E2M1 and E2M1C store sign | magnitude index (index 0..7,
@@ -141,13 +142,23 @@ size_t ufp4_workspace_size(int64_t rows, int64_t cols, int32_t num_groups);
  * schedule).  Every later call leaves it ready for the next one. */
 int ufp4_workspace_init(void* ws, size_t ws_bytes, ufp4_stream_t stream);
 
-/* After a grouped call: writes UFP4_OK or UFP4_ERR_OFFSETS (the device found
- * the offsets invalid and wrote no output); UFP4_ERR_SYNC after a single-pass
- * call whose exchange timed out.  Synchronizes the stream. */
+/* Reads the status word the last call left in the workspace and writes it to
+ * *status_out: UFP4_OK; UFP4_ERR_OFFSETS after a grouped call whose offsets
+ * the device found invalid (no output written); UFP4_ERR_SYNC after a
+ * single-pass call whose exchange timed out (outputs incomplete; the next
+ * single-pass call clears it); UFP4_ERR_WORKSPACE if the word holds anything
+ * else (a workspace never initialized, or overwritten).  Returns UFP4_OK when
+ * the word was read.  Synchronizes the stream. */
 int ufp4_workspace_status(const void* ws, size_t ws_bytes, int* status_out, ufp4_stream_t stream);
 
 /* Row-wise quantization of x[rows][ld] (bf16 bit patterns), blocks along each
- * row.  cols must be a multiple of 16 (NV16) or 32 (MX32); rows may be any
+ * row: the operand layout of the forward GEMM and of dY in the input-gradient
+ * GEMM.  Implements steps 1-4 above for one layout: the RHT of every block
+ * ("Shrinkage Bias: The Hidden Geometric Trap in FP4 Training" (zhichai.net),
+ * "Key points", the RHT paradox and the fix), the two-level scale (hotpaper.ai
+ * summary, technical approach: NVFP4 / MXFP4 formats), rounding onto the
+ * selected grid (zhichai.net "Key points": the E2M1 and E1M2 grids;
+ * autonainews.com "The UFP4 Recipe": E1M2 or INT4, stochastic rounding).  cols must be a multiple of 16 (NV16) or 32 (MX32); rows may be any
  * size >= 0.  x must be 16-byte aligned with ld a multiple of 8 elements and
  * ld >= cols; output pointers 16-byte aligned.
  * Output: codes[rows][cols/2], scales[rows][cols/B] (B = 16 or 32),
@@ -156,8 +167,13 @@ int ufp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                   const ufp4_config* cfg, ufp4_qtensor row_out, void* ws, size_t ws_bytes,
                   ufp4_stream_t stream);
 
-/* Row-wise and column-wise quantization of the same tensor in one call.
- * rows and cols must both be multiples of B.  Column-wise output is stored
+/* Row-wise and column-wise quantization of the same tensor in one call: the
+ * fused RHT + quantization of a training-GEMM operand in both of the
+ * orientations the three GEMMs read it in ("Shrinkage Bias: The Hidden
+ * Geometric Trap in FP4 Training" (zhichai.net), "Key points": RHT on all
+ * three GEMM paths, fused RHT+quantization kernels; autonainews.com "The UFP4
+ * Recipe": fwd_y, bwd_dx and bwd_dw operands).  rows and cols must both be
+ * multiples of B.  Column-wise output is stored
  * transposed: codes[cols][rows/2], scales[cols][rows/B], tensor_scale[1]
  * (its own per-tensor scale, from the column-wise transformed values). */
 int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
@@ -165,7 +181,16 @@ int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
                          void* ws, size_t ws_bytes, ufp4_stream_t stream);
 
 /* Grouped (MoE) quantization of x[total_rows][cols] whose rows are split into
- * num_groups ragged segments: segment e is rows [offsets[e], offsets[e+1]).
+ * num_groups ragged segments: segment e is rows [offsets[e], offsets[e+1]);
+ * the per-expert operands of the mixture-of-experts models the recipe is
+ * validated on ("Shrinkage Bias: The Hidden Geometric Trap in FP4 Training"
+ * (zhichai.net), "Key points", validation results: MoE models; autonainews.com
+ * "Empirical Validation and Hardware Implications").  Each segment is
+ * quantized exactly as ufp4_quantize_rowcol would quantize it alone, its
+ * column-wise blocks zero-padded.  The column-wise line length is passed as
+ * padded_rows (a host value) rather than as a device array of column offsets:
+ * the offsets follow from offsets_dev and the block, and the device derives
+ * them, so the two can never disagree.
  * offsets_dev: device array of num_groups+1 int64, offsets[0] = 0, non-
  * decreasing, offsets[E] = total_rows.  Each segment gets its own tensor scale
  * per layout.  Column-wise blocks restart at each segment start; a segment's
@@ -184,7 +209,11 @@ int ufp4_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
                           void* ws, size_t ws_bytes, ufp4_stream_t stream);
 
 /* Dequantize one layout in its own orientation: `rows` lines of `cols`
- * elements (for a column-wise output: rows = tensor cols, cols = tensor rows).
+ * elements (for a column-wise output: rows = tensor cols, cols = tensor rows):
+ * the values the GEMM consumes, x_hat = value(code) * d_b, which the pages'
+ * decomposition of a quantized operand into a scaled copy plus a residual is
+ * about ("Shrinkage Bias: The Hidden Geometric Trap in FP4 Training"
+ * (zhichai.net), "Key points": compounding decay).
  * out[rows][cols] = value(code) * d_b, one rounding, d_b = decode(scale) * S_t
  * (NV16) or 2^(scale-127) (MX32); with inverse_rht != 0 each 16-block is then
  * mapped back through the inverse transform (butterfly, x1/4, signs). */
@@ -193,7 +222,12 @@ int ufp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* te
                     float* out, ufp4_stream_t stream);
 
 /* Diagnostics (ufp4_stats_t) of one dense layout of x (layout 0 row-wise,
- * 1 column-wise) against its quantization (codes/scales/tensor_scale as
+ * 1 column-wise), the quantities the pages reason with: SQNR (zhichai.net
+ * "Key points", the RHT paradox), the per-bucket mean signed error that makes
+ * E2M1 shrink (zhichai.net "Key points", the cause; autonainews.com
+ * "Unveiling the Geometric Roots of Shrinkage Bias"), the gain alpha and the
+ * bucket utilisation (hotpaper.ai summary, core idea), against its
+ * quantization (codes/scales/tensor_scale as
  * written by ufp4_quantize / _rowcol).  Uses the workspace; synchronizes the
  * stream and fills *host_out. */
 int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_t layout,

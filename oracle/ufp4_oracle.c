@@ -251,6 +251,7 @@ uint8_t orc_round_to_code(float y, int32_t grid, int32_t rounding, uint32_t r32)
 int orc_round_f32(const float* y, int64_t n, int32_t grid, int32_t rounding,
                   uint64_t sr_seed, uint8_t* codes) {
   if (n < 0 || (n > 0 && (!y || !codes))) return 1;
+  if (grid < 0 || grid > 3 || rounding < 0 || rounding > 1) return 1;
   for (int64_t i = 0; i < n; ++i) {
     uint32_t r = rounding == ORC_ROUND_SR ? orc_sr_word(sr_seed, (uint64_t)i, 0u) : 0u;
     codes[i] = orc_round_to_code(y[i], grid, rounding, r);

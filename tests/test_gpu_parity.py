@@ -477,6 +477,28 @@ def test_single_pass_workspace_reuse_across_shapes(env, schedule):
     assert ws.status() == 0
 
 
+def test_workspace_status_words(env, schedule):
+    # the status word is planted from the host (no fault is provoked): the
+    # device writes 0, 6 (grouped offsets rejected) or 7 (a single-pass
+    # exchange that did not complete); anything else is a corrupt workspace
+    torch, F, orc = env
+    ws = F.Workspace(256, 256)
+    for word, want in ((0, 0), (6, 6), (7, 7), (5, 4), (0xDEAD, 4)):
+        ws.buf[4:8] = torch.tensor([word], dtype=torch.int32).view(torch.uint8).cuda()
+        assert ws.status() == want, (word, want)
+    # a later single-pass call clears a stale failure and leaves a valid output
+    schedule(SINGLE_PASS)
+    ws.buf[4:8] = torch.tensor([7], dtype=torch.int32).view(torch.uint8).cuda()
+    xb = synth.activation(256, 256, seed=3)
+    fc, oc = cfgs(F, orc, E1M2, RTNE, NV16, 1, 3, 3)
+    x = to_dev(torch, xb)
+    row, col = F.alloc_layout(256, 256, NV16), F.alloc_layout(256, 256, NV16)
+    F.ufp4_quantize_rowcol(x, fc, row, col, ws)
+    assert ws.status() == 0
+    assert_layout_equal(row, orc.quantize(xb, oc, ROW), "row")
+    assert_layout_equal(col, orc.quantize(xb, oc, COL), "col")
+
+
 # ------------------------------------------------------------------ grouped
 def gpu_grouped(env, xb, offsets, fc, row=True, col=True):
     torch, F, _ = env

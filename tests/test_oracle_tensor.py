@@ -161,6 +161,72 @@ def test_sr_index_mapping_row(orc):
         assert u[r, c] == want
 
 
+def _col_sr_code(orc, seg_f32, m_pad, c, m, coff_e, R_pad, scale_byte, seed, signs):
+    """Expected stochastic-rounding code of column-wise output element (c, m)
+    of a segment, rebuilt from pinned pieces only: the block's transform
+    (orc.rht16, pinned by the Hadamard tests), the MX32 power-of-two factor
+    read from the scale byte (exact), the random word of index
+    c*R_pad + col_off + m in stream 1 (orc.sr_word, pinned against rocRAND)
+    and the rounding rule with an explicit word (pinned by the 3-sigma and
+    exact-grid tests)."""
+    b0 = (m // 16) * 16
+    blk = np.zeros(16, np.float32)
+    for t in range(16):
+        if b0 + t < seg_f32.shape[0]:
+            blk[t] = seg_f32[b0 + t, c]
+    v = orc.rht16(blk, signs)[m - b0]
+    y = np.float32(v * np.float32(2.0 ** -(int(scale_byte) - 127)))
+    word = orc.sr_word(seed, c * R_pad + coff_e + m, 1)
+    return int(orc.lib().orc_round_to_code(float(y), E1M2, SR, word))
+
+
+def test_sr_index_mapping_col_dense(orc):
+    # column output element (c, m) is line c, position m: SR word index
+    # c*R + m of stream 1 (each output's own flat index; a row-major index
+    # r*C + c or the row stream would fail here)
+    R, C, seed = 64, 48, 13
+    xb = synth.output_grad(R, C, 6)
+    xf = synth.bf16_to_f32(xb)
+    cfg = orc.config(rounding=SR, sr_seed=seed, rht=1, rht_seed=5, scaling=MX32)
+    codes, scales, _ = orc.quantize(xb, cfg, COL)
+    u = unpack(codes)
+    signs = orc.rht_signs(5)
+    rng = np.random.default_rng(1)
+    picks = [(0, 0), (47, 63), (5, 17), (30, 40)] + [tuple(p) for p in rng.integers(0, [C, R], size=(24, 2))]
+    for c, m in picks:
+        want = _col_sr_code(orc, xf, R, c, m, 0, R, scales[c, m // 32], seed, signs)
+        assert u[c, m] == want, (c, m)
+
+
+def test_sr_index_mapping_col_grouped(orc):
+    # grouped column output: segment e occupies positions [col_off[e],
+    # col_off[e+1]) of each line, padded to a multiple of the block; element m
+    # of segment e in line c uses index c*R_pad + col_off[e] + m (padded
+    # positions included: they are nonzero after the transform)
+    counts = np.array([5, 0, 37, 16, 70])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    R, C, seed = int(off[-1]), 32, 21
+    xb = synth.output_grad(R, C, 8)
+    xf = synth.bf16_to_f32(xb)
+    cfg = orc.config(rounding=SR, sr_seed=seed, rht=1, rht_seed=7, scaling=MX32)
+    _, (cc, cs, _), coff = orc.quantize_grouped(xb, off, cfg, row=False)
+    R_pad = int(coff[-1])
+    u = unpack(cc)
+    signs = orc.rht_signs(7)
+    rng = np.random.default_rng(2)
+    n_pad = 0
+    for e in np.flatnonzero(counts):
+        seg = xf[off[e]:off[e + 1]]
+        P = int(coff[e + 1] - coff[e])
+        ms = sorted({0, int(counts[e]) - 1, P - 1, *rng.integers(0, P, size=6).tolist()})
+        for m in ms:
+            c = int(rng.integers(0, C))
+            n_pad += m >= counts[e]
+            want = _col_sr_code(orc, seg, P, c, m, int(coff[e]), R_pad, cs[c, (coff[e] + m) // 32], seed, signs)
+            assert u[c, coff[e] + m] == want, (e, c, m)
+    assert n_pad > 0
+
+
 # ---------------------------------------------------------------- grouped
 def test_grouped_matches_dense_per_segment(orc):
     rng = np.random.default_rng(8)
