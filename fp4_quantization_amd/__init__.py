@@ -111,6 +111,14 @@ def ufp4_quantize_rowcol(x: torch.Tensor, cfg: ufp4_config, row_out: QTensor, co
                                    ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)))
 
 
+def ufp4_quantize_rowcol_noalloc(x: torch.Tensor, cfg: ufp4_config, row_out: QTensor, col_out: QTensor,
+                                 stream=None) -> None:
+    rows, cols, ld = _bf16_view(x)
+    check("ufp4_quantize_rowcol_noalloc",
+          lib.ufp4_quantize_rowcol_noalloc(_ptr(x), rows, cols, ld, ctypes.byref(cfg), row_out.c(), col_out.c(),
+                                           _stream(stream)))
+
+
 def ufp4_quantize_grouped(x: torch.Tensor, offsets_dev: torch.Tensor, padded_rows: int,
                           cfg: ufp4_config, row_out: QTensor | None, col_out: QTensor | None,
                           ws: Workspace | None, stream=None) -> None:

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/ufp4.h"
 #include "ufp4_internal.hpp"
@@ -41,6 +42,32 @@ std::atomic<int> g_schedule{UFP4_SCHEDULE_AUTO};
 std::atomic<int> g_left_stride{0};
 
 size_t stats_ws_bytes() { return kWsPartOffset + (size_t)kStatsMaxWg * kStatsSlots * sizeof(double); }
+
+// Workspace of ufp4_quantize_rowcol_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  In host code `scratch` only
+// names the symbol; its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)1 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of the scratch array, zeroed (by a fill kernel
+// on `stream`) before its first use; null if the runtime call fails.
+void* scratch_for_current_device(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    if (launch_fill(static_cast<uint32_t*>(ptr), (int64_t)(kScratchBytes / 4), 0u, stream) != hipSuccess)
+      return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 // An empty output (no elements) may pass null codes/scales; the tensor
 // scale is always written.
@@ -346,6 +373,20 @@ int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
                          const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws,
                          size_t ws_bytes, ufp4_stream_t stream) {
   return rowcol_impl(x, rows, cols, ld, cfg, row_out, col_out, ws, ws_bytes, stream, nullptr);
+}
+
+int ufp4_quantize_rowcol_noalloc(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                 const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out,
+                                 ufp4_stream_t stream) {
+  // the same argument checks as the workspace variant come first (it reports
+  // them before looking at the workspace)
+  const int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (rows < 0 || cols < 0 || ld < cols) return UFP4_ERR_INVALID_ARGUMENT;
+  if (quant_ws_bytes(rows, cols, 1) > kScratchBytes) return UFP4_ERR_WORKSPACE;
+  void* ws = scratch_for_current_device((hipStream_t)stream);
+  if (!ws) return UFP4_ERR_HIP;
+  return rowcol_impl(x, rows, cols, ld, cfg, row_out, col_out, ws, kScratchBytes, stream, nullptr);
 }
 
 int ufp4_time_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const ufp4_config* cfg,

@@ -180,6 +180,22 @@ int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
                          const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out,
                          void* ws, size_t ws_bytes, ufp4_stream_t stream);
 
+/* ufp4_quantize_rowcol for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and outputs, bit for bit, without a
+ * workspace.  Scratch memory is a 1 MiB array the library holds on each GPU
+ * it runs on until the process ends; its address is looked up (no
+ * allocation) and the array zeroed by a fill kernel on `stream` at the first
+ * call on each device.  Tensors whose workspace would exceed it (more than
+ * about 127,000 tiles of 128 x 256 elements, 4.2e9 elements) give
+ * UFP4_ERR_WORKSPACE; a failed symbol lookup gives UFP4_ERR_HIP.  All calls
+ * on one GPU share the array: calls that overlap on one GPU (concurrent
+ * streams, threads) race and must be serialized by the caller.  Calls no
+ * hipMalloc, hipFree or other allocating routine. */
+int ufp4_quantize_rowcol_noalloc(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                 const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out,
+                                 ufp4_stream_t stream);
+
 /* Grouped (MoE) quantization of x[total_rows][cols] whose rows are split into
  * num_groups ragged segments: segment e is rows [offsets[e], offsets[e+1]);
  * the per-expert operands of the mixture-of-experts models the recipe is

@@ -127,6 +127,18 @@ int main() {
   EXPECT(ufp4_time_rowcol(x, 8192, 2048, 2048, &ok, row, col, ws, wsb, nullptr, nullptr, &tq),
          UFP4_ERR_INVALID_ARGUMENT);
 
+  // the no-allocation variant: argument errors first, then the size limit;
+  // a valid call needs the device's scratch array, which a GPU-less run
+  // cannot look up (UFP4_ERR_HIP), or runs to the stubbed launches
+  EXPECT(ufp4_quantize_rowcol_noalloc(x, 64, 64, 64, nullptr, row, col, nullptr), UFP4_ERR_INVALID_ARGUMENT);
+  EXPECT(ufp4_quantize_rowcol_noalloc(x, 64, 64, 32, &ok, row, col, nullptr), UFP4_ERR_INVALID_ARGUMENT);
+  EXPECT(ufp4_quantize_rowcol_noalloc(x, (int64_t)1 << 24, 16384, 16384, &ok, row, col, nullptr),
+         UFP4_ERR_WORKSPACE);
+  {
+    const int r = ufp4_quantize_rowcol_noalloc(x, 8192, 2048, 2048, &ok, row, col, nullptr);
+    EXPECT(r == UFP4_ERR_HIP || r == UFP4_OK, 1);
+  }
+
   // ufp4_quantize_grouped
   const int64_t* off = dev<int64_t>((size_t)8 << 30);
   const size_t gwsb = ufp4_workspace_size(65536, 4096, 64);
