@@ -174,12 +174,13 @@ def ufp4_quantize_delayed(x: torch.Tensor, cfg: ufp4_config, amax_in: torch.Tens
                                     row_out.c(), col, _stream(stream)))
 
 
-def ufp4_schedule_of(rows: int, cols: int, cfg: ufp4_config, num_groups: int = 1) -> int:
+def ufp4_schedule_of(rows: int, cols: int, cfg: ufp4_config, num_groups: int = 1,
+                     both_layouts: bool = True) -> int:
     """SCHEDULE_SINGLE_PASS or SCHEDULE_TWO_PASS: what a call on this shape
-    and configuration takes on the current device."""
+    and configuration (both layouts, or one) takes on the current device."""
     out = ctypes.c_int32(0)
-    check("ufp4_schedule_of", lib.ufp4_schedule_of(int(rows), int(cols), int(num_groups), ctypes.byref(cfg),
-                                                   ctypes.byref(out)))
+    check("ufp4_schedule_of", lib.ufp4_schedule_of(int(rows), int(cols), int(num_groups), int(bool(both_layouts)),
+                                                   ctypes.byref(cfg), ctypes.byref(out)))
     return out.value
 
 

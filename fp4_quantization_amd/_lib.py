@@ -114,7 +114,7 @@ def _load():
     L.ufp4_recipe_config.restype = ctypes.c_int
     L.ufp4_recipe_config.argtypes = [i32, i32, i32, u64, u64, cfgp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ufp4_schedule_of.restype = ctypes.c_int
-    L.ufp4_schedule_of.argtypes = [i64, i64, i32, cfgp, ctypes.POINTER(i32)]
+    L.ufp4_schedule_of.argtypes = [i64, i64, i32, i32, cfgp, ctypes.POINTER(i32)]
     return L
 
 

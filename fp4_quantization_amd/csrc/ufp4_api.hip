@@ -99,12 +99,25 @@ void base_params(QuantParams& p, const uint16_t* x, int64_t rows, int64_t cols, 
   p.ws_status = ws ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + 4) : nullptr;
 }
 
+// Workgroups of the single-pass kernels the current device holds at once
+// (two per compute unit), 0 if it cannot be queried.
+int64_t resident_tiles() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return 2 * (int64_t)cus;
+}
+
 // Whether a dense NV16 call of n_work tiles takes the single pass.  AUTO
-// takes the two-pass schedule: on MI355X it is the faster one for every
-// tensor measured (an 8192 x 2048 call: 26.8 us against 42.6 us).
-bool single_pass(bool grouped, bool mx, int64_t n_work) {
+// takes it for row+column calls whose tiles the device holds at once (on
+// MI355X the 8192 x 2048 row+column call takes 26.0 us against 27.9 us in
+// two passes, and reads its input once instead of twice); single-layout
+// calls keep the two-pass schedule.
+bool single_pass(bool grouped, bool mx, bool both, int64_t n_work) {
   if (grouped || mx || n_work > kMaxFusedTiles) return false;
-  return g_schedule.load(std::memory_order_relaxed) == UFP4_SCHEDULE_SINGLE_PASS;
+  const int mode = g_schedule.load(std::memory_order_relaxed);
+  if (mode == UFP4_SCHEDULE_SINGLE_PASS) return true;
+  return mode == UFP4_SCHEDULE_AUTO && both && n_work <= resident_tiles();
 }
 
 // Start and end events of the two kernels of one call.
@@ -132,7 +145,7 @@ int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream, Ker
     const size_t need = quant_ws_bytes(p.rows, p.cols, p.num_groups);
     if (!ws || ws_bytes < need || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
     p.ws_part = reinterpret_cast<float2*>(static_cast<uint8_t*>(ws) + kWsPartOffset);
-    if (single_pass(p.offsets != nullptr, false, p.n_work)) {
+    if (single_pass(p.offsets != nullptr, false, p.do_row && p.do_col, p.n_work)) {
       const int mode = g_schedule.load(std::memory_order_relaxed);
       // every tile fits on the device at once: one pass over the input
       uint8_t* base = static_cast<uint8_t*>(ws);
@@ -282,14 +295,14 @@ int ufp4_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   return UFP4_OK;
 }
 
-int ufp4_schedule_of(int64_t rows, int64_t cols, int32_t num_groups, const ufp4_config* cfg,
+int ufp4_schedule_of(int64_t rows, int64_t cols, int32_t num_groups, int32_t both_layouts, const ufp4_config* cfg,
                      int32_t* schedule_out) {
   if (check_cfg(cfg) || !schedule_out || rows < 0 || cols < 0 || num_groups < 1)
     return UFP4_ERR_INVALID_ARGUMENT;
   int32_t nb, nt;
   grid_size_quant(rows, cols, num_groups, block_of(cfg), &nb, &nt);
   const bool one = rows > 0 && cols > 0 &&
-                   single_pass(num_groups > 1, cfg->scaling == UFP4_SCALE_MX32, (int64_t)nb * nt);
+                   single_pass(num_groups > 1, cfg->scaling == UFP4_SCALE_MX32, both_layouts != 0, (int64_t)nb * nt);
   *schedule_out = one ? UFP4_SCHEDULE_SINGLE_PASS : UFP4_SCHEDULE_TWO_PASS;
   return UFP4_OK;
 }

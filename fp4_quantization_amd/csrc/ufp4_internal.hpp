@@ -50,19 +50,24 @@ struct QuantParams {
   float2* amax_out;       // [n_work], or null
   // single-pass schedule
   uint32_t* fs_gen;          // call generation, advanced once per call
-  uint64_t* fs_words;        // [3][n_work] generation-tagged words: start, row-wise and column-wise partial
+  uint64_t* fs_words;        // generation-tagged words: start words, tile maxima, aggregators' results
   int32_t fs_orphan_stride;  // > 1: tiles whose index is not a multiple leave their work to others
 };
 
 // Workspace layout (bytes): a 256-byte header (status word at 4, call
 // generation at 128), the single-pass schedule's generation-tagged words
-// (three 8-byte words per tile, up to kMaxFusedTiles tiles; nothing else is
+// (start words in kFsReplicas copies, tile maxima and the aggregators'
+// results, up to kMaxFusedTiles tiles; nothing else is
 // ever stored there, so a stale word carries an older generation), then one
 // float2 partial per tile for the two-pass schedule.
 constexpr size_t kWsHeader = 256;
 constexpr size_t kWsGenOffset = 128;
 constexpr int kMaxFusedTiles = 1024;
-constexpr size_t kWsFusedWords = (size_t)kMaxFusedTiles * 3 * sizeof(uint64_t);
+// The single-pass start words are written in kFsReplicas copies and each
+// workgroup reads one of them, so that no memory line has more than
+// 1/kFsReplicas of the workgroups reading it.
+constexpr int kFsReplicas = 8;
+constexpr size_t kWsFusedWords = ((size_t)(kFsReplicas + 2) * kMaxFusedTiles + 64 * 16) * sizeof(uint64_t);
 constexpr size_t kWsPartOffset = kWsHeader + kWsFusedWords;
 
 void fill_rht_signs(uint64_t seed, QuantParams& p);

@@ -473,20 +473,250 @@ __device__ __forceinline__ bool block_scales(const float raw[NB], const TensorSc
   return !__any(bad);
 }
 
-// Staging of a tile's column-wise output: [chunk][column] with chunk = the
-// 16-row block of one half-wavefront (8 per 128-row tile).  One padding
-// entry per chunk row spreads the write-out reads over the LDS banks.
-struct ColStage {
-  uint2 codes[8][kBandCols + 1];
-  uint8_t scales[8][kBandCols + 4];
+// Staging of a tile's column-wise output for NK of each lane's 8 columns
+// (32 NK of the band's 256): [chunk][staged column] with chunk = the 16-row
+// block of one half-wavefront (8 per 128-row tile).  One padding entry per
+// chunk row spreads the write-out reads over the LDS banks.
+template <int NK>
+struct ColStageT {
+  uint2 codes[8][32 * NK + 1];
+  uint8_t scales[8][32 * NK + 4];
 };
+using ColStage = ColStageT<8>;
+
+// RTNE onto E1M2/INT4/E2M1C has an exact fast form; it needs no clamp when
+// the block scale is a normal E4M3 value (then |y| <= 1.0625 Qmax) and the
+// tensor maximum is the tensor's own (otherwise it clamps to +-Qmax).
+template <int GRID, bool SR>
+struct GridTraits {
+  static constexpr bool kFast = !SR && GRID != kGridE2M1;      // uniform grids
+  static constexpr float kMul = GRID == kGridINT4 ? 1.0f : 2.0f;  // grid step -> integer
+  static constexpr float kTop = (float)grid_top<GRID>();          // clamp, in grid steps
+};
+
+// Row-wise pass over the lane's 16 rows, NR row blocks per step (4, or 2
+// where registers are short): values, block scales, one wavefront vote,
+// round, pack, store.  src(i, v)
+// writes the lane's 8 transformed values of row i (before the transform's
+// final 1/4; the row's own values without the transform) to v and returns
+// the largest magnitude of the 16-element block (over the lane pair).  fin
+// is the lane's output multiplier (the 1/4 and the folded sign).  Returns the
+// largest block maximum seen (for DELAYED).
+template <int GRID, bool SR, bool MX, bool RHT, bool DELAYED, int NR = 4, typename RowSrc>
+__device__ __forceinline__ float row_pass(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
+                                          const TensorScale& tsr, const float* lut_l, float fin,
+                                          RowSrc&& src) {
+  using G = GridTraits<GRID, SR>;
+  float tile_r = 0.0f;
+  const bool fast_r = __builtin_amdgcn_readfirstlane((int)tsr.fast) != 0;
+  const int parity = L.lc & 1;
+  const int64_t C = p.cols;
+  const int64_t tile_row0 = T.seg_row0 + T.m0;
+  const uint32_t lrow = (uint32_t)(32 * L.wave + 16 * L.half);  // lane's first row in the tile
+  const int B = MX ? 32 : 16;
+  uint8_t* rc_base = p.row_codes + tile_row0 * (C / 2) + (int64_t)T.band * (kBandCols / 2);
+  uint8_t* rsc_base = p.row_scales + tile_row0 * (C / B) + (int64_t)T.band * (kBandCols / B);
+  const uint32_t rc_stride = (uint32_t)(C / 2), rsc_stride = (uint32_t)(C / B);
+#pragma clang loop unroll(full)
+  for (int g4 = 0; g4 < 16 / NR; ++g4) {
+    float v[NR][8];
+    float raw[NR], inv[NR];
+    uint32_t sbyte[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      float m = src(NR * g4 + r, v[r]);
+      if (MX) m = fmaxf(m, dpp_xor2(m));
+      raw[r] = m;
+    }
+    const bool ok = block_scales<GRID, MX, RHT, NR, DELAYED>(raw, tsr, fast_r, lut_l, sbyte, inv);
+    if (DELAYED) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) tile_r = fmaxf(tile_r, raw[r]);
+    }
+    uint32_t packed[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) packed[r] = 0u;
+    if (G::kFast && ok) {
+      // t = y / (grid step) as one product: an exact power-of-two rescaling
+      // of fl(fl(v/4) * inv_b) for every element whose code can be nonzero
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float mult = inv[r] * (fin * G::kMul);
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float t = v[r][j] * mult;
+          if (MX || DELAYED) t = __builtin_amdgcn_fmed3f(t, -G::kTop, G::kTop);
+          acc = push_nibble(__float_as_uint(t + kMagic), acc);
+        }
+        packed[r] = GRID == kGridINT4 ? acc : tc_to_signmag8(acc);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int i = NR * g4 + r;
+        if (SR) {
+          const uint64_t base = (uint64_t)(T.seg_row0 + L.m_h0 + i) * (uint64_t)C + (uint64_t)L.c0;
+          const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
+          const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
+          packed[r] = quantize_code<GRID, SR>((v[r][0] * fin) * inv[r], r0.x) |
+                      (quantize_code<GRID, SR>((v[r][1] * fin) * inv[r], r0.y) << 4) |
+                      (quantize_code<GRID, SR>((v[r][2] * fin) * inv[r], r0.z) << 8) |
+                      (quantize_code<GRID, SR>((v[r][3] * fin) * inv[r], r0.w) << 12) |
+                      (quantize_code<GRID, SR>((v[r][4] * fin) * inv[r], r1.x) << 16) |
+                      (quantize_code<GRID, SR>((v[r][5] * fin) * inv[r], r1.y) << 20) |
+                      (quantize_code<GRID, SR>((v[r][6] * fin) * inv[r], r1.z) << 24) |
+                      (quantize_code<GRID, SR>((v[r][7] * fin) * inv[r], r1.w) << 28);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            packed[r] |= quantize_code<GRID, false>((v[r][j] * fin) * inv[r], 0u) << (4 * j);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int i = NR * g4 + r;
+      if (L.lane_ok && L.m_h0 + i < T.M) {
+        const uint32_t li = lrow + (uint32_t)i;
+        __builtin_nontemporal_store(packed[r], reinterpret_cast<uint32_t*>(rc_base + (li * rc_stride + 4u * (uint32_t)L.lc)));
+        if (MX) {
+          if ((L.lc & 3) == 0) rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 2)] = (uint8_t)sbyte[r];
+        } else if (parity == 0) {
+          rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 1)] = (uint8_t)sbyte[r];
+        }
+      }
+    }
+  }
+  return tile_r;
+}
+
+// Column-wise pass over the lane's columns K0 .. K0+NK-1 (of its 8), two
+// column blocks per step, then the write-out.  src(k, v) writes the lane's
+// 16 transformed values of its column k (before the final 1/4) to v and
+// returns their largest magnitude.  Codes and scales go to LDS first (chunk
+// = one half-wavefront's 16 rows), then leave as contiguous 8-byte code runs
+// and byte runs per output line, instead of one scattered store per lane and
+// column.  The staging area is read by the write-out after a barrier; a
+// caller that reuses it must synchronize first.  Returns the largest block
+// maximum seen (for DELAYED).
+template <int GRID, bool SR, bool MX, bool RHT, bool DELAYED, int K0 = 0, int NK = 8, typename ColSrc>
+__device__ __forceinline__ float col_pass(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
+                                          const TensorScale& tsc, const float* lut_l, ColStageT<NK>& cst,
+                                          ColSrc&& src) {
+  static_assert(K0 % 2 == 0 && NK % 2 == 0 && K0 + NK <= 8, "whole column pairs of the lane");
+  using G = GridTraits<GRID, SR>;
+  float tile_c = 0.0f;
+  const bool fast_c = __builtin_amdgcn_readfirstlane((int)tsc.fast) != 0;
+  const float fin = RHT ? p.sg.fin : 1.0f;
+  const int ch = 2 * L.wave + L.half;  // chunk of this half-wavefront
+#pragma clang loop unroll(full)
+  for (int g2 = K0 / 2; g2 < (K0 + NK) / 2; ++g2) {
+    float v[2][16];
+    float raw[2], inv[2];
+    uint32_t sbyte[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float m = src(2 * g2 + r, v[r]);
+      if (MX) m = fmaxf(m, __shfl_xor(m, 32));
+      raw[r] = m;
+    }
+    const bool ok = block_scales<GRID, MX, RHT, 2, DELAYED>(raw, tsc, fast_c, lut_l, sbyte, inv);
+    if (DELAYED) tile_c = fmaxf(tile_c, fmaxf(raw[0], raw[1]));
+    uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+    if (G::kFast && ok) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float mult = inv[r] * (fin * G::kMul);
+        uint32_t a0 = 0u, a1 = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float t0 = v[r][j] * mult, t1 = v[r][8 + j] * mult;
+          if (MX || DELAYED) {
+            t0 = __builtin_amdgcn_fmed3f(t0, -G::kTop, G::kTop);
+            t1 = __builtin_amdgcn_fmed3f(t1, -G::kTop, G::kTop);
+          }
+          a0 = push_nibble(__float_as_uint(t0 + kMagic), a0);
+          a1 = push_nibble(__float_as_uint(t1 + kMagic), a1);
+        }
+        lo[r] = GRID == kGridINT4 ? a0 : tc_to_signmag8(a0);
+        hi[r] = GRID == kGridINT4 ? a1 : tc_to_signmag8(a1);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (SR) {
+          const int64_t cglob = L.c0 + 2 * g2 + r;
+          const uint64_t base = (uint64_t)cglob * (uint64_t)p.padded_rows + (uint64_t)(T.coff + L.m_h0);
+          uint32_t word[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const Ctr4 rr = sr_words4((base >> 2) + q, 1u, p.sr_k0, p.sr_k1);
+            word[q] = quantize_code<GRID, SR>((v[r][4 * q + 0] * fin) * inv[r], rr.x) |
+                      (quantize_code<GRID, SR>((v[r][4 * q + 1] * fin) * inv[r], rr.y) << 4) |
+                      (quantize_code<GRID, SR>((v[r][4 * q + 2] * fin) * inv[r], rr.z) << 8) |
+                      (quantize_code<GRID, SR>((v[r][4 * q + 3] * fin) * inv[r], rr.w) << 12);
+          }
+          lo[r] = word[0] | (word[1] << 16);
+          hi[r] = word[2] | (word[3] << 16);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            lo[r] |= quantize_code<GRID, false>((v[r][j] * fin) * inv[r], 0u) << (4 * j);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            hi[r] |= quantize_code<GRID, false>((v[r][8 + j] * fin) * inv[r], 0u) << (4 * j);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int sc = NK * L.lc + 2 * g2 + r - K0;  // staged column
+      cst.codes[ch][sc] = make_uint2(lo[r], hi[r]);
+      cst.scales[ch][sc] = (uint8_t)sbyte[r];
+    }
+  }
+  __syncthreads();
+  // write-out: 8 threads per output line (column), one 8-byte code run each;
+  // staged column sc is band column 8 (sc / NK) + K0 + sc % NK
+  const int64_t Rp = p.padded_rows;
+  const int B = MX ? 32 : 16;
+  const int64_t band_c0 = (int64_t)T.band * kBandCols;
+  const int64_t ncols = p.cols - band_c0 < kBandCols ? p.cols - band_c0 : kBandCols;
+  const int64_t rows_here = T.P - T.m0;
+  const int nch = rows_here >= kTileRows ? 8 : (int)(rows_here / 16);  // chunks that exist
+  uint8_t* cc = p.col_codes + band_c0 * (Rp / 2) + (T.coff + T.m0) / 2;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int q = threadIdx.x + j * kThreads;
+    const int sc = q >> 3, chq = q & 7;
+    const int col = 8 * (sc / NK) + K0 + sc % NK;
+    if (col < ncols && chq < nch) {
+      const uint2 cw = cst.codes[chq][sc];
+      const u32x2 cv2 = {cw.x, cw.y};
+      __builtin_nontemporal_store(cv2, reinterpret_cast<u32x2*>(cc + (int64_t)col * (Rp / 2) + 8 * chq));
+    }
+  }
+  uint8_t* cs = p.col_scales + band_c0 * (Rp / B) + (T.coff + T.m0) / B;
+  const int nsc = MX ? nch / 2 : nch;  // scale bytes per line in this tile
+  constexpr int per = MX ? 4 : 8;
+#pragma unroll
+  for (int j = 0; j < NK * per / 8; ++j) {
+    const int q = threadIdx.x + j * kThreads;
+    const int sc = q / per, b = q % per;
+    const int col = 8 * (sc / NK) + K0 + sc % NK;
+    if (col < ncols && b < nsc) cs[(int64_t)col * (Rp / B) + b] = cst.scales[MX ? 2 * b : b][sc];
+  }
+  return tile_c;
+}
 
 // Quantize one tile whose rows are loaded (or in flight, in load order) in
 // w, given the per-tensor scales of the two layouts and their inverse
 // block-factor tables: row-wise codes and scales straight to memory,
-// column-wise ones through the LDS staging area.  KEEP: the rows are
-// unpacked once and kept unpacked for the column-wise pass (fewer
-// instructions); otherwise they are unpacked again there (fewer registers).
+// column-wise ones through the LDS staging area.  Both transforms are
+// computed here.  KEEP: the rows are unpacked once and kept unpacked for the
+// column-wise pass (fewer instructions); otherwise they are unpacked again
+// there (fewer registers).
 template <int GRID, bool SR, bool MX, bool RHT, bool KEEP = true, bool DELAYED = false>
 __device__ __forceinline__ float2 quant_tile(const QuantParams& p, const TileInfo& T, const LaneGeom& L,
                                              const uint32_t (&w)[16][4], const TensorScale& tsr,
@@ -495,7 +725,6 @@ __device__ __forceinline__ float2 quant_tile(const QuantParams& p, const TileInf
   // exceed them; scales and codes saturate, and the lane's largest block
   // maxima (before the final 1/4) are returned for the next call.
   float tile_r = 0.0f, tile_c = 0.0f;
-
   // The sub-tile is unpacked once (row by row, in load order, inside the
   // row-wise pass) and kept for the column-wise pass.
   float xf[16][8];
@@ -509,221 +738,39 @@ __device__ __forceinline__ float2 quant_tile(const QuantParams& p, const TileInf
       }
     }
   }
-  // wave-uniform (scalar) copies of the per-tensor fast-path conditions
-  const bool fast_r = __builtin_amdgcn_readfirstlane((int)tsr.fast) != 0;
-  const bool fast_c = __builtin_amdgcn_readfirstlane((int)tsc.fast) != 0;
-  const int parity = L.lc & 1;
-  const RowLaneSigns rs = row_lane_signs<RHT>(p, parity);
-  const int64_t C = p.cols;
-  // RTNE onto E1M2/INT4 has an exact fast form; it needs no clamp when the
-  // block scale is a normal E4M3 value (then |y| <= 1.0625 Qmax) and the
-  // tensor maximum is the tensor's own (otherwise it clamps to +-Qmax).
-  constexpr bool kFastGrid = !SR && GRID != kGridE2M1;  // uniform grids
-  constexpr float kGridMul = GRID == kGridINT4 ? 1.0f : 2.0f;  // grid step -> integer
-  constexpr float kTop = (float)grid_top<GRID>();              // MX32 clamp, in grid steps
-  // Addresses: a uniform tile base plus a 32-bit per-lane offset.
-  const int64_t tile_row0 = T.seg_row0 + T.m0;
-  const uint32_t lrow = (uint32_t)(32 * L.wave + 16 * L.half);  // lane's first row in the tile
-
+  const RowLaneSigns rs = row_lane_signs<RHT>(p, L.lc & 1);
   if (p.do_row) {
-    const int B = MX ? 32 : 16;
-    uint8_t* rc_base = p.row_codes + tile_row0 * (C / 2) + (int64_t)T.band * (kBandCols / 2);
-    uint8_t* rsc_base = p.row_scales + tile_row0 * (C / B) + (int64_t)T.band * (kBandCols / B);
-    const uint32_t rc_stride = (uint32_t)(C / 2), rsc_stride = (uint32_t)(C / B);
-#pragma clang loop unroll(full)
-    for (int g4 = 0; g4 < 4; ++g4) {
-      // four independent row blocks per step: transform, scale, vote, round
-      float v[4][8];
-      float raw[4], inv[4];
-      uint32_t sbyte[4];
+    tile_r = row_pass<GRID, SR, MX, RHT, DELAYED>(
+        p, T, L, tsr, lut[0], rs.fin, [&](int i, float(&v)[8]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * g4 + r;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          xf[i][2 * k] = bf_lo(w[i][k]);
-          xf[i][2 * k + 1] = bf_hi(w[i][k]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[r][j] = xf[i][j];  // (without KEEP, xf is dead beyond this row)
-        if (RHT) {
-          fwht8_half(v[r], rs.h);
-          cross_stage8(v[r], rs.s4);
-        }
-        float m = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[r][j]));
-        m = fmaxf(m, dpp_xor1(m));
-        if (MX) m = fmaxf(m, dpp_xor2(m));
-        raw[r] = m;
-      }
-      const bool ok = block_scales<GRID, MX, RHT, 4, DELAYED>(raw, tsr, fast_r, lut[0], sbyte, inv);
-      if (DELAYED) tile_r = fmaxf(tile_r, fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])));
-      uint32_t packed[4] = {0u, 0u, 0u, 0u};
-      if (kFastGrid && ok) {
-        // t = y / (grid step) as one product: an exact power-of-two rescaling
-        // of fl(fl(v/4) * inv_b) for every element whose code can be nonzero
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float mult = inv[r] * (rs.fin * kGridMul);
-          uint32_t acc = 0u;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float t = v[r][j] * mult;
-            if (MX || DELAYED) t = __builtin_amdgcn_fmed3f(t, -kTop, kTop);
-            acc = push_nibble(__float_as_uint(t + kMagic), acc);
+          for (int k = 0; k < 4; ++k) {
+            xf[i][2 * k] = bf_lo(w[i][k]);
+            xf[i][2 * k + 1] = bf_hi(w[i][k]);
           }
-          packed[r] = GRID == kGridINT4 ? acc : tc_to_signmag8(acc);
-        }
-      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * g4 + r;
-          const float f = rs.fin;
-          if (SR) {
-            const uint64_t base = (uint64_t)(T.seg_row0 + L.m_h0 + i) * (uint64_t)C + (uint64_t)L.c0;
-            const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
-            const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
-            packed[r] = quantize_code<GRID, SR>((v[r][0] * f) * inv[r], r0.x) |
-                        (quantize_code<GRID, SR>((v[r][1] * f) * inv[r], r0.y) << 4) |
-                        (quantize_code<GRID, SR>((v[r][2] * f) * inv[r], r0.z) << 8) |
-                        (quantize_code<GRID, SR>((v[r][3] * f) * inv[r], r0.w) << 12) |
-                        (quantize_code<GRID, SR>((v[r][4] * f) * inv[r], r1.x) << 16) |
-                        (quantize_code<GRID, SR>((v[r][5] * f) * inv[r], r1.y) << 20) |
-                        (quantize_code<GRID, SR>((v[r][6] * f) * inv[r], r1.z) << 24) |
-                        (quantize_code<GRID, SR>((v[r][7] * f) * inv[r], r1.w) << 28);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              packed[r] |= quantize_code<GRID, false>((v[r][j] * f) * inv[r], 0u) << (4 * j);
+          for (int j = 0; j < 8; ++j) v[j] = xf[i][j];  // (without KEEP, xf is dead beyond this row)
+          if (RHT) {
+            fwht8_half(v, rs.h);
+            cross_stage8(v, rs.s4);
           }
-        }
-      }
+          float m = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * g4 + r;
-        if (L.lane_ok && L.m_h0 + i < T.M) {
-          const uint32_t li = lrow + (uint32_t)i;
-          __builtin_nontemporal_store(packed[r], reinterpret_cast<uint32_t*>(rc_base + (li * rc_stride + 4u * (uint32_t)L.lc)));
-          if (MX) {
-            if ((L.lc & 3) == 0) rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 2)] = (uint8_t)sbyte[r];
-          } else if (parity == 0) {
-            rsc_base[li * rsc_stride + ((uint32_t)L.lc >> 1)] = (uint8_t)sbyte[r];
-          }
-        }
-      }
-    }
+          for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+          return fmaxf(m, dpp_xor1(m));
+        });
   }
-
   if (p.do_col) {
-    // Column-wise blocks: codes and scales go to LDS first (chunk = one
-    // half-wavefront's 16 rows), then leave as contiguous 8-byte code runs
-    // and byte runs per output line, instead of one scattered store per
-    // lane and column.
-    const float fin = RHT ? p.sg.fin : 1.0f;
-    const int ch = 2 * L.wave + L.half;  // chunk of this half-wavefront
-#pragma clang loop unroll(full)
-    for (int g2 = 0; g2 < 4; ++g2) {
-      // two independent column blocks per step
-      float v[2][16];
-      float raw[2], inv[2];
-      uint32_t sbyte[2];
+    tile_c = col_pass<GRID, SR, MX, RHT, DELAYED>(
+        p, T, L, tsc, lut[1], cst, [&](int k, float(&v)[16]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int k = 2 * g2 + r;
+          for (int i = 0; i < 16; ++i)
+            v[i] = KEEP ? xf[i][k] : ((k & 1) ? bf_hi(w[i][k >> 1]) : bf_lo(w[i][k >> 1]));
+          if (RHT) fwht16_inlane(v, p.sg);
+          float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[r][i] = KEEP ? xf[i][k] : ((k & 1) ? bf_hi(w[i][k >> 1]) : bf_lo(w[i][k >> 1]));
-        if (RHT) fwht16_inlane(v[r], p.sg);
-        float m = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[r][j]));
-        if (MX) m = fmaxf(m, __shfl_xor(m, 32));
-        raw[r] = m;
-      }
-      const bool ok = block_scales<GRID, MX, RHT, 2, DELAYED>(raw, tsc, fast_c, lut[1], sbyte, inv);
-      if (DELAYED) tile_c = fmaxf(tile_c, fmaxf(raw[0], raw[1]));
-      uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
-      if (kFastGrid && ok) {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const float mult = inv[r] * (fin * kGridMul);
-          uint32_t a0 = 0u, a1 = 0u;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float t0 = v[r][j] * mult, t1 = v[r][8 + j] * mult;
-            if (MX || DELAYED) {
-              t0 = __builtin_amdgcn_fmed3f(t0, -kTop, kTop);
-              t1 = __builtin_amdgcn_fmed3f(t1, -kTop, kTop);
-            }
-            a0 = push_nibble(__float_as_uint(t0 + kMagic), a0);
-            a1 = push_nibble(__float_as_uint(t1 + kMagic), a1);
-          }
-          lo[r] = GRID == kGridINT4 ? a0 : tc_to_signmag8(a0);
-          hi[r] = GRID == kGridINT4 ? a1 : tc_to_signmag8(a1);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          if (SR) {
-            const int64_t cglob = L.c0 + 2 * g2 + r;
-            const uint64_t base =
-                (uint64_t)cglob * (uint64_t)p.padded_rows + (uint64_t)(T.coff + L.m_h0);
-            uint32_t word[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const Ctr4 rr = sr_words4((base >> 2) + q, 1u, p.sr_k0, p.sr_k1);
-              word[q] = quantize_code<GRID, SR>((v[r][4 * q + 0] * fin) * inv[r], rr.x) |
-                        (quantize_code<GRID, SR>((v[r][4 * q + 1] * fin) * inv[r], rr.y) << 4) |
-                        (quantize_code<GRID, SR>((v[r][4 * q + 2] * fin) * inv[r], rr.z) << 8) |
-                        (quantize_code<GRID, SR>((v[r][4 * q + 3] * fin) * inv[r], rr.w) << 12);
-            }
-            lo[r] = word[0] | (word[1] << 16);
-            hi[r] = word[2] | (word[3] << 16);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              lo[r] |= quantize_code<GRID, false>((v[r][j] * fin) * inv[r], 0u) << (4 * j);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              hi[r] |= quantize_code<GRID, false>((v[r][8 + j] * fin) * inv[r], 0u) << (4 * j);
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int col = 8 * L.lc + 2 * g2 + r;  // column within the band
-        cst.codes[ch][col] = make_uint2(lo[r], hi[r]);
-        cst.scales[ch][col] = (uint8_t)sbyte[r];
-      }
-    }
-    __syncthreads();
-    // write-out: 8 threads per output line (column), one 8-byte code run each
-    const int64_t Rp = p.padded_rows;
-    const int B = MX ? 32 : 16;
-    const int64_t band_c0 = (int64_t)T.band * kBandCols;
-    const int64_t ncols = p.cols - band_c0 < kBandCols ? p.cols - band_c0 : kBandCols;
-    const int64_t rows_here = T.P - T.m0;
-    const int nch = rows_here >= kTileRows ? 8 : (int)(rows_here / 16);  // chunks that exist
-    uint8_t* cc = p.col_codes + band_c0 * (Rp / 2) + (T.coff + T.m0) / 2;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = threadIdx.x + j * kThreads;
-      const int col = q >> 3, chq = q & 7;
-      if (col < ncols && chq < nch) {
-        const uint2 cw = cst.codes[chq][col];
-        const u32x2 cv2 = {cw.x, cw.y};
-        __builtin_nontemporal_store(cv2, reinterpret_cast<u32x2*>(cc + (int64_t)col * (Rp / 2) + 8 * chq));
-      }
-    }
-    uint8_t* cs = p.col_scales + band_c0 * (Rp / B) + (T.coff + T.m0) / B;
-    const int nsc = MX ? nch / 2 : nch;  // scale bytes per line in this tile
-    const int per = MX ? 4 : 8;
-#pragma unroll
-    for (int j = 0; j < (MX ? 4 : 8); ++j) {
-      const int q = threadIdx.x + j * kThreads;
-      const int col = q / per, b = q % per;
-      if (col < ncols && b < nsc) cs[(int64_t)col * (Rp / B) + b] = cst.scales[MX ? 2 * b : b][col];
-    }
+          for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
+          return m;
+        });
   }
   return make_float2(tile_r, tile_c);
 }
@@ -923,7 +970,17 @@ __global__ __launch_bounds__(kThreads) void ufp4_delayed_kernel(QuantParams p) {
 // always finds every tile started, so at least one stays.
 constexpr uint64_t kGraceTicks = 10000;      // 100 us of the 100 MHz real-time counter
 constexpr uint64_t kStuckTicks = 200000000;  // 2 s: only a device fault gets here
-constexpr int kWatch = kMaxFusedTiles / kThreads;  // tiles watched per thread
+constexpr int kWatch = kMaxFusedTiles / kThreads;  // start words read per thread
+constexpr int kAggregators = 8;             // workgroups that read every tile's maxima
+constexpr int kResCopies = 64;              // copies of the aggregators' results line
+static_assert(kResCopies <= kThreads && 2 * kAggregators * sizeof(uint64_t) == 128 &&
+                  (size_t)kResCopies * 2 * kAggregators <= 64 * 16,
+              "one results line per copy, written by one thread each, inside the workspace");
+constexpr uint64_t kFallbackTicks = 3000;   // 30 us without an aggregator's answer
+constexpr int kPollBase = 64;                         // the pollers: waves 1..3
+constexpr int kPollers = kThreads - kPollBase;
+constexpr int kPollWatch = (kMaxFusedTiles + kPollers - 1) / kPollers;  // tiles watched per poller
+static_assert(kThreads == 256 && kMaxFusedTiles % 64 == 0, "left-mask words from the pollers' ballots");
 
 __device__ __forceinline__ uint64_t ld_agent(uint64_t* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -951,116 +1008,226 @@ __device__ __forceinline__ void tensor_setup(float r, float c, float qmax, Tenso
   __syncthreads();
 }
 
-// LDS of the single-pass kernel: the tile's raw rows, kept from phase A to
-// phase B (register room goes to phase A's column butterflies), share their
-// space with the column-wise staging area, which is used only after the rows
-// are back in registers.
-constexpr size_t kFusedTileLds = 16 * kThreads * sizeof(uint4);
-static_assert(sizeof(ColStage) <= kFusedTileLds, "staging area fits the tile buffer");
+// State of one workgroup's part in a single-pass exchange.
+//
+// A call's words carry its generation tag (the workspace's generation word
+// + 1), so words left by earlier calls are never taken for this call's.
+// Each workgroup marks its start in its tile's start words (kFsReplicas
+// copies: every workgroup reads all of them once, and a copy per group of
+// readers keeps any one memory line from having all of them as readers),
+// and after phase A publishes its tile maxima in its tile's pair of words.
+// The last kAggregators tiles' workgroups ("aggregators") read every tile's
+// pair and publish the tensor maxima in a result pair of their own, written
+// into every one of kResCopies copies of the results line; every other
+// workgroup reads only its own copy.  (Many workgroups reading the same
+// memory lines while they are written delays every one of those accesses
+// by microseconds.)  When some tile was left, or
+// no aggregator has answered within kFallbackTicks (an aggregator left its
+// tile), a workgroup reads every tile's pair itself.
+struct Exchange {
+  uint64_t t_begin;
+  uint32_t tag;      // this call's generation (never 0)
+  int32_t n;         // tiles of the call
+  uint64_t* w_start; // [kFsReplicas][n] start words
+  uint64_t* w_max;   // [n][2] the tile's row-wise maximum (bit 31 of the value: tile
+                     // left) and column-wise maximum, side by side
+  uint64_t* w_res;   // [kResCopies][kAggregators][2]: the aggregators' result pairs
+                     // (row-wise maximum, bit 31: some tile left; column-wise), in
+                     // kResCopies copies of one 128-byte line each
+  int32_t rep;       // the copy of the start words this workgroup reads
+  int32_t agg;       // this workgroup's aggregator index, or -1
+  int32_t copy;      // the copy of the results line this workgroup reads
+};
 
-template <int GRID, bool SR, bool RHT>
-__global__ __launch_bounds__(kThreads, 2) void ufp4_fused_kernel(QuantParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t big[kFusedTileLds];
-  __shared__ float lut[2][128];
-  __shared__ float red[2][kThreads / 64];
-  __shared__ uint64_t left_mask[kMaxFusedTiles / 64];
-  __shared__ int32_t pick;
-  uint4 (&wl)[16][kThreads] = *reinterpret_cast<uint4 (*)[16][kThreads]>(big);
-  ColStage& cst = *reinterpret_cast<ColStage*>(big);
-  const TileInfo T = dense_tile(p, remap_xcd((int32_t)blockIdx.x, (int32_t)gridDim.x));
-  if (!T.active) return;  // uniform per workgroup; owns no tile
-  const uint64_t t_begin = rt_now();
-  const int32_t n = p.n_work;
-  uint64_t* const w_start = p.fs_words;
-  uint64_t* const w_row = w_start + n;
-  uint64_t* const w_col = w_row + n;
-  uint32_t tag = __hip_atomic_load(p.fs_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  tag = tag ? tag : 1u;
-  if (threadIdx.x == 0) {
-    st_agent(&w_start[T.work], tag);
-    // a new call starts with a clean status (a failed earlier call left 7)
-    if (T.work == 0 && p.ws_status) __hip_atomic_store(p.ws_status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  const LaneGeom L = lane_geom(p, T);
-  uint32_t w[16][4];
-  load_rows<0, 16, true>(p, T, L, w);
+// Start of a single-pass call: the call's generation and the tile's start
+// words.  The first tile also clears a failure status an earlier call left.
+__device__ __forceinline__ Exchange exchange_begin(const QuantParams& p, const TileInfo& T) {
+  Exchange X;
+  X.t_begin = rt_now();
+  X.n = p.n_work;
+  X.w_start = p.fs_words;
+  X.w_max = X.w_start + (size_t)kFsReplicas * kMaxFusedTiles;
+  X.w_res = X.w_max + 2 * (size_t)kMaxFusedTiles;
+  X.rep = T.work % kFsReplicas;
+  X.agg = T.work >= X.n - kAggregators ? X.n - 1 - T.work : -1;
+  X.copy = T.work % kResCopies;
+  const uint32_t tag = __hip_atomic_load(p.fs_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  X.tag = tag ? tag : 1u;
+  if (threadIdx.x < kFsReplicas) st_agent(&X.w_start[threadIdx.x * X.n + T.work], X.tag);
+  if (threadIdx.x == 0 && T.work == 0 && p.ws_status)
+    __hip_atomic_store(p.ws_status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return X;
+}
 
-  // Phase A on the tile; the start words are read half-way through, when
-  // every workgroup that can start has long since written its own.
-  uint32_t sw[kWatch];
-  const float2 m = tile_amax<RHT>(p, L, w, red, [&] {
+// Every tile's start word, kWatch tiles per thread (read half-way through
+// phase A, when every workgroup that can start has long since written its
+// own).  The loads are unconditional (a clamped index, the result selected
+// afterwards): a load under a branch would make the compiler wait there for
+// every load in flight, the tile's rows included.
+__device__ __forceinline__ void exchange_read_starts(const Exchange& X, uint32_t (&sw)[kWatch]) {
 #pragma unroll
-    for (int k = 0; k < kWatch; ++k) {
-      const int32_t i = (int32_t)threadIdx.x + k * kThreads;
-      sw[k] = i < n ? ld_tag(&w_start[i]) : tag;
+  for (int k = 0; k < kWatch; ++k) {
+    const int32_t i = (int32_t)threadIdx.x + k * kThreads;
+    const uint32_t t = ld_tag(&X.w_start[X.rep * X.n + (i < X.n ? i : 0)]);
+    sw[k] = i < X.n ? t : X.tag;
+  }
+}
+
+// The exchange did not complete within kStuckTicks (only a device fault
+// gets here): report it and advance the generation, so that the next call
+// on this workspace never takes this call's words for its own.
+__device__ __forceinline__ void exchange_abort(const QuantParams& p, const Exchange& X) {
+  if (threadIdx.x == 0) {
+    if (p.ws_status) __hip_atomic_store(p.ws_status, 7u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.fs_gen, X.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Waves 1..3 read every tile's pair of words until each carries this call's
+// generation (wave 0 published: its loads would wait for its stores to
+// complete).  A round re-reads only the tiles not seen yet, all of its loads
+// issued before any of their results is used (a load under a per-lane
+// branch would be waited for on its own).  Each poller accumulates the
+// maxima of its tiles and their left bits (lbits bit k: tile
+// pt + k kPollers).  False if stuck (the caller exits).
+__device__ __forceinline__ bool poll_all_tiles(const QuantParams& p, const Exchange& X, float& r, float& c,
+                                               uint32_t& lbits) {
+  const int32_t n = X.n;
+  const int32_t pt = (int32_t)threadIdx.x - kPollBase;  // poller index (negative in wave 0)
+  uint32_t need = 0u;
+#pragma unroll
+  for (int k = 0; k < kPollWatch; ++k)
+    if (pt >= 0 && pt + k * kPollers < n) need |= 1u << k;
+  constexpr int kBatch = 3;  // tiles whose words are in flight at once (registers are short)
+  for (;;) {
+#pragma unroll
+    for (int k0 = 0; k0 < kPollWatch; k0 += kBatch) {
+      uint64_t a[kBatch], b[kBatch];
+#pragma unroll
+      for (int k = k0; k < k0 + kBatch && k < kPollWatch; ++k) {
+        a[k - k0] = 0u;
+        b[k - k0] = 0u;
+        if (need & (1u << k)) {
+          const int32_t i = pt + k * kPollers;
+          a[k - k0] = ld_agent(&X.w_max[2 * i]);
+          b[k - k0] = ld_agent(&X.w_max[2 * i + 1]);
+        }
+      }
+#pragma unroll
+      for (int k = k0; k < k0 + kBatch && k < kPollWatch; ++k) {
+        if ((need & (1u << k)) && (uint32_t)a[k - k0] == X.tag && (uint32_t)b[k - k0] == X.tag) {
+          const uint32_t hi = (uint32_t)(a[k - k0] >> 32);
+          need &= ~(1u << k);
+          lbits |= (hi >> 31) << k;
+          r = fmaxf(r, __uint_as_float(hi & 0x7FFFFFFFu));
+          c = fmaxf(c, __uint_as_float((uint32_t)(b[k - k0] >> 32)));
+        }
+      }
     }
-  }, [&](int i) { wl[i][threadIdx.x] = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]); });
+    if (__syncthreads_and(need == 0u)) return true;
+    if (__syncthreads_or(rt_now() - X.t_begin > kStuckTicks)) {
+      exchange_abort(p, X);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Publish the tile maxima m (row-wise, column-wise; before the final 1/4)
+// and collect the tensor's.  Returns false when this workgroup leaves its
+// tile (some tile had not started within the grace period, or the host
+// forced it) or the exchange never completed (status 7); the workgroup then
+// exits.  On true, r and c hold the tensor maxima (the same in every lane),
+// any_left tells whether some tile was left and then left_mask marks them.
+__device__ __forceinline__ bool exchange_maxima(const QuantParams& p, const TileInfo& T, const Exchange& X,
+                                                const uint32_t (&sw)[kWatch], float2 m, float& r_out, float& c_out,
+                                                bool& any_left, uint64_t* left_mask, float (&red)[2][kThreads / 64]) {
+  __shared__ uint32_t found;
+  const int32_t n = X.n;
   bool ok = true;
 #pragma unroll
-  for (int k = 0; k < kWatch; ++k) ok = ok && sw[k] == tag;
+  for (int k = 0; k < kWatch; ++k) ok = ok && sw[k] == X.tag;
   bool all = __syncthreads_and(ok) != 0;
   bool left = p.fs_orphan_stride > 1 && T.work % p.fs_orphan_stride != 0;
+  // (the start-word polls issue all of a thread's loads back to back:
+  // clamped indexes, results selected afterwards)
+  const int nk = (n + kThreads - 1) / kThreads;  // watched tiles per thread (uniform)
   while (!all && !left) {
-    if (__syncthreads_or(rt_now() - t_begin > kGraceTicks)) {
+    if (__syncthreads_or(rt_now() - X.t_begin > kGraceTicks)) {
       left = true;
       break;
     }
     __builtin_amdgcn_s_sleep(2);
-    ok = true;
+    uint32_t t[kWatch];
 #pragma unroll
     for (int k = 0; k < kWatch; ++k) {
       const int32_t i = (int32_t)threadIdx.x + k * kThreads;
-      if (i < n && ld_tag(&w_start[i]) != tag) ok = false;
+      if (k < nk) t[k] = ld_tag(&X.w_start[X.rep * n + (i < n ? i : n - 1)]);
     }
+    ok = true;
+#pragma unroll
+    for (int k = 0; k < kWatch; ++k)
+      if (k < nk && (int32_t)threadIdx.x + k * kThreads < n && t[k] != X.tag) ok = false;
     all = __syncthreads_and(ok) != 0;
   }
   if (threadIdx.x == 0) {
-    st_agent(&w_col[T.work], (uint64_t)tag | ((uint64_t)__float_as_uint(m.y) << 32));
-    st_agent(&w_row[T.work], (uint64_t)tag | ((uint64_t)(__float_as_uint(m.x) | (left ? 0x80000000u : 0u)) << 32));
+    st_agent(&X.w_max[2 * T.work + 1], (uint64_t)X.tag | ((uint64_t)__float_as_uint(m.y) << 32));
+    st_agent(&X.w_max[2 * T.work],
+             (uint64_t)X.tag | ((uint64_t)(__float_as_uint(m.x) | (left ? 0x80000000u : 0u)) << 32));
   }
-  if (left) return;
+  if (left) return false;
 
-  // Exchange: every thread watches its tiles until both words of each carry
-  // this call's generation.
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float r = 0.0f, c = 0.0f;
-  uint32_t have = 0u, need = 0u, lbits = 0u;
-#pragma unroll
-  for (int k = 0; k < kWatch; ++k)
-    if ((int32_t)threadIdx.x + k * kThreads < n) need |= 1u << k;
-  for (;;) {
-#pragma unroll
-    for (int k = 0; k < kWatch; ++k) {
-      if ((need & ~have) & (1u << k)) {
-        const int32_t i = (int32_t)threadIdx.x + k * kThreads;
-        const uint64_t a = ld_agent(&w_row[i]), b = ld_agent(&w_col[i]);
-        if ((uint32_t)a == tag && (uint32_t)b == tag) {
-          const uint32_t hi = (uint32_t)(a >> 32);
-          have |= 1u << k;
-          lbits |= (hi >> 31) << k;
-          r = fmaxf(r, __uint_as_float(hi & 0x7FFFFFFFu));
-          c = fmaxf(c, __uint_as_float((uint32_t)(b >> 32)));
+  uint32_t lbits = 0u;
+  bool flat = X.agg >= 0;  // aggregators read every tile's words
+  if (!flat) {
+    // wave 1 reads the aggregators' results (lane a: aggregator a) until one
+    // carries this call's generation
+    const int na = n < kAggregators ? n : kAggregators;
+    const uint64_t t_wait = rt_now();
+    if (threadIdx.x == 0) found = 0u;
+    __syncthreads();
+    for (;;) {
+      if (wave == 1) {
+        uint64_t a = 0u, b = 0u;
+        if (lane < na) {
+          a = ld_agent(&X.w_res[2 * (kAggregators * X.copy + lane)]);
+          b = ld_agent(&X.w_res[2 * (kAggregators * X.copy + lane) + 1]);
+        }
+        const bool valid = lane < na && (uint32_t)a == X.tag && (uint32_t)b == X.tag;
+        const uint64_t vm = __ballot(valid);
+        if (vm) {
+          const int src = __builtin_ctzll(vm);
+          const uint32_t hi = (uint32_t)(__shfl(a, src) >> 32);
+          r = __uint_as_float(hi & 0x7FFFFFFFu);
+          c = __uint_as_float((uint32_t)(__shfl(b, src) >> 32));
+          if (lane == 0) found = (hi >> 31) ? 2u : 1u;  // 2: some tile was left
         }
       }
+      __syncthreads();
+      if (found) break;
+      if (__syncthreads_or(rt_now() - t_wait > kFallbackTicks)) break;  // (an aggregator left its tile)
+      __builtin_amdgcn_s_sleep(1);
     }
-    if (__syncthreads_and(have == need)) break;
-    if (__syncthreads_or(rt_now() - t_begin > kStuckTicks)) {
-      // report the failure and advance the generation, so that the next
-      // call on this workspace never takes this call's words for its own
-      if (threadIdx.x == 0) {
-        if (p.ws_status) __hip_atomic_store(p.ws_status, 7u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.fs_gen, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      return;
+    flat = found != 1u;  // no answer, or tiles were left: read every tile's words
+    if (flat) {
+      r = 0.0f;
+      c = 0.0f;
     }
-    __builtin_amdgcn_s_sleep(1);
   }
+  if (flat && !poll_all_tiles(p, X, r, c, lbits)) return false;
   r = wave_max(r);
   c = wave_max(c);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  any_left = flat && __syncthreads_or(lbits != 0u) != 0;
+  if (any_left && wave > 0) {
+    // poller p = 64 (wave - 1) + lane watches tiles p + 192 k: wave w's k-th
+    // ballot covers tiles 64 (w - 1 + 3 k) .. +63
 #pragma unroll
-  for (int k = 0; k < kWatch; ++k) {
-    const uint64_t bits = __ballot((lbits >> k) & 1u);
-    if (lane == 0) left_mask[k * (kThreads / 64) + wave] = bits;
+    for (int k = 0; k < kPollWatch; ++k) {
+      const uint64_t bits = __ballot((lbits >> k) & 1u);
+      if (lane == 0 && (wave - 1 + 3 * k) < kMaxFusedTiles / 64) left_mask[wave - 1 + 3 * k] = bits;
+    }
   }
   if (lane == 0) {
     red[0][wave] = r;
@@ -1072,45 +1239,54 @@ __global__ __launch_bounds__(kThreads, 2) void ufp4_fused_kernel(QuantParams p) 
     r = fmaxf(r, red[0][i]);
     c = fmaxf(c, red[1][i]);
   }
+  if (X.agg >= 0 && threadIdx.x < kResCopies) {
+    uint64_t* res = &X.w_res[2 * (kAggregators * threadIdx.x + X.agg)];
+    st_agent(&res[1], (uint64_t)X.tag | ((uint64_t)__float_as_uint(c) << 32));
+    st_agent(&res[0], (uint64_t)X.tag | ((uint64_t)(__float_as_uint(r) | (any_left ? 0x80000000u : 0u)) << 32));
+  }
   // the same in every lane: keep the tensor quantities in scalar registers
-  r = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r)));
-  c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));
-  constexpr float qmax = grid_qmax<GRID>();
-  TensorScale tsr, tsc;
-  tensor_setup<RHT>(r, c, qmax, tsr, tsc, lut);
-  // The workgroup's own tile first (already in registers); then the tiles
-  // that were left, the q-th (by index) going to the staying tile of rank
-  // q mod (number staying).
-  int32_t n_left = 0, below = 0;
-  for (int j = 0; j < (n + 63) / 64; ++j) {
+  r_out = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r)));
+  c_out = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));
+  return true;
+}
+
+// The number of tiles that were left and this tile's rank among the ones
+// that stay.  The staying tile of rank 0 (at least one tile always stays)
+// advances the generation word: every workgroup has read it by now, so one
+// writer suffices (stores from all workgroups to one word serialize at the
+// memory and hold up each writer's following stores by microseconds).
+__device__ __forceinline__ void exchange_ranks(const QuantParams& p, const TileInfo& T, const Exchange& X,
+                                               bool any_left, const uint64_t* left_mask, int32_t& n_left,
+                                               int32_t& q) {
+  n_left = 0;
+  int32_t below = 0;
+  for (int j = 0; any_left && j < (X.n + 63) / 64; ++j) {
     const uint64_t mk = left_mask[j];
     n_left += __popcll(mk);
     if (64 * j + 63 < T.work) below += __popcll(mk);
     else if (64 * j < T.work) below += __popcll(mk & ((1ull << (T.work - 64 * j)) - 1ull));
   }
-  const int32_t n_stay = n - n_left;
-  int32_t q = T.work - below;  // rank among the staying tiles
-  // Every workgroup has read the generation word by now, so one writer
-  // suffices: the staying tile of rank 0 (at least one tile always stays).
-  // (Stores from all workgroups to this one word serialize at the memory
-  // and hold up each writer's following stores by microseconds.)
-  if (threadIdx.x == 0 && q == 0) __hip_atomic_store(p.fs_gen, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint4 u = wl[i][threadIdx.x];
-      w[i][0] = u.x;
-      w[i][1] = u.y;
-      w[i][2] = u.z;
-      w[i][3] = u.w;
-    }
-    __syncthreads();  // the staging area reuses the rows' space
-    if (threadIdx.x == 0 && T.band == 0 && T.m0 == 0) {
-      if (p.do_row && p.row_ts) p.row_ts[0] = tsr.S;
-      if (p.do_col && p.col_ts) p.col_ts[0] = tsc.S;
-    }
-    quant_tile<GRID, SR, false, RHT>(p, T, L, w, tsr, tsc, lut, cst);
+  q = T.work - below;
+  if (threadIdx.x == 0 && q == 0) __hip_atomic_store(p.fs_gen, X.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Writes the per-tensor scales once per call (by the tile at the origin).
+__device__ __forceinline__ void write_tensor_scales(const QuantParams& p, const TileInfo& T, const TensorScale& tsr,
+                                                    const TensorScale& tsc) {
+  if (threadIdx.x == 0 && T.band == 0 && T.m0 == 0) {
+    if (p.do_row && p.row_ts) p.row_ts[0] = tsr.S;
+    if (p.do_col && p.col_ts) p.col_ts[0] = tsc.S;
   }
+}
+
+// The tiles that were left: the q-th (by index) goes to the staying tile of
+// rank q mod (number staying), which reloads and quantizes it.
+template <int GRID, bool SR, bool RHT>
+__device__ __forceinline__ void quantize_left_tiles(const QuantParams& p, const Exchange& X, const uint64_t* left_mask,
+                                                    int32_t n_left, int32_t q, const TensorScale& tsr,
+                                                    const TensorScale& tsc, const float (&lut)[2][128], ColStage& cst,
+                                                    int32_t& pick) {
+  const int32_t n = X.n, n_stay = n - n_left;
   for (; q < n_left; q += n_stay) {
     if (threadIdx.x == 0) {
       int32_t want = q, o = -1;
@@ -1137,12 +1313,221 @@ __global__ __launch_bounds__(kThreads, 2) void ufp4_fused_kernel(QuantParams p) 
     LU.m_h0 = U.m0 + 32 * LU.wave + 16 * LU.half;
     LU.c0 = (int64_t)U.band * kBandCols + 8 * LU.lc;
     LU.lane_ok = LU.c0 < p.cols;
+    uint32_t w[16][4];
     load_rows<0, 16, true>(p, U, LU, w);
-    if (threadIdx.x == 0 && U.band == 0 && U.m0 == 0) {
-      if (p.do_row && p.row_ts) p.row_ts[0] = tsr.S;
-      if (p.do_col && p.col_ts) p.col_ts[0] = tsc.S;
-    }
+    write_tensor_scales(p, U, tsr, tsc);
     quant_tile<GRID, SR, false, RHT, false>(p, U, LU, w, tsr, tsc, lut, cst);
+  }
+}
+
+// LDS of the one-kernel variants: the tile's raw rows, kept from phase A to
+// phase B, share their space with the column-wise staging area, which is
+// used only after the rows have been read back.
+constexpr size_t kFusedTileLds = 16 * kThreads * sizeof(uint4);
+static_assert(sizeof(ColStage) <= kFusedTileLds, "staging area fits the tile buffer");
+
+// The single pass for either layout alone: phase A's maxima, then both
+// transforms computed again from the rows kept in LDS.
+template <int GRID, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads, 2) void ufp4_fused_kernel(QuantParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t big[kFusedTileLds];
+  __shared__ float lut[2][128];
+  __shared__ float red[2][kThreads / 64];
+  __shared__ uint64_t left_mask[kMaxFusedTiles / 64];
+  __shared__ int32_t pick;
+  uint4 (&wl)[16][kThreads] = *reinterpret_cast<uint4 (*)[16][kThreads]>(big);
+  ColStage& cst = *reinterpret_cast<ColStage*>(big);
+  const TileInfo T = dense_tile(p, remap_xcd((int32_t)blockIdx.x, (int32_t)gridDim.x));
+  if (!T.active) return;  // uniform per workgroup; owns no tile
+  const Exchange X = exchange_begin(p, T);
+  const LaneGeom L = lane_geom(p, T);
+  uint32_t w[16][4];
+  load_rows<0, 16, true>(p, T, L, w);
+  uint32_t sw[kWatch];
+  const float2 m = tile_amax<RHT>(p, L, w, red, [&] { exchange_read_starts(X, sw); },
+                                  [&](int i) { wl[i][threadIdx.x] = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]); });
+  float r, c;
+  bool any_left;
+  if (!exchange_maxima(p, T, X, sw, m, r, c, any_left, left_mask, red)) return;
+  constexpr float qmax = grid_qmax<GRID>();
+  TensorScale tsr, tsc;
+  tensor_setup<RHT>(r, c, qmax, tsr, tsc, lut);
+  int32_t n_left, q;
+  exchange_ranks(p, T, X, any_left, left_mask, n_left, q);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint4 u = wl[i][threadIdx.x];
+    w[i][0] = u.x;
+    w[i][1] = u.y;
+    w[i][2] = u.z;
+    w[i][3] = u.w;
+  }
+  __syncthreads();  // the staging area reuses the rows' space
+  write_tensor_scales(p, T, tsr, tsc);
+  quant_tile<GRID, SR, false, RHT>(p, T, L, w, tsr, tsc, lut, cst);
+  quantize_left_tiles<GRID, SR, RHT>(p, X, left_mask, n_left, q, tsr, tsc, lut, cst, pick);
+}
+
+// Phase A of the row+column single pass.  As each row of the lane's 16 x 8
+// sub-tile arrives it is stored raw to LDS (wl, for phase B's row-wise
+// pass), its row-wise half blocks are transformed for their maxima only
+// (the last butterfly stage folds into the maximum, as in tile_amax), and
+// the column-wise butterflies advance one stage whenever the rows they pair
+// are present.  After the last row the column-wise blocks are completed and
+// KEPT: cv holds the lane's 8 transformed columns (before the final 1/4;
+// the raw columns without the transform), cmax their block maxima, rmax the
+// 16 row-wise block maxima (over the lane pair).  Returns the workgroup's
+// tile maxima (row-wise, column-wise) in every thread.
+template <bool RHT, typename Mid>
+__device__ __forceinline__ float2 tile_amax_keep(const QuantParams& p, const LaneGeom& L, const uint32_t (&w)[16][4],
+                                                 uint4 (&wl)[16][kThreads], float (&cv)[16][8], float (&rmax)[16],
+                                                 float (&cmax)[8], float (&red)[2][kThreads / 64], Mid&& mid) {
+  float acc_r = 0.0f, acc_c = 0.0f;
+  const RowLaneSigns rs = row_lane_signs<RHT>(p, L.lc & 1);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    wl[i][threadIdx.x] = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      cv[i][2 * k] = bf_lo(w[i][k]);
+      cv[i][2 * k + 1] = bf_hi(w[i][k]);
+    }
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = cv[i][j];
+    float mr = 0.0f;
+    if (RHT) {
+      fwht8_half(v, rs.h);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mr = lastpair_max(mr, v[j], dpp_xor1(v[j]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mr = fmaxf(mr, fabsf(v[j]));
+      mr = fmaxf(mr, dpp_xor1(mr));
+    }
+    rmax[i] = mr;
+    acc_r = fmaxf(acc_r, mr);
+    if (i == 8) mid();
+    if (RHT) {
+      if (i % 2 == 1) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bfly(cv[i - 1][c], cv[i][c], p.sg.q1[i / 2]);
+      }
+      if (i % 4 == 3) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          bfly(cv[i - 3][c], cv[i - 1][c], p.sg.q2[i / 4]);
+          bfly(cv[i - 2][c], cv[i][c], p.sg.q2[i / 4]);
+        }
+      }
+      if (i % 8 == 7) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) bfly(cv[i - 7 + j][c], cv[i - 3 + j][c], p.sg.q3[i / 8]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if (RHT) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bfly(cv[j][c], cv[j + 8][c], p.sg.q4);
+    }
+    float mc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mc = fmaxf(mc, fabsf(cv[i][c]));
+    cmax[c] = mc;
+    acc_c = fmaxf(acc_c, mc);
+  }
+  acc_r = wave_max(acc_r);
+  acc_c = wave_max(acc_c);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = acc_r;
+    red[1][threadIdx.x >> 6] = acc_c;
+  }
+  __syncthreads();
+  float r = red[0][0], c = red[1][0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) {
+    r = fmaxf(r, red[0][i]);
+    c = fmaxf(c, red[1][i]);
+  }
+  return make_float2(r, c);
+}
+
+// The single pass for the row+column call (dense NV16).  Phase A transforms
+// each column-wise block once and keeps the result in registers across the
+// exchange, so phase B rounds the column-wise layout without recomputing it
+// and recomputes only the row-wise transform, from the raw rows kept in LDS.
+// Every block maximum is kept from phase A as well.
+template <int GRID, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads, 2) void ufp4_single_kernel(QuantParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t big[kFusedTileLds];
+  __shared__ ColStageT<4> cst;  // the own tile's column-wise staging, half the columns at a time
+  __shared__ float lut[2][128];
+  __shared__ float red[2][kThreads / 64];
+  __shared__ uint64_t left_mask[kMaxFusedTiles / 64];
+  __shared__ int32_t pick;
+  uint4 (&wl)[16][kThreads] = *reinterpret_cast<uint4 (*)[16][kThreads]>(big);
+  ColStage& full = *reinterpret_cast<ColStage*>(big);  // reloaded tiles' staging, once the rows are read
+  const TileInfo T = dense_tile(p, remap_xcd((int32_t)blockIdx.x, (int32_t)gridDim.x));
+  if (!T.active) return;  // uniform per workgroup; owns no tile
+  const Exchange X = exchange_begin(p, T);
+  const LaneGeom L = lane_geom(p, T);
+  float cv[16][8], rmax[16], cmax[8];
+  uint32_t sw[kWatch];
+  {
+    uint32_t w[16][4];
+    load_rows<0, 16, true>(p, T, L, w);
+    const float2 m = tile_amax_keep<RHT>(p, L, w, wl, cv, rmax, cmax, red, [&] { exchange_read_starts(X, sw); });
+    float r, c;
+    bool any_left;
+    if (!exchange_maxima(p, T, X, sw, m, r, c, any_left, left_mask, red)) return;
+    constexpr float qmax = grid_qmax<GRID>();
+    TensorScale tsr, tsc;
+    tensor_setup<RHT>(r, c, qmax, tsr, tsc, lut);
+    int32_t n_left, q;
+    exchange_ranks(p, T, X, any_left, left_mask, n_left, q);
+    write_tensor_scales(p, T, tsr, tsc);
+    // column-wise first: it consumes the kept values, which frees their
+    // registers for the row-wise pass; half the columns at a time, so the
+    // staging area fits beside the raw rows
+    auto col_src = [&](int k, float(&v)[16]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = cv[i][k];
+      return cmax[k];
+    };
+    col_pass<GRID, SR, false, RHT, false, 0, 4>(p, T, L, tsc, lut[1], cst, col_src);
+    __syncthreads();  // the first half's write-out has read the staging area
+    col_pass<GRID, SR, false, RHT, false, 4, 4>(p, T, L, tsc, lut[1], cst, col_src);
+    // the lane's row-wise signs, derived again through an opaque copy of
+    // its parity rather than held in registers since phase A
+    int parity = L.lc & 1;
+    asm volatile("" : "+v"(parity));
+    const RowLaneSigns rs = row_lane_signs<RHT>(p, parity);
+    row_pass<GRID, SR, false, RHT, false>(
+        p, T, L, tsr, lut[0], rs.fin, [&](int i, float(&v)[8]) __attribute__((always_inline)) {
+          const uint4 u = wl[i][threadIdx.x];
+          v[0] = bf_lo(u.x);
+          v[1] = bf_hi(u.x);
+          v[2] = bf_lo(u.y);
+          v[3] = bf_hi(u.y);
+          v[4] = bf_lo(u.z);
+          v[5] = bf_hi(u.z);
+          v[6] = bf_lo(u.w);
+          v[7] = bf_hi(u.w);
+          if (RHT) {
+            fwht8_half(v, rs.h);
+            cross_stage8(v, rs.s4);
+          }
+          return rmax[i];
+        });
+    if (n_left > 0) {
+      __syncthreads();  // every row has been read back: the tile area is free for reloaded tiles' staging
+      quantize_left_tiles<GRID, SR, RHT>(p, X, left_mask, n_left, q, tsr, tsc, lut, full, pick);
+    }
   }
 }
 
@@ -1208,10 +1593,17 @@ hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s, hipEv
 
 template <int GRID, bool SR>
 static void launch_fused_rht(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  if (p.rht)
+  // both layouts: the variant that keeps the column-wise transform
+  if (p.do_row && p.do_col) {
+    if (p.rht)
+      launch(ufp4_single_kernel<GRID, SR, true>, p, grid, s, t0, t1);
+    else
+      launch(ufp4_single_kernel<GRID, SR, false>, p, grid, s, t0, t1);
+  } else if (p.rht) {
     launch(ufp4_fused_kernel<GRID, SR, true>, p, grid, s, t0, t1);
-  else
+  } else {
     launch(ufp4_fused_kernel<GRID, SR, false>, p, grid, s, t0, t1);
+  }
 }
 
 template <int GRID>

@@ -187,7 +187,7 @@ int ufp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
  * it runs on until the process ends; its address is looked up (no
  * allocation) and the array zeroed by a fill kernel on `stream` at the first
  * call on each device.  Tensors whose workspace would exceed it (more than
- * about 127,000 tiles of 128 x 256 elements, 4.2e9 elements) give
+ * about 106,000 tiles of 128 x 256 elements, 3.4e9 elements) give
  * UFP4_ERR_WORKSPACE; a failed symbol lookup gives UFP4_ERR_HIP.  All calls
  * on one GPU share the array: calls that overlap on one GPU (concurrent
  * streams, threads) race and must be serialized by the caller.  Calls no
@@ -312,9 +312,10 @@ int ufp4_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols, int64_t
  * some tile not started within 100 us leaves its tile to the workgroups that
  * did start, which reload and quantize it, so the call always completes
  * (slowly when the device is shared).  UFP4_SCHEDULE_AUTO (the default)
- * takes the two-pass schedule, the faster one on MI355X for every tensor
- * measured.  Results are bit-identical in every schedule.  Process-wide
- * setting. */
+ * takes the single pass for row+column calls whose tiles the device holds
+ * at once (two per compute unit; the faster schedule there on MI355X) and
+ * two passes otherwise.  Results are bit-identical in every schedule.
+ * Process-wide setting. */
 enum ufp4_schedule { UFP4_SCHEDULE_AUTO = 0, UFP4_SCHEDULE_TWO_PASS = 1, UFP4_SCHEDULE_SINGLE_PASS = 2 };
 
 /* Select the schedule.  left_stride (test hook, single-pass schedule only):
@@ -325,11 +326,12 @@ int ufp4_set_schedule(int32_t schedule, int32_t left_stride);
 
 /* The schedule a quantization call on a tensor of rows x cols with
  * num_groups segments and this configuration takes on the current device
- * under the current setting: UFP4_SCHEDULE_SINGLE_PASS or
+ * under the current setting, for a call with both layouts (both_layouts != 0,
+ * ufp4_quantize_rowcol) or one: UFP4_SCHEDULE_SINGLE_PASS or
  * UFP4_SCHEDULE_TWO_PASS (also for MX32, grouped and empty tensors, which
  * need no separate maxima pass or have their own).  Host only. */
-int ufp4_schedule_of(int64_t rows, int64_t cols, int32_t num_groups, const ufp4_config* cfg,
-                     int32_t* schedule_out);
+int ufp4_schedule_of(int64_t rows, int64_t cols, int32_t num_groups, int32_t both_layouts,
+                     const ufp4_config* cfg, int32_t* schedule_out);
 
 /* --- training recipes ------------------------------------------------------ */
 

@@ -110,8 +110,10 @@ int main() {
   for (int sched = 0; sched <= 2; ++sched) {
     EXPECT(ufp4_set_schedule(sched, sched == 2 ? 3 : 0), UFP4_OK);
     int32_t which = -1;
-    EXPECT(ufp4_schedule_of(8192, 2048, 1, &ok, &which), UFP4_OK);
-    EXPECT(which == (sched == 2 ? 2 : 1), 1);
+    EXPECT(ufp4_schedule_of(8192, 2048, 1, 0, &ok, &which), UFP4_OK);
+    EXPECT(which == (sched == 2 ? 2 : 1), 1);  // one layout: two passes unless forced
+    EXPECT(ufp4_schedule_of(8192, 2048, 1, 1, &ok, &which), UFP4_OK);
+    EXPECT(which == 1 || which == 2, 1);  // AUTO: single pass if the device (none here) holds every tile
     EXPECT(ufp4_quantize_rowcol(x, 8192, 2048, 2048, &ok, row, col, ws, wsb, nullptr), UFP4_OK);
     EXPECT(ufp4_quantize_rowcol(x, 65536, 4096, 4096, &ok, row, col, ws, ufp4_workspace_size(65536, 4096, 1),
                                 nullptr),
@@ -121,7 +123,7 @@ int main() {
   EXPECT(ufp4_set_schedule(0, -1), UFP4_ERR_INVALID_ARGUMENT);
   EXPECT(ufp4_set_schedule(0, 0), UFP4_OK);
   int32_t which = 0;
-  EXPECT(ufp4_schedule_of(16, 16, 1, nullptr, &which), UFP4_ERR_INVALID_ARGUMENT);
+  EXPECT(ufp4_schedule_of(16, 16, 1, 1, nullptr, &which), UFP4_ERR_INVALID_ARGUMENT);
   float ta = 0, tq = 0;
   EXPECT(ufp4_time_rowcol(x, 8192, 2048, 2048, &mx, row, col, ws, wsb, nullptr, &ta, &tq), UFP4_ERR_INVALID_ARGUMENT);
   EXPECT(ufp4_time_rowcol(x, 8192, 2048, 2048, &ok, row, col, ws, wsb, nullptr, nullptr, &tq),
