@@ -20,7 +20,7 @@ from ._lib import (GEMM_BWD_DW, GEMM_BWD_DX, GEMM_FWD_Y, OPERAND_A, OPERAND_B, R
 
 __all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "GRID_E2M1C", "ROUND_RTNE", "ROUND_STOCHASTIC", "SCALE_NV16",
            "SCALE_MX32", "SCHEDULE_AUTO", "SCHEDULE_TWO_PASS", "SCHEDULE_SINGLE_PASS", "ufp4_set_schedule",
-           "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "ufp4_gemm_nt", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
+           "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_grouped_delayed", "ufp4_quantize_rowcol_noalloc", "ufp4_quantize_delayed", "ufp4_gemm_nt", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
            "ufp4_quantize", "ufp4_quantize_rowcol", "ufp4_quantize_grouped", "ufp4_dequantize",
            "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol",
            "block_len", "ufp4_recipe_config", "RECIPE_UFP4", "RECIPE_UFP4_INT4", "RECIPE_NVFP4",
@@ -135,6 +135,27 @@ def ufp4_quantize_grouped(x: torch.Tensor, offsets_dev: torch.Tensor, padded_row
                                     col_out.c() if col_out else null, ws.ptr if ws else None,
                                     ws.nbytes if ws else 0, _stream(stream)))
 
+
+
+def ufp4_quantize_grouped_delayed(x: torch.Tensor, offsets_dev: torch.Tensor, padded_rows: int,
+                                  cfg: ufp4_config, amax_in: torch.Tensor, amax_out: torch.Tensor | None,
+                                  row_out: QTensor | None, col_out: QTensor | None, ws: Workspace,
+                                  stream=None) -> None:
+    """amax_in / amax_out: float32 device tensors of num_groups (row, column) pairs."""
+    rows, cols, ld = _bf16_view(x)
+    if ld != cols:
+        raise ValueError("grouped input must be contiguous")
+    if offsets_dev.dtype != torch.int64 or amax_in.dtype != torch.float32:
+        raise TypeError("offsets must be int64 and maxima float32")
+    E = offsets_dev.numel() - 1
+    if amax_in.numel() != 2 * E or (amax_out is not None and amax_out.numel() != 2 * E):
+        raise ValueError("one (row, column) pair of maxima per segment")
+    null = ufp4_qtensor(None, None, None)
+    check("ufp4_quantize_grouped_delayed",
+          lib.ufp4_quantize_grouped_delayed(_ptr(x), rows, cols, _ptr(offsets_dev), E, int(padded_rows),
+                                            ctypes.byref(cfg), _ptr(amax_in), _ptr(amax_out),
+                                            row_out.c() if row_out else null, col_out.c() if col_out else null,
+                                            ws.ptr, ws.nbytes, _stream(stream)))
 
 def ufp4_set_schedule(schedule: int, left_stride: int = 0) -> None:
     """Process-wide schedule of dense NV16 calls (SCHEDULE_AUTO, _TWO_PASS,

@@ -31,7 +31,8 @@ EXPORTED = ["ufp4_status_string", "ufp4_workspace_size", "ufp4_workspace_init",
             "ufp4_quantize_grouped", "ufp4_dequantize", "ufp4_stats", "ufp4_round_f32",
             "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol", "ufp4_set_schedule",
             "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "ufp4_gemm_nt",
-            "ufp4_recipe_config", "ufp4_f32_to_bf16", "ufp4_quantize_rowcol_noalloc"]
+            "ufp4_recipe_config", "ufp4_f32_to_bf16", "ufp4_quantize_rowcol_noalloc",
+            "ufp4_quantize_grouped_delayed"]
 
 
 class Ufp4Error(RuntimeError):
@@ -84,6 +85,9 @@ def _load():
     L.ufp4_quantize_rowcol.argtypes = [P, i64, i64, i64, cfgp, ufp4_qtensor, ufp4_qtensor, P, sz, P]
     L.ufp4_quantize_rowcol_noalloc.restype = ctypes.c_int
     L.ufp4_quantize_rowcol_noalloc.argtypes = [P, i64, i64, i64, cfgp, ufp4_qtensor, ufp4_qtensor, P]
+    L.ufp4_quantize_grouped_delayed.restype = ctypes.c_int
+    L.ufp4_quantize_grouped_delayed.argtypes = [P, i64, i64, P, i32, i64, cfgp, P, P, ufp4_qtensor, ufp4_qtensor,
+                                                P, sz, P]
     L.ufp4_quantize_grouped.restype = ctypes.c_int
     L.ufp4_quantize_grouped.argtypes = [P, i64, i64, P, i32, i64, cfgp, ufp4_qtensor, ufp4_qtensor,
                                         P, sz, P]

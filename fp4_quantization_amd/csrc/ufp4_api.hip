@@ -466,6 +466,74 @@ int ufp4_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
   return run_quant(p, ws, ws_bytes, (hipStream_t)stream);
 }
 
+int ufp4_quantize_grouped_delayed(const uint16_t* x, int64_t total_rows, int64_t cols,
+                                  const int64_t* offsets_dev, int32_t num_groups, int64_t padded_rows,
+                                  const ufp4_config* cfg, const float* amax_in, float* amax_out,
+                                  ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws, size_t ws_bytes,
+                                  ufp4_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->scaling != UFP4_SCALE_NV16) return UFP4_ERR_INVALID_ARGUMENT;
+  if (total_rows < 0 || cols < 0 || num_groups < 1 || num_groups > kMaxGroups || !amax_in)
+    return UFP4_ERR_INVALID_ARGUMENT;
+  if (!offsets_dev) return UFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned(offsets_dev, 8) || !aligned(amax_in, 8) || !aligned(amax_out, 8)) return UFP4_ERR_ALIGNMENT;
+  if (cols % 16) return UFP4_ERR_SHAPE;
+  const bool do_row = row_out.tensor_scale != nullptr, do_col = col_out.tensor_scale != nullptr;
+  if (!do_row && !do_col) return UFP4_ERR_INVALID_ARGUMENT;
+  if (amax_out) {
+    // the kernel reads the provided maxima while it folds in its own
+    const uintptr_t a0 = (uintptr_t)amax_in, a1 = a0 + (uintptr_t)num_groups * 2 * sizeof(float);
+    const uintptr_t b0 = (uintptr_t)amax_out, b1 = b0 + (uintptr_t)num_groups * 2 * sizeof(float);
+    if (a0 < b1 && b0 < a1) return UFP4_ERR_INVALID_ARGUMENT;
+  }
+  const bool empty = total_rows == 0 || cols == 0;
+  if (do_row && (rc = check_qtensor(row_out, empty))) return rc;
+  if (do_col) {
+    if ((rc = check_qtensor(col_out, empty))) return rc;
+    if (padded_rows < total_rows || padded_rows % 16 || padded_rows > total_rows + 15 * (int64_t)num_groups)
+      return UFP4_ERR_SHAPE;
+  }
+  if (!empty) {
+    if (!x) return UFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || cols % 8) return UFP4_ERR_ALIGNMENT;
+  }
+  if (!ws || ws_bytes < kWsHeader || !aligned(ws, 256)) return UFP4_ERR_WORKSPACE;
+  QuantParams p;
+  base_params(p, x, total_rows, cols, cols, cfg, ws);
+  p.offsets = offsets_dev;
+  p.num_groups = num_groups;
+  p.padded_rows = do_col ? padded_rows : 0;
+  p.do_row = do_row;
+  p.do_col = do_col;
+  p.row_codes = row_out.codes;
+  p.row_scales = row_out.scales;
+  p.row_ts = row_out.tensor_scale;
+  p.col_codes = col_out.codes;
+  p.col_scales = col_out.scales;
+  p.col_ts = col_out.tensor_scale;
+  p.amax_in = reinterpret_cast<const float2*>(amax_in);
+  p.n_in = num_groups;
+  p.amax_out = reinterpret_cast<float2*>(amax_out);
+  hipStream_t s = (hipStream_t)stream;
+  // this call's maxima are folded into zeroed entries (empty segments stay 0)
+  if (amax_out && launch_fill(reinterpret_cast<uint32_t*>(amax_out), 2 * (int64_t)num_groups, 0u, s) != hipSuccess)
+    return UFP4_ERR_HIP;
+  if (empty) {
+    if (do_row && launch_fill(reinterpret_cast<uint32_t*>(p.row_ts), num_groups, 0x3F800000u, s) != hipSuccess)
+      return UFP4_ERR_HIP;
+    if (do_col && launch_fill(reinterpret_cast<uint32_t*>(p.col_ts), num_groups, 0x3F800000u, s) != hipSuccess)
+      return UFP4_ERR_HIP;
+    return UFP4_OK;
+  }
+  if (p.cols >= kMaxDim || p.padded_rows >= kMaxDim) return UFP4_ERR_SHAPE;
+  const int64_t grid = grid_size_quant(total_rows, cols, num_groups, 16, &p.n_band, &p.n_tiles);
+  p.n_work = p.n_band * p.n_tiles;
+  if (grid > 0x7FFFFFFF) return UFP4_ERR_SHAPE;
+  if (launch_grouped_delayed(p, grid, s) != hipSuccess) return UFP4_ERR_HIP;
+  return UFP4_OK;
+}
+
 int ufp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t rows,
                     int64_t cols, const ufp4_config* cfg, int32_t inverse_rht, float* out,
                     ufp4_stream_t stream) {

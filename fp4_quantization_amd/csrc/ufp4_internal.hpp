@@ -84,6 +84,10 @@ hipError_t launch_quant(const QuantParams& p, int64_t grid, hipStream_t s, hipEv
 // Delayed scaling (dense NV16): one kernel, tensor scales from p.amax_in.
 hipError_t launch_delayed(const QuantParams& p, int64_t grid, hipStream_t s, hipEvent_t t0 = nullptr,
                           hipEvent_t t1 = nullptr);
+// Delayed scaling of grouped (MoE) segments (NV16): one kernel, per-segment
+// tensor scales from p.amax_in[e], per-segment maxima folded into
+// p.amax_out[e] (zeroed beforehand) when it is not null.
+hipError_t launch_grouped_delayed(const QuantParams& p, int64_t grid, hipStream_t s);
 // The single-pass schedule (dense NV16 tensors of at most kMaxFusedTiles
 // tiles): one kernel, every tile kept in registers across a device-wide
 // exchange of the tile maxima.

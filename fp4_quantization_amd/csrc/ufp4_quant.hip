@@ -951,6 +951,78 @@ __global__ __launch_bounds__(kThreads) void ufp4_delayed_kernel(QuantParams p) {
   }
 }
 
+// ------------------------------------------------- grouped delayed
+// Delayed scaling for ragged expert segments (NV16): segment e's tensor
+// scales come from the provided maxima p.amax_in[e] = (row-wise,
+// column-wise) maxima of that segment's transformed values (the previous
+// step's, for instance), so the input is read once by one kernel.  Each
+// workgroup folds its tile maxima into p.amax_out[e] (when given; zeroed by
+// the host beforehand) with an atomic max on the bit patterns, which order
+// like the non-negative values; the updates are not waited for.
+template <int GRID, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void ufp4_grouped_delayed_kernel(QuantParams p) {
+  __shared__ GroupLds g;
+  __shared__ float lut[2][128];
+  __shared__ float red[2][kThreads / 64];
+  __shared__ ColStage cst;
+  const TileInfo T = tile_info(p, g);
+  if (blockIdx.x == 0) {
+    if (p.ws_status && threadIdx.x == 0) *p.ws_status = T.bad ? 6u : 0u;
+    if (!T.bad) {
+      for (int e = threadIdx.x; e < p.num_groups; e += kThreads) {
+        if (g.off[e + 1] == g.off[e]) {  // empty segment: nothing to quantize, S_t = 1
+          if (p.do_row && p.row_ts) p.row_ts[e] = 1.0f;
+          if (p.do_col && p.col_ts) p.col_ts[e] = 1.0f;
+        }
+      }
+    }
+  }
+  if (!T.active) return;  // uniform per workgroup
+  const LaneGeom L = lane_geom(p, T);
+  constexpr float qmax = grid_qmax<GRID>();
+  const float2 given = p.amax_in[T.seg];
+  uint32_t w[16][4];
+  load_rows<0, 4, true>(p, T, L, w);
+  const TensorScale tsr = given_tensor_scale<RHT>(given_max(given.x), qmax);
+  const TensorScale tsc = given_tensor_scale<RHT>(given_max(given.y), qmax);
+  {
+    const int t = threadIdx.x, l = t >> 7, cc = t & 127;
+    const float S = l ? tsc.S : tsr.S;
+    const float d = (cc == 127) ? 0.0f : e4m3_decode_pos((uint32_t)cc) * S;
+    lut[l][cc] = (d == 0.0f) ? 0.0f : 1.0f / d;  // inverse dequantization factor per code
+  }
+  if (threadIdx.x == 0 && T.band == 0 && T.m0 == 0) {
+    if (p.do_row && p.row_ts) p.row_ts[T.seg] = tsr.S;
+    if (p.do_col && p.col_ts) p.col_ts[T.seg] = tsc.S;
+  }
+  __syncthreads();
+  load_rows<4, 16, true>(p, T, L, w);
+  float2 m = quant_tile<GRID, SR, false, RHT, true, true>(p, T, L, w, tsr, tsc, lut, cst);
+  m.x = wave_max(m.x);
+  m.y = wave_max(m.y);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = m.x;
+    red[1][threadIdx.x >> 6] = m.y;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && p.amax_out) {
+    float a = red[0][0], b = red[1][0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) {
+      a = fmaxf(a, red[0][i]);
+      b = fmaxf(b, red[1][i]);
+    }
+    // maxima of the transformed values: the final 1/4 is exact
+    if (RHT) {
+      a *= 0.25f;
+      b *= 0.25f;
+    }
+    uint32_t* out = reinterpret_cast<uint32_t*>(p.amax_out + T.seg);
+    if (p.do_row) __hip_atomic_fetch_max(out, __float_as_uint(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (p.do_col) __hip_atomic_fetch_max(out + 1, __float_as_uint(b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // ------------------------------------------------------- single pass
 // One kernel for a dense NV16 tensor whose tiles the device can hold at
 // once: each workgroup loads its tile, computes the tile maxima (phase A),
@@ -1639,6 +1711,28 @@ hipError_t launch_delayed(const QuantParams& p, int64_t grid, hipStream_t s, hip
     case kGridINT4: return launch_delayed_grid<kGridINT4>(p, grid, s, t0, t1);
     case kGridE2M1: return launch_delayed_grid<kGridE2M1>(p, grid, s, t0, t1);
     case kGridE2M1C: return launch_delayed_grid<kGridE2M1C>(p, grid, s, t0, t1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int GRID>
+static hipError_t launch_grouped_delayed_grid(const QuantParams& p, int64_t grid, hipStream_t s) {
+  if (p.sr) {
+    if (p.rht) launch(ufp4_grouped_delayed_kernel<GRID, true, true>, p, grid, s, nullptr, nullptr);
+    else launch(ufp4_grouped_delayed_kernel<GRID, true, false>, p, grid, s, nullptr, nullptr);
+  } else {
+    if (p.rht) launch(ufp4_grouped_delayed_kernel<GRID, false, true>, p, grid, s, nullptr, nullptr);
+    else launch(ufp4_grouped_delayed_kernel<GRID, false, false>, p, grid, s, nullptr, nullptr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_delayed(const QuantParams& p, int64_t grid, hipStream_t s) {
+  switch (p.grid) {
+    case kGridE1M2: return launch_grouped_delayed_grid<kGridE1M2>(p, grid, s);
+    case kGridINT4: return launch_grouped_delayed_grid<kGridINT4>(p, grid, s);
+    case kGridE2M1: return launch_grouped_delayed_grid<kGridE2M1>(p, grid, s);
+    case kGridE2M1C: return launch_grouped_delayed_grid<kGridE2M1C>(p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -300,6 +300,34 @@ int ufp4_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols, int64_t
                           const ufp4_config* cfg, const float* amax_in, int32_t n_in, float* amax_out,
                           ufp4_qtensor row_out, ufp4_qtensor col_out, ufp4_stream_t stream);
 
+/* Delayed scaling of grouped (MoE) segments (NV16 only): as
+ * ufp4_quantize_grouped, but segment e's tensor scales come from provided
+ * maxima instead of the segment's own, so the input is read once by one
+ * kernel (the mixture-of-experts operands of "Shrinkage Bias: The Hidden
+ * Geometric Trap in FP4 Training" (zhichai.net), "Key points", validation
+ * results; the maxima rules of ufp4_quantize_delayed, per segment).
+ *   amax_in: device, num_groups pairs (row-wise, column-wise): maxima of
+ *     |transformed value| (after the RHT's 1/4; of |x| without the RHT) of
+ *     each segment's values in that layout.  An entry that is not a positive
+ *     finite number counts as zero (S_t = 1).  S_t = max / (Qmax * 448).
+ *   amax_out: device, num_groups pairs, or NULL: this call's own per-segment
+ *     maxima in the same units (0 for an empty segment or a layout not
+ *     requested), to pass as the next call's amax_in when the routing stays
+ *     comparable.  Must not overlap amax_in (UFP4_ERR_INVALID_ARGUMENT).
+ *   Blocks whose maximum exceeds the provided one saturate (E4M3 scale 448,
+ *   codes at +-Qmax).  With each segment's own maxima provided, the outputs
+ *   equal ufp4_quantize_grouped's bit for bit.
+ * Shapes, layouts, offsets rules and workspace (its status word reports
+ * offsets the device rejects) as ufp4_quantize_grouped; amax_in and amax_out
+ * 8-byte aligned.  MX32 gives UFP4_ERR_INVALID_ARGUMENT.  A numerics choice
+ * (delayed scaling), not the pages' recipe, which takes each tensor's own
+ * maximum. */
+int ufp4_quantize_grouped_delayed(const uint16_t* x, int64_t total_rows, int64_t cols,
+                                  const int64_t* offsets_dev, int32_t num_groups, int64_t padded_rows,
+                                  const ufp4_config* cfg, const float* amax_in, float* amax_out,
+                                  ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws, size_t ws_bytes,
+                                  ufp4_stream_t stream);
+
 /* --- schedule ------------------------------------------------------------ */
 
 /* Dense NV16 calls need the tensor maximum before any code is written.

@@ -100,6 +100,9 @@ def lib():
         L.orc_quantize_grouped.restype = ctypes.c_int
         L.orc_quantize_grouped.argtypes = [P, i64, i64, P, i32, ctypes.POINTER(Config),
                                            P, P, P, P, P, P]
+        L.orc_quantize_grouped_given_amax.restype = ctypes.c_int
+        L.orc_quantize_grouped_given_amax.argtypes = [P, i64, i64, P, i32, ctypes.POINTER(Config), P, P,
+                                                      P, P, P, P, P, P]
         L.orc_dequantize.restype = ctypes.c_int
         L.orc_dequantize.argtypes = [P, P, P, i64, i64, ctypes.POINTER(Config), i32, P]
         L.orc_compute_stats.restype = ctypes.c_int
@@ -282,6 +285,36 @@ def quantize_grouped(x_bf16: np.ndarray, offsets, cfg: Config, row=True, col=Tru
     if rc:
         raise ValueError(f"orc_quantize_grouped failed ({rc})")
     return (rc_, rs_, rts), (cc_, cs_, cts), coff
+
+
+def quantize_grouped_given_amax(x_bf16: np.ndarray, offsets, cfg: Config, amax_given, row=True, col=True):
+    """Grouped delayed scaling (NV16): segment e's tensor scales from
+    amax_given[e] = (row-wise, column-wise) maxima.  Returns the row and
+    column outputs as quantize_grouped, the column offsets, and each
+    segment's own maxima [E][2]."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    R, C = x.shape
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    E = off.size - 1
+    B = block_len(cfg.scaling)
+    coff = grouped_col_offsets(off, B)
+    R_pad = int(coff[-1])
+    given = np.ascontiguousarray(np.asarray(amax_given, np.float32).reshape(E, 2))
+    seen = np.zeros((E, 2), np.float32)
+    rc_ = np.zeros((R, C // 2), np.uint8) if row else None
+    rs_ = np.zeros((R, C // B), np.uint8) if row else None
+    rts = np.zeros(E, np.float32)
+    cc_ = np.zeros((C, R_pad // 2), np.uint8) if col else None
+    cs_ = np.zeros((C, R_pad // B), np.uint8) if col else None
+    cts = np.zeros(E, np.float32)
+    nul = ctypes.c_void_p(0)
+    rc = lib().orc_quantize_grouped_given_amax(
+        _ptr(x), R, C, _ptr(off), E, ctypes.byref(cfg), _ptr(given), _ptr(seen),
+        _ptr(rc_) if row else nul, _ptr(rs_) if row else nul, _ptr(rts),
+        _ptr(cc_) if col else nul, _ptr(cs_) if col else nul, _ptr(cts))
+    if rc:
+        raise ValueError(f"orc_quantize_grouped_given_amax failed ({rc})")
+    return (rc_, rs_, rts), (cc_, cs_, cts), coff, seen
 
 
 def dequantize(codes, scales, tensor_scale, rows: int, cols: int, cfg: Config,

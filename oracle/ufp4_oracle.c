@@ -404,10 +404,6 @@ static float quantize_lineset_amax(const lineset* L, const orc_config* cfg, uint
   return S_t;
 }
 
-static float quantize_lineset(const lineset* L, const orc_config* cfg, uint8_t* codes,
-                              uint8_t* scales) {
-  return quantize_lineset_amax(L, cfg, codes, scales, NULL, NULL);
-}
 
 static int check_cfg(const orc_config* cfg) {
   if (!cfg) return 1;
@@ -465,10 +461,15 @@ int orc_grouped_col_offsets(const int64_t* offsets, int32_t num_groups, int32_t 
   return 0;
 }
 
-int orc_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
-                         const int64_t* offsets, int32_t num_groups, const orc_config* cfg,
-                         uint8_t* row_codes, uint8_t* row_scales, float* row_tensor_scale,
-                         uint8_t* col_codes, uint8_t* col_scales, float* col_tensor_scale) {
+/* Grouped driver: segment e is one lineset per layout.  With amax_given,
+ * segment e's tensor scales come from amax_given[2e] (row-wise) and
+ * amax_given[2e+1] (column-wise) (delayed scaling per segment); amax_seen
+ * receives each segment's own maxima in the same layout.                   */
+static int quantize_grouped_impl(const uint16_t* x, int64_t total_rows, int64_t cols,
+                                 const int64_t* offsets, int32_t num_groups, const orc_config* cfg,
+                                 const float* amax_given, float* amax_seen,
+                                 uint8_t* row_codes, uint8_t* row_scales, float* row_tensor_scale,
+                                 uint8_t* col_codes, uint8_t* col_scales, float* col_tensor_scale) {
   if (check_cfg(cfg) || num_groups < 0 || cols < 0) return 1;
   int B = block_len(cfg);
   if (cols % B) return 2;
@@ -480,15 +481,37 @@ int orc_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
     int64_t r0 = offsets[e], m = offsets[e + 1] - offsets[e];
     if (row_codes) {
       lineset L = {x + r0 * cols, cols, 1, m, cols, cols, cols, r0 * cols, 0u};
-      row_tensor_scale[e] = quantize_lineset(&L, cfg, row_codes, row_scales);
+      row_tensor_scale[e] = quantize_lineset_amax(&L, cfg, row_codes, row_scales,
+                                                  amax_given ? &amax_given[2 * e] : NULL,
+                                                  amax_seen ? &amax_seen[2 * e] : NULL);
     }
     if (col_codes) {
       int64_t P = col_off[e + 1] - col_off[e];
       lineset L = {x + r0 * cols, 1, cols, cols, P, m, R_pad, col_off[e], 1u};
-      col_tensor_scale[e] = quantize_lineset(&L, cfg, col_codes, col_scales);
+      col_tensor_scale[e] = quantize_lineset_amax(&L, cfg, col_codes, col_scales,
+                                                  amax_given ? &amax_given[2 * e + 1] : NULL,
+                                                  amax_seen ? &amax_seen[2 * e + 1] : NULL);
     }
   }
   return 0;
+}
+
+int orc_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
+                         const int64_t* offsets, int32_t num_groups, const orc_config* cfg,
+                         uint8_t* row_codes, uint8_t* row_scales, float* row_tensor_scale,
+                         uint8_t* col_codes, uint8_t* col_scales, float* col_tensor_scale) {
+  return quantize_grouped_impl(x, total_rows, cols, offsets, num_groups, cfg, NULL, NULL, row_codes, row_scales,
+                               row_tensor_scale, col_codes, col_scales, col_tensor_scale);
+}
+
+int orc_quantize_grouped_given_amax(const uint16_t* x, int64_t total_rows, int64_t cols,
+                                    const int64_t* offsets, int32_t num_groups, const orc_config* cfg,
+                                    const float* amax_given, float* amax_seen,
+                                    uint8_t* row_codes, uint8_t* row_scales, float* row_tensor_scale,
+                                    uint8_t* col_codes, uint8_t* col_scales, float* col_tensor_scale) {
+  if (!cfg || cfg->scaling != ORC_SCALE_NV16 || !amax_given) return 1;
+  return quantize_grouped_impl(x, total_rows, cols, offsets, num_groups, cfg, amax_given, amax_seen, row_codes,
+                               row_scales, row_tensor_scale, col_codes, col_scales, col_tensor_scale);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -106,6 +106,18 @@ int orc_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
                          uint8_t* row_codes, uint8_t* row_scales, float* row_tensor_scale,
                          uint8_t* col_codes, uint8_t* col_scales, float* col_tensor_scale);
 
+/* Grouped delayed scaling (NV16 only): as orc_quantize_grouped, but segment
+ * e's tensor scales come from amax_given[2e] (row-wise) and amax_given[2e+1]
+ * (column-wise), maxima of that segment's transformed values supplied by the
+ * caller, with the same rules as orc_quantize_given_amax; amax_seen (may be
+ * null) receives each segment's own maxima in the same layout (0 for an
+ * empty segment).  Returns 1 for MX32. */
+int orc_quantize_grouped_given_amax(const uint16_t* x, int64_t total_rows, int64_t cols,
+                                    const int64_t* offsets, int32_t num_groups, const orc_config* cfg,
+                                    const float* amax_given, float* amax_seen,
+                                    uint8_t* row_codes, uint8_t* row_scales, float* row_tensor_scale,
+                                    uint8_t* col_codes, uint8_t* col_scales, float* col_tensor_scale);
+
 /* Dequantize one layout, in that layout's own orientation (rows = number of
  * block lines, cols = elements per line).  Optional inverse RHT per block. */
 int orc_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,

@@ -167,6 +167,32 @@ int main() {
   EXPECT(ufp4_quantize_grouped(x, 65536, 4096, off, 64, 65536, &ok, none, col, ws, 64, nullptr), UFP4_ERR_WORKSPACE);
   EXPECT(ufp4_quantize_grouped(x, 65536, 4096, off, 64, 65536, &mx, row, col, ws, 256, nullptr), UFP4_OK);
 
+  // grouped delayed scaling
+  {
+    const float* gin = dev<float>((size_t)12 << 30);
+    float* gout = dev<float>((size_t)13 << 30);
+    EXPECT(ufp4_quantize_grouped_delayed(x, 65536, 4096, off, 64, 65536, &mx, gin, gout, row, col, ws, gwsb, nullptr),
+           UFP4_ERR_INVALID_ARGUMENT);
+    EXPECT(ufp4_quantize_grouped_delayed(x, 65536, 4096, off, 64, 65536, &ok, nullptr, gout, row, col, ws, gwsb,
+                                         nullptr),
+           UFP4_ERR_INVALID_ARGUMENT);
+    EXPECT(ufp4_quantize_grouped_delayed(x, 65536, 4096, off, 64, 65536, &ok, gin, const_cast<float*>(gin) + 2, row,
+                                         col, ws, gwsb, nullptr),
+           UFP4_ERR_INVALID_ARGUMENT);  // overlapping maxima
+    EXPECT(ufp4_quantize_grouped_delayed(x, 65536, 4096, off, 64, 65536, &ok, gin + 1, gout, row, col, ws, gwsb,
+                                         nullptr),
+           UFP4_ERR_ALIGNMENT);
+    EXPECT(ufp4_quantize_grouped_delayed(x, 65536, 4096, off, 64, 65536, &ok, gin, gout, row, col, nullptr, 0, nullptr),
+           UFP4_ERR_WORKSPACE);
+    EXPECT(ufp4_quantize_grouped_delayed(x, 65536, 4096, off, 64, 65536 + 16 * 60, &ok, gin, gout, row, col, ws, 256,
+                                         nullptr),
+           UFP4_OK);
+    EXPECT(ufp4_quantize_grouped_delayed(x, 65536, 4096, off, 64, 0, &sr, gin, nullptr, row, none, ws, 256, nullptr),
+           UFP4_OK);
+    EXPECT(ufp4_quantize_grouped_delayed(nullptr, 0, 4096, off, 64, 0, &ok, gin, gout, row, col, ws, 256, nullptr),
+           UFP4_OK);
+  }
+
   // ufp4_dequantize and ufp4_stats
   EXPECT(ufp4_dequantize(row.codes, row.scales, row.tensor_scale, 64, 72, &ok, 1, dev<float>((size_t)9 << 30), nullptr),
          UFP4_ERR_SHAPE);

@@ -46,6 +46,10 @@ hipError_t launch_delayed(const QuantParams& p, int64_t grid, hipStream_t, hipEv
   require(p.amax_in != nullptr && p.n_in >= 1 && !p.mx && p.offsets == nullptr, "delayed");
   return quant_launch(p, grid, "delayed");
 }
+hipError_t launch_grouped_delayed(const QuantParams& p, int64_t grid, hipStream_t) {
+  require(p.amax_in != nullptr && p.n_in == p.num_groups && p.offsets != nullptr && !p.mx && p.ws_status, "grouped delayed");
+  return quant_launch(p, grid, "grouped delayed");
+}
 hipError_t launch_fused(const QuantParams& p, int64_t grid, hipStream_t, hipEvent_t, hipEvent_t) {
   require(p.fs_gen != nullptr && p.fs_words != nullptr && p.n_work <= kMaxFusedTiles && !p.mx, "single pass");
   return quant_launch(p, grid, "single pass");

@@ -152,3 +152,23 @@ def test_moe_grouped_65536x4096(env):
     eq("col codes", cq.codes.cpu().numpy(), cc)
     eq("col scales", cq.scales.cpu().numpy(), cs)
     eq("col tensor scales", cq.tensor_scale.cpu().numpy()[:E].view(np.uint32), cts.view(np.uint32))
+
+    # grouped delayed scaling, chained as in training: a first call under
+    # stale per-segment maxima, then a call under the first one's maxima,
+    # which are the segments' own: the exact grouped path, bit for bit
+    say("[full] MoE 65536x4096 grouped delayed, chained")
+    stale = torch.full((E, 2), 3.0, dtype=torch.float32, device="cuda")
+    a1 = torch.full((E, 2), -1.0, dtype=torch.float32, device="cuda")
+    a2 = torch.full((E, 2), -1.0, dtype=torch.float32, device="cuda")
+    offd = torch.from_numpy(offsets).cuda()
+    F.ufp4_quantize_grouped_delayed(x, offd, Rp, fc, stale, a1, rq, cq, ws)
+    F.ufp4_quantize_grouped_delayed(x, offd, Rp, fc, a1, a2, rq, cq, ws)
+    torch.cuda.synchronize()
+    assert ws.status() == 0
+    assert torch.equal(a1, a2) and bool((a1 >= 0).all())
+    eq("delayed row codes", rq.codes.cpu().numpy(), rc)
+    eq("delayed row scales", rq.scales.cpu().numpy(), rs)
+    eq("delayed row tensor scales", rq.tensor_scale.cpu().numpy()[:E].view(np.uint32), rts.view(np.uint32))
+    eq("delayed col codes", cq.codes.cpu().numpy(), cc)
+    eq("delayed col scales", cq.scales.cpu().numpy(), cs)
+    eq("delayed col tensor scales", cq.tensor_scale.cpu().numpy()[:E].view(np.uint32), cts.view(np.uint32))

@@ -556,6 +556,72 @@ def test_grouped_single_outputs_and_bad_offsets(env):
     assert bool((rqb.codes == 0xAB).all())
 
 
+@pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
+@pytest.mark.parametrize("rounding", [RTNE, SR])
+@pytest.mark.parametrize("rht", [1, 0])
+def test_grouped_delayed_matches_oracle(env, grid, rounding, rht):
+    # per-segment provided maxima: the segment's own, larger, smaller
+    # (saturating), zero and non-finite; codes, scales, tensor scales and the
+    # per-segment maxima written for the next call against the oracle
+    torch, F, orc = env
+    counts = np.array([0, 5, 16, 37, 1, 130, 0, 23, 64, 200, 3])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    E = len(counts)
+    xb = synth.activation(int(offsets[-1]), 320, seed=17)
+    say(f"[grouped delayed] grid={grid} rnd={rounding} rht={rht}")
+    fc, oc = cfgs(F, orc, grid, rounding, NV16, rht, rht_seed=6, sr_seed=7)
+    *_, own = orc.quantize_grouped_given_amax(xb, offsets, oc, np.ones((E, 2), np.float32))
+    rng = np.random.default_rng(grid * 4 + rounding * 2 + rht)
+    given = (own * rng.choice([1.0, 3.0, 0.3], size=own.shape)).astype(np.float32)
+    given[1, 0], given[2, 1], given[5, 0] = 0.0, np.inf, -1.0
+    (rc, rs, rts), (cc, cs, cts), coff, seen = orc.quantize_grouped_given_amax(xb, offsets, oc, given)
+    R, C = xb.shape
+    Rp = int(coff[-1])
+    x = to_dev(torch, xb)
+    off = torch.from_numpy(offsets).cuda()
+    rq, cq = F.alloc_layout(R, C, NV16, E), F.alloc_layout(C, Rp, NV16, E)
+    a_in = torch.from_numpy(given.copy()).cuda()
+    a_out = torch.full((E, 2), -1.0, dtype=torch.float32, device="cuda")
+    ws = F.Workspace(R, C, E)
+    F.ufp4_quantize_grouped_delayed(x, off, Rp, fc, a_in, a_out, rq, cq, ws)
+    assert ws.status() == 0
+    assert_layout_equal(rq, (rc, rs, rts), "grouped delayed row")
+    assert_layout_equal(cq, (cc, cs, cts), "grouped delayed col")
+    np.testing.assert_array_equal(a_out.cpu().numpy().view(np.uint32), seen.view(np.uint32))
+
+
+def test_grouped_delayed_single_layouts_and_bad_offsets(env):
+    torch, F, orc = env
+    counts = np.array([17, 0, 48, 9])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    E = len(counts)
+    xb = synth.activation(int(offsets[-1]), 64, seed=18)
+    fc, oc = cfgs(F, orc, E1M2, RTNE, NV16, 1, 3, 3)
+    *_, own = orc.quantize_grouped_given_amax(xb, offsets, oc, np.ones((E, 2), np.float32))
+    (rc, rs, rts), (cc, cs, cts), coff, _ = orc.quantize_grouped_given_amax(xb, offsets, oc, own)
+    R, C = xb.shape
+    Rp = int(coff[-1])
+    x = to_dev(torch, xb)
+    off = torch.from_numpy(offsets).cuda()
+    a_in = torch.from_numpy(own.copy()).cuda()
+    a_out = torch.zeros((E, 2), dtype=torch.float32, device="cuda")
+    ws = F.Workspace(R, C, E)
+    rq = F.alloc_layout(R, C, NV16, E)
+    F.ufp4_quantize_grouped_delayed(x, off, Rp, fc, a_in, a_out, rq, None, ws)
+    assert_layout_equal(rq, (rc, rs, rts), "row only")
+    got = a_out.cpu().numpy()
+    assert np.array_equal(got[:, 0], own[:, 0]) and np.all(got[:, 1] == 0)  # column layout not requested
+    cq = F.alloc_layout(C, Rp, NV16, E)
+    F.ufp4_quantize_grouped_delayed(x, off, Rp, fc, a_in, None, None, cq, ws)
+    assert_layout_equal(cq, (cc, cs, cts), "col only")
+    bad = torch.from_numpy(np.array([0, 40, 20, 60, 74], np.int64)).cuda()
+    rqb = F.alloc_layout(R, C, NV16, E)
+    rqb.codes.fill_(0xAB)
+    F.ufp4_quantize_grouped_delayed(x, bad, Rp, fc, a_in, None, rqb, None, ws)
+    assert ws.status() == 6
+    assert bool((rqb.codes == 0xAB).all())
+
+
 # ------------------------------------------------------- dequantize / stats
 @pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
 @pytest.mark.parametrize("scaling", [NV16, MX32])

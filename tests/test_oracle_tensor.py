@@ -470,6 +470,72 @@ def test_given_maximum_not_positive_finite_counts_as_zero(orc):
         np.testing.assert_array_equal(c, ref[0])
 
 
+# ------------------------------------- grouped delayed scaling (per segment)
+def _segment_refs(orc, xb, off, cfg, given, e, coff):
+    """Segment e through the dense given-maximum path (pinned above): its
+    rows row-wise, and its rows zero-padded to the block column-wise."""
+    r0, m = int(off[e]), int(off[e + 1] - off[e])
+    seg = xb[r0:r0 + m]
+    P = int(coff[e + 1] - coff[e])
+    padded = np.zeros((P, xb.shape[1]), np.uint16)
+    padded[:m] = seg
+    return (orc.quantize_given_amax(seg, cfg, ROW, float(given[e, 0])),
+            orc.quantize_given_amax(padded, cfg, COL, float(given[e, 1])))
+
+
+def test_grouped_given_maxima_are_the_dense_given_path_per_segment(orc):
+    # (round to nearest: stochastic rounding draws the word of an element's
+    # index in the whole grouped output, which the per-segment dense calls do
+    # not share; that index is pinned by the stochastic-rounding index tests)
+    rounding = RTNE
+    counts = np.array([0, 7, 16, 45, 1, 0, 90])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    R, C = int(off[-1]), 64
+    xb = synth.activation(R, C, 15)
+    cfg = orc.config(grid=E1M2, rounding=rounding, rht=1, rht_seed=4, sr_seed=9)
+    rng = np.random.default_rng(3)
+    # per segment: its own maximum, a larger one, a smaller one (saturation),
+    # zero and a non-finite value (S_t = 1)
+    _, _, coff, own = orc.quantize_grouped_given_amax(xb, off, cfg, np.ones((len(counts), 2), np.float32))
+    factors = rng.choice([1.0, 3.0, 0.25], size=own.shape)
+    given = (own * factors).astype(np.float32)
+    given[3, 0], given[6, 1] = 0.0, np.inf
+    (rc, rs, rts), (cc, cs, cts), coff2, seen = orc.quantize_grouped_given_amax(xb, off, cfg, given)
+    np.testing.assert_array_equal(coff, coff2)
+    np.testing.assert_array_equal(seen, own)
+    for e, m in enumerate(counts):
+        if m == 0:
+            assert rts[e] == 1.0 and cts[e] == 1.0 and seen[e, 0] == 0.0 and seen[e, 1] == 0.0
+            continue
+        (c1, s1, t1, m1), (c2, s2, t2, m2) = _segment_refs(orc, xb, off, cfg, given, e, coff)
+        r0 = int(off[e])
+        np.testing.assert_array_equal(rc[r0:r0 + m], c1)
+        np.testing.assert_array_equal(rs[r0:r0 + m], s1)
+        assert rts[e] == t1[0] and seen[e, 0] == np.float32(m1)
+        P = int(coff[e + 1] - coff[e])
+        np.testing.assert_array_equal(cc[:, coff[e] // 2:(coff[e] + P) // 2], c2)
+        np.testing.assert_array_equal(cs[:, coff[e] // 16:(coff[e] + P) // 16], s2)
+        assert cts[e] == t2[0] and seen[e, 1] == np.float32(m2)
+
+
+def test_grouped_given_own_maxima_reproduce_exact_grouped_path(orc):
+    counts = np.array([5, 0, 37, 16, 70])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    xb = synth.activation(int(off[-1]), 96, 16)
+    for grid, rounding in ((E1M2, RTNE), (INT4, RTNE), (E2M1, RTNE), (E2M1_CLAMP, RTNE), (E1M2, SR), (E2M1, SR)):
+        cfg = orc.config(grid=grid, rounding=rounding, rht=1, rht_seed=2, sr_seed=5)
+        (rc, rs, rts), (cc, cs, cts), _ = orc.quantize_grouped(xb, off, cfg)
+        *_, own = orc.quantize_grouped_given_amax(xb, off, cfg, np.ones((len(counts), 2), np.float32))
+        (rc2, rs2, rts2), (cc2, cs2, cts2), _, seen = orc.quantize_grouped_given_amax(xb, off, cfg, own)
+        np.testing.assert_array_equal(seen, own)
+        for a, b in ((rc, rc2), (rs, rs2), (cc, cc2), (cs, cs2)):
+            np.testing.assert_array_equal(a, b)
+        np.testing.assert_array_equal(rts.view(np.uint32), rts2.view(np.uint32))
+        np.testing.assert_array_equal(cts.view(np.uint32), cts2.view(np.uint32))
+    with pytest.raises(ValueError):
+        orc.quantize_grouped_given_amax(xb, off, orc.config(scaling=MX32), own)
+
+
 # ------------------------------------------------------ consumer GEMM reference
 @pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1_CLAMP])
 def test_gemm_reference_is_the_product_of_exactly_quantized_inputs(orc, grid):
