@@ -2,7 +2,7 @@
 activation on one MI355X, reported as HBM GB/s (algorithmic bytes / time).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-warm] [--copy]
-                [--schedule auto|two-pass|single-pass] [--no-extra]
+                [--schedule auto|two-pass|single-pass] [--no-extra] [--workload NAME]
 
 A step is one ufp4_quantize_rowcol call (every stage of the hot path: load,
 random signs, 16-point Walsh-Hadamard transform, tensor and block maxima,
@@ -29,13 +29,15 @@ buffer sets.
 The oracle leg (cpu_baseline) times the single-threaded CPU oracle on the same
 tensor (row-wise and column-wise), a reported baseline only.
 
-Reported beside the headline, under "extra" (never as the value): the RHT-off
+Reported beside the headline, under "extra" (never as the value): a
+bandwidth reference on the same buffers (ufp4_roof_rowcol: the quantization
+kernels' loads and the call's output bytes with no arithmetic), the RHT-off
 call, the E2M1, INT4 and MX32 variants of the call, the other schedule,
 delayed scaling, the consumer GEMM, a streaming
 copy of 512 MiB on the same box, the weight workload's shrinkage sweep (SQNR,
 mean signed error in grid units and gain alpha per grid, RHT on and off),
 the output-gradient workload (stochastic rounding, row+col) and MoE workload
-(grouped, row+col) call times, and the compounding of the GEMM gain through
+(grouped, row+col; grouped delayed scaling) call times, and the compounding of the GEMM gain through
 16 quantized layers.
 """
 from __future__ import annotations
@@ -91,6 +93,7 @@ SINGLE_KERNEL = "ufp4_single_kernel<0, false, true>"
 DELAYED_KERNEL = "ufp4_delayed_kernel<0, false, true>"
 AMAX_KERNEL = "ufp4_amax_kernel<true>"
 QUANT_KERNEL = "ufp4_quant_kernel<0, false, false, true>"
+ROOF_KERNEL = "ufp4_roof_kernel"
 
 
 def _counter_means(csv_dir, counter):
@@ -121,7 +124,7 @@ def _counter_means(csv_dir, counter):
     return means, copy_mean
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands, workload=None):
     """Write the counter summary bench.py reads: HBM bytes per launch of the
     single-pass kernel, of the two-pass quantization kernel and per two-pass
     call, each counter scaled by what it reads for a plain 512 MiB device
@@ -132,6 +135,12 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
     _, copy_write = _counter_means(copy_write_dir, "WRITE_SIZE")
     copy_kib = 512 * 1024
     ff, wf = copy_kib / copy_fetch, copy_kib / copy_write
+    if workload:
+        summarize_workload_counters(workload, fetch, write,
+                                    {"copy_bytes": copy_kib * 1024, "fetch_kib_raw": copy_fetch,
+                                     "write_kib_raw": copy_write, "fetch_factor": ff, "write_factor": wf},
+                                    ff, wf, commands)
+        return
 
     def pick(d, key):
         hits = [k for k in d if key in k]
@@ -147,21 +156,55 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
     _, wq = pick(write, QUANT_KERNEL)
     kd, fd = pick(fetch, DELAYED_KERNEL)
     _, wd = pick(write, DELAYED_KERNEL)
+    kr, fr = pick(fetch, ROOF_KERNEL)
+    _, wr = pick(write, ROOF_KERNEL)
+    roof = (fr * ff + wr * wf) * 1024
     delayed = (fd * ff + wd * wf) * 1024
     fused = (ff_ * ff + wf_ * wf) * 1024
     quant = (fq * ff + wq * wf) * 1024
     call = quant + (fa * ff + wa * wf) * 1024
-    out = {"fetch_kib_raw": {kf: ff_, ka: fa, kq: fq, kd: fd}, "write_kib_raw": {kf: wf_, ka: wa, kq: wq, kd: wd},
+    out = {"fetch_kib_raw": {kf: ff_, ka: fa, kq: fq, kd: fd, kr: fr},
+           "write_kib_raw": {kf: wf_, ka: wa, kq: wq, kd: wd, kr: wr},
            "copy_calibration": {"copy_bytes": copy_kib * 1024, "fetch_kib_raw": copy_fetch,
                                 "write_kib_raw": copy_write, "fetch_factor": ff, "write_factor": wf},
            "hbm_bytes": {"single_pass_kernel": round(fused), "two_pass_quant_kernel": round(quant),
-                         "two_pass_call": round(call), "delayed_kernel": round(delayed)},
+                         "two_pass_call": round(call), "delayed_kernel": round(delayed),
+                         "roof_kernel": round(roof)},
            "algorithmic_bytes_per_call": algorithmic_bytes(ROWS, COLS),
            "kernel_source_sha256": kernel_source_sha(), "commands": commands,
            "note": "KiB per dispatch, mean over dispatches; bytes = (fetch * fetch_factor + "
                    "write * write_factor) * 1024; FETCH_SIZE counts traffic beyond L2 (HBM and "
                    "Infinity Cache)"}
     with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def workload_bytes(name: str) -> int:
+    """Algorithmic bytes per call of a named workload (as workload_leg)."""
+    if name == "output_grad_16384x4096_sr":
+        R, C = 16384, 4096
+        return 2 * R * C + R * C + 2 * R * C // 16 + 8
+    import synth
+    counts = synth.moe_counts(8192, 64, 8, seed=4)
+    Rm, Rp, E = int(counts.sum()), int(sum((int(m) + 15) // 16 * 16 for m in counts)), 64
+    nbytes = 2 * Rm * 4096 + Rm * 4096 // 2 + Rm * 4096 // 16 + 4096 * Rp // 2 + 4096 * Rp // 16 + 2 * E * 4
+    return nbytes + (2 * E * 8 if name.endswith("delayed") else 0)
+
+
+def summarize_workload_counters(name, fetch, write, copy_cal, ff, wf, commands):
+    """Counter summary of a --workload run: calibrated HBM bytes per dispatch
+    of every kernel the call launches, and per call."""
+    per = {k: round((fetch[k] * ff + write.get(k, 0.0) * wf) * 1024) for k in fetch}
+    alg = workload_bytes(name)
+    out = {"workload": name, "hbm_bytes_per_dispatch": per, "hbm_bytes_per_call": sum(per.values()),
+           "algorithmic_bytes_per_call": alg, "traffic_over_algorithmic": round(sum(per.values()) / alg, 4),
+           "fetch_kib_raw": fetch, "write_kib_raw": write, "copy_calibration": copy_cal,
+           "kernel_source_sha256": kernel_source_sha(), "commands": commands,
+           "note": "KiB per dispatch, mean over dispatches; bytes = (fetch * fetch_factor + write * write_factor) "
+                   "* 1024; every kernel of the run is one per call"}
+    path = os.path.join(ROOT, "profiles", f"counters_{name}.json")
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
 
@@ -299,12 +342,81 @@ def variant_legs(torch, F, sets, stream, steps):
     return out
 
 
+WORKLOADS = ("output_grad_16384x4096_sr", "moe_65536x4096_grouped", "moe_65536x4096_grouped_delayed")
+
+
+def workload_leg(torch, F, synth, np, dev, stream, name):
+    """One call of a named workload other than the headline, on synthetic
+    input resident in HBM: (fn, algorithmic bytes per call, elements, the
+    buffers to keep alive)."""
+    if name == "output_grad_16384x4096_sr":
+        # output gradient dY, Laplace + outliers: RHT + E1M2 + stochastic rounding, row+col
+        R, C = 16384, 4096
+        g = torch.from_numpy(synth.output_grad(R, C, seed=3).view(np.int16)).to(dev)
+        c = F.config(F.GRID_E1M2, F.ROUND_STOCHASTIC, F.SCALE_NV16, rht=1, rht_seed=3, sr_seed=3)
+        row, col, ws = (F.alloc_layout(R, C, F.SCALE_NV16, device=dev), F.alloc_layout(C, R, F.SCALE_NV16, device=dev),
+                        F.Workspace(R, C, device=dev))
+        return (lambda: F.ufp4_quantize_rowcol(g, c, row, col, ws, stream),
+                2 * R * C + R * C + 2 * R * C // 16 + 8, R * C, (g, row, col, ws, c))
+    # MoE activation, 64 ragged expert segments: grouped RHT + E1M2, row+col
+    xm, off = synth.moe_activation(8192, 4096, 64, 8, seed=4)
+    Rm, E = xm.shape[0], 64
+    coff = F.ufp4_grouped_col_offsets(off, 16)
+    Rp = int(coff[-1])
+    x = torch.from_numpy(xm.view(np.int16)).to(dev)
+    offd = torch.from_numpy(off.astype(np.int64)).to(dev)
+    c = F.config(F.GRID_E1M2, F.ROUND_RTNE, F.SCALE_NV16, rht=1, rht_seed=4)
+    row = F.alloc_layout(Rm, 4096, F.SCALE_NV16, n_tensor_scales=E, device=dev)
+    col = F.alloc_layout(4096, Rp, F.SCALE_NV16, n_tensor_scales=E, device=dev)
+    ws = F.Workspace(Rm, 4096, E, device=dev)
+    nbytes = 2 * Rm * 4096 + Rm * 4096 // 2 + Rm * 4096 // 16 + 4096 * Rp // 2 + 4096 * Rp // 16 + 2 * E * 4
+    keep = (x, offd, row, col, ws, c)
+    if name == "moe_65536x4096_grouped":
+        return lambda: F.ufp4_quantize_grouped(x, offd, Rp, c, row, col, ws, stream), nbytes, Rm * 4096, keep
+    if name != "moe_65536x4096_grouped_delayed":
+        raise ValueError(name)
+    # delayed scaling, chained: each call reads the previous call's
+    # per-segment maxima (2 x 4 B per segment in, the same out)
+    amax = [torch.full((E, 2), 3.0, dtype=torch.float32, device=dev) for _ in range(2)]
+    state = [0]
+
+    def fn():
+        i = state[0]
+        state[0] ^= 1
+        F.ufp4_quantize_grouped_delayed(x, offd, Rp, c, amax[i], amax[i ^ 1], row, col, ws, stream)
+    return fn, nbytes + 2 * E * 8, Rm * 4096, keep + (amax,)
+
+
+def run_workload(torch, F, synth, np, args):
+    """Profiler runs of one named workload: warmup + K eager calls, one JSON
+    line with the mean call time (so that its kernels' counters and
+    durations are not mixed with other tensors')."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.set_stream(stream)
+    fn, nbytes, n_elem, keep = workload_leg(torch, F, synth, np, dev, stream, args.workload)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"workload": args.workload, "steps": args.steps, "ms_per_call": round(ms, 6),
+                      "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes_per_call": nbytes,
+                      "elements": n_elem}), flush=True)
+
+
 def extra_legs(torch, F, synth, np, dev, stream, steps):
     """Measurements reported beside the headline: a streaming-copy reference
     bandwidth; the weight workload's shrinkage sweep (SQNR, mean signed error
     and gain alpha per grid, RHT on and off); the output-gradient workload
     (SR, row+col) and the MoE workload (grouped, row+col) call times; and the
-    compounding of the GEMM gain through a chain of quantized layers."""
+    compounding of the GEMM gain through a chain of quantized layers; the
+    grouped delayed-scaling call on the MoE workload."""
     out = {}
     # streaming copy of 512 MiB on the same box (read + write)
     n = 512 * 1024 * 1024 // 4
@@ -355,30 +467,10 @@ def extra_legs(torch, F, synth, np, dev, stream, steps):
     out["weight_2048x8192_sweep"] = sweep
     del w, ws, q
 
-    # output gradient dY 16384 x 4096, Laplace + outliers: RHT + E1M2 + SR, row+col
-    R, C = 16384, 4096
-    g = torch.from_numpy(synth.output_grad(R, C, seed=3).view(np.int16)).to(dev)
-    c = F.config(F.GRID_E1M2, F.ROUND_STOCHASTIC, F.SCALE_NV16, rht=1, rht_seed=3, sr_seed=3)
-    row, col, ws = (F.alloc_layout(R, C, F.SCALE_NV16, device=dev), F.alloc_layout(C, R, F.SCALE_NV16, device=dev),
-                    F.Workspace(R, C, device=dev))
-    ms = timed(lambda: F.ufp4_quantize_rowcol(g, c, row, col, ws, stream), max(10, steps // 10))
-    out["output_grad_16384x4096_sr"] = rate(2 * R * C + R * C + 2 * R * C // 16 + 8, R * C, ms)
-    del g, row, col, ws
-    # MoE 65536 x 4096 in 64 ragged expert segments: grouped RHT + E1M2, row+col
-    xm, off = synth.moe_activation(8192, 4096, 64, 8, seed=4)
-    Rm = xm.shape[0]
-    coff = F.ufp4_grouped_col_offsets(off, 16)
-    Rp = int(coff[-1])
-    x = torch.from_numpy(xm.view(np.int16)).to(dev)
-    offd = torch.from_numpy(off.astype(np.int64)).to(dev)
-    c = F.config(F.GRID_E1M2, F.ROUND_RTNE, F.SCALE_NV16, rht=1, rht_seed=4)
-    row = F.alloc_layout(Rm, 4096, F.SCALE_NV16, n_tensor_scales=64, device=dev)
-    col = F.alloc_layout(4096, Rp, F.SCALE_NV16, n_tensor_scales=64, device=dev)
-    ws = F.Workspace(Rm, 4096, 64, device=dev)
-    ms = timed(lambda: F.ufp4_quantize_grouped(x, offd, Rp, c, row, col, ws, stream), max(10, steps // 10))
-    moe_bytes = 2 * Rm * 4096 + Rm * 4096 // 2 + Rm * 4096 // 16 + 4096 * Rp // 2 + 4096 * Rp // 16 + 2 * 64 * 4
-    out["moe_65536x4096_grouped"] = rate(moe_bytes, Rm * 4096, ms)
-    del x, row, col, ws
+    for name in ("output_grad_16384x4096_sr", "moe_65536x4096_grouped", "moe_65536x4096_grouped_delayed"):
+        fn, nbytes, n_elem, keep = workload_leg(torch, F, synth, np, dev, stream, name)
+        out[name] = rate(nbytes, n_elem, timed(fn, max(10, steps // 10)))
+        del fn, keep
     # compounding of the GEMM gain: 16 layers, 8192 tokens x 1024, orthogonal weights
     import fp4_quantization_amd.shrinkage as S
     T, D, L = 8192, 1024, 16
@@ -410,6 +502,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the legs beyond the headline workload's own (the profiler runs use it: those "
                          "legs launch the same kernels on other tensors)")
+    ap.add_argument("--workload", choices=WORKLOADS, default=None,
+                    help="profiler runs: time only this workload's call (no headline line)")
     ap.add_argument("--copy", action="store_true",
                     help="time a plain device copy of 512 MiB instead (bandwidth and counter calibration)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -419,16 +513,17 @@ def main():
     args = ap.parse_args()
     if args.summarize_counters:
         d = args.summarize_counters
-        summarize_counters(*d, commands=[
-            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[0]} -o run -- "
-            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --no-warm",
-            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[1]} -o run -- "
-            "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --no-warm",
+        run = (f"python3 bench.py --workload {args.workload} --steps 5 --warmup 2" if args.workload else
+               "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra --no-warm")
+        wl = f" --workload {args.workload}" if args.workload else ""
+        summarize_counters(*d, workload=args.workload, commands=[
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[0]} -o run -- {run}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[1]} -o run -- {run}",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[2]} -o run -- "
             "python3 bench.py --copy --steps 5 --warmup 2",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[3]} -o run -- "
             "python3 bench.py --copy --steps 5 --warmup 2",
-            f"python3 bench.py --summarize-counters {' '.join(d)}"])
+            f"python3 bench.py --summarize-counters {' '.join(d)}{wl}"])
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
@@ -446,6 +541,9 @@ def main():
 
     if args.copy:
         copy_bench(torch, args)
+        return
+    if args.workload:
+        run_workload(torch, F, synth, np, args)
         return
 
     dev = torch.device("cuda:0")
@@ -485,6 +583,17 @@ def main():
     ms_off, _ = time_graph(torch, off, args.steps, args.warmup, stream)
     ms_eager = time_eager(torch, on, args.steps, args.warmup, stream)
     ms_warm = None if args.no_warm else time_graph(torch, on[:1], args.steps, args.warmup, stream)[0]
+    # bandwidth reference: the same loads and output bytes with no arithmetic
+    roof_fns = []
+    for x, row, col, ws in sets:
+        ra = (ctypes.c_void_p(x.data_ptr()), ROWS, COLS, row.c(), col.c(), sptr)
+
+        def rfn(a=ra):
+            rc = F.lib.ufp4_roof_rowcol(*a)
+            if rc:
+                raise F.Ufp4Error("ufp4_roof_rowcol", rc)
+        roof_fns.append(rfn)
+    ms_roof, _ = time_graph(torch, roof_fns, args.steps, args.warmup, stream)
     # per-kernel durations: hipEvents around each kernel of one call, on the
     # launch stream, over calls that rotate through the buffer sets
     per_kernel = []
@@ -578,6 +687,9 @@ def main():
                   "amax_kernel_ms_median": round(float(np.median(k_amax)), 6),
                   "quant_kernel_ms_median": round(float(np.median(k_quant)), 6),
                   "event_call_ms_median": round(float(np.median(k_amax + k_quant)), 6),
+                  "roof_ms": round(ms_roof, 6),
+                  "roof_gbps": round(nbytes / (ms_roof * 1e-3) / 1e9, 1),
+                  "call_time_over_roof": round(ms / ms_roof, 4),
                   "rht_off_ms": round(ms_off, 6),
                   "rht_overhead": round(ms / ms_off - 1.0, 4),
                   "eager_launch_ms": round(ms_eager, 6),

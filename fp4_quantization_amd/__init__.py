@@ -22,7 +22,7 @@ __all__ = ["GRID_E1M2", "GRID_INT4", "GRID_E2M1", "GRID_E2M1C", "ROUND_RTNE", "R
            "SCALE_MX32", "SCHEDULE_AUTO", "SCHEDULE_TWO_PASS", "SCHEDULE_SINGLE_PASS", "ufp4_set_schedule",
            "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_grouped_delayed", "ufp4_quantize_rowcol_noalloc", "ufp4_quantize_delayed", "ufp4_gemm_nt", "LIB_PATH", "Ufp4Error", "config", "QTensor", "Workspace", "alloc_layout",
            "ufp4_quantize", "ufp4_quantize_rowcol", "ufp4_quantize_grouped", "ufp4_dequantize",
-           "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol",
+           "ufp4_stats", "ufp4_round_f32", "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol", "ufp4_roof_rowcol",
            "block_len", "ufp4_recipe_config", "RECIPE_UFP4", "RECIPE_UFP4_INT4", "RECIPE_NVFP4",
            "GEMM_FWD_Y", "GEMM_BWD_DX", "GEMM_BWD_DW", "OPERAND_A", "OPERAND_B", "TENSOR_X", "TENSOR_W",
            "TENSOR_DY", "ufp4_f32_to_bf16"]
@@ -217,6 +217,17 @@ def ufp4_time_rowcol(x: torch.Tensor, cfg: ufp4_config, row_out: QTensor, col_ou
                                                    col_out.c(), ws.ptr, ws.nbytes, _stream(stream),
                                                    ctypes.byref(a), ctypes.byref(b)))
     return a.value, b.value
+
+
+def ufp4_roof_rowcol(x: torch.Tensor, row_out: QTensor, col_out: QTensor, stream=None) -> None:
+    """The memory traffic of a row+col call on x with no arithmetic (a
+    bandwidth reference): the quantization kernels' loads, and every byte of
+    both layouts' codes and block scales written (as zeros, unless a lane's
+    input words xor to one fixed constant).  rows % 128 == 0, cols % 256 == 0."""
+    rows, cols, ld = _bf16_view(x)
+    if ld != cols:
+        raise ValueError("the roof hook takes a contiguous tensor")
+    check("ufp4_roof_rowcol", lib.ufp4_roof_rowcol(_ptr(x), rows, cols, row_out.c(), col_out.c(), _stream(stream)))
 
 
 def ufp4_dequantize(q: QTensor, rows: int, cols: int, cfg: ufp4_config, inverse_rht: bool,

@@ -32,7 +32,7 @@ EXPORTED = ["ufp4_status_string", "ufp4_workspace_size", "ufp4_workspace_init",
             "ufp4_rht_signs", "ufp4_grouped_col_offsets", "ufp4_time_rowcol", "ufp4_set_schedule",
             "ufp4_schedule_of", "ufp4_amax_tiles", "ufp4_quantize_delayed", "ufp4_gemm_nt",
             "ufp4_recipe_config", "ufp4_f32_to_bf16", "ufp4_quantize_rowcol_noalloc",
-            "ufp4_quantize_grouped_delayed"]
+            "ufp4_quantize_grouped_delayed", "ufp4_roof_rowcol"]
 
 
 class Ufp4Error(RuntimeError):
@@ -101,6 +101,8 @@ def _load():
     L.ufp4_time_rowcol.restype = ctypes.c_int
     L.ufp4_time_rowcol.argtypes = [P, i64, i64, i64, cfgp, ufp4_qtensor, ufp4_qtensor, P, sz, P,
                                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]
+    L.ufp4_roof_rowcol.restype = ctypes.c_int
+    L.ufp4_roof_rowcol.argtypes = [P, i64, i64, ufp4_qtensor, ufp4_qtensor, P]
     L.ufp4_rht_signs.restype = ctypes.c_int
     L.ufp4_rht_signs.argtypes = [u64, P]
     L.ufp4_grouped_col_offsets.restype = ctypes.c_int

@@ -425,6 +425,32 @@ int ufp4_time_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, 
   return rc;
 }
 
+int ufp4_roof_rowcol(const uint16_t* x, int64_t rows, int64_t cols, ufp4_qtensor row_out, ufp4_qtensor col_out,
+                     ufp4_stream_t stream) {
+  if (!x || !row_out.codes || !row_out.scales || !col_out.codes || !col_out.scales) return UFP4_ERR_INVALID_ARGUMENT;
+  if (rows <= 0 || cols <= 0 || rows % kTileRows || cols % kBandCols || rows >= kMaxDim || cols >= kMaxDim)
+    return UFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(row_out.codes, 16) || !aligned(row_out.scales, 16) ||
+      !aligned(col_out.codes, 16) || !aligned(col_out.scales, 8))
+    return UFP4_ERR_ALIGNMENT;
+  QuantParams p = {};
+  p.x = x;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld = cols;
+  p.num_groups = 1;
+  p.block = 16;
+  p.padded_rows = rows;
+  p.row_codes = row_out.codes;
+  p.row_scales = row_out.scales;
+  p.col_codes = col_out.codes;
+  p.col_scales = col_out.scales;
+  const int64_t grid = grid_size_quant(rows, cols, 1, 16, &p.n_band, &p.n_tiles);
+  p.n_work = p.n_band * p.n_tiles;
+  if (grid > 0x7FFFFFFF) return UFP4_ERR_SHAPE;
+  return launch_roof(p, grid, (hipStream_t)stream) == hipSuccess ? UFP4_OK : UFP4_ERR_HIP;
+}
+
 int ufp4_quantize_grouped(const uint16_t* x, int64_t total_rows, int64_t cols,
                           const int64_t* offsets_dev, int32_t num_groups, int64_t padded_rows,
                           const ufp4_config* cfg, ufp4_qtensor row_out, ufp4_qtensor col_out, void* ws,

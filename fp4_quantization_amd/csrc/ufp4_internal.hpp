@@ -88,6 +88,7 @@ hipError_t launch_delayed(const QuantParams& p, int64_t grid, hipStream_t s, hip
 // tensor scales from p.amax_in[e], per-segment maxima folded into
 // p.amax_out[e] (zeroed beforehand) when it is not null.
 hipError_t launch_grouped_delayed(const QuantParams& p, int64_t grid, hipStream_t s);
+hipError_t launch_roof(const QuantParams& p, int64_t grid, hipStream_t s);
 // The single-pass schedule (dense NV16 tensors of at most kMaxFusedTiles
 // tiles): one kernel, every tile kept in registers across a device-wide
 // exchange of the tile maxima.

@@ -1023,6 +1023,45 @@ __global__ __launch_bounds__(kThreads) void ufp4_grouped_delayed_kernel(QuantPar
   }
 }
 
+// ------------------------------------------------------- bandwidth roof
+// The memory traffic of a dense NV16 row+col call with no arithmetic: the
+// same tile walk (XCD-aware order) and 16-byte non-temporal loads of the
+// lane sub-tiles as the quantization kernels, and the call's output bytes
+// (both layouts' codes and block scales) as coalesced non-temporal stores.
+// The stored value is the loaded words folded to one word and compared with
+// a constant, so every load is live; it is zero unless a lane's 64 words
+// xor to that constant.  Full tiles only (rows a multiple of 128, columns of
+// 256; the host checks).
+__global__ __launch_bounds__(kThreads) void ufp4_roof_kernel(QuantParams p) {
+  const TileInfo T = dense_tile(p, remap_xcd((int32_t)blockIdx.x, (int32_t)gridDim.x));
+  if (!T.active) return;
+  const LaneGeom L = lane_geom(p, T);
+  uint32_t w[16][4];
+  load_rows<0, 16, true>(p, T, L, w);
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc ^= w[i][0] ^ w[i][1] ^ w[i][2] ^ w[i][3];
+  const uint32_t z = (acc == 0x9E3779B9u) ? 1u : 0u;
+  const u32x4 o = {z, z, z, z};
+  const int t = threadIdx.x;
+  const int64_t c0 = (int64_t)T.band * kBandCols;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // row-wise codes: 128 rows x 128 bytes
+    const int i = t + kThreads * j, r = i >> 3, k = i & 7;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p.row_codes + (T.m0 + r) * (p.cols / 2) + c0 / 2 + 16 * k));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // column-wise codes: 256 columns x 64 bytes
+    const int i = t + kThreads * j, c = i >> 2, k = i & 3;
+    __builtin_nontemporal_store(
+        o, reinterpret_cast<u32x4*>(p.col_codes + (c0 + c) * (p.padded_rows / 2) + T.m0 / 2 + 16 * k));
+  }
+  if (t < kTileRows)  // row-wise scales: 16 bytes per row
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p.row_scales + (T.m0 + t) * (p.cols / 16) + c0 / 16));
+  const u32x2 o2 = {z, z};  // column-wise scales: 8 bytes per column
+  __builtin_nontemporal_store(o2, reinterpret_cast<u32x2*>(p.col_scales + (c0 + t) * (p.padded_rows / 16) + T.m0 / 16));
+}
+
 // ------------------------------------------------------- single pass
 // One kernel for a dense NV16 tensor whose tiles the device can hold at
 // once: each workgroup loads its tile, computes the tile maxima (phase A),
@@ -1745,6 +1784,11 @@ hipError_t launch_fused(const QuantParams& p, int64_t grid, hipStream_t s, hipEv
     case kGridE2M1C: return launch_fused_grid<kGridE2M1C>(p, grid, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_roof(const QuantParams& p, int64_t grid, hipStream_t s) {
+  launch(ufp4_roof_kernel, p, grid, s, nullptr, nullptr);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill(uint32_t* ptr, int64_t n, uint32_t value, hipStream_t s) {

@@ -429,6 +429,21 @@ int ufp4_time_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                      void* ws, size_t ws_bytes, ufp4_stream_t stream, float* ms_amax_host,
                      float* ms_quant_host);
 
+/* Measurement hook (not part of the quantization path): the memory traffic
+ * of a dense NV16 ufp4_quantize_rowcol call on the same tensor with no
+ * arithmetic, for the bandwidth this access pattern attains.  Reads the
+ * rows x cols bf16 tensor x (ld = cols) with the quantization kernels' tile
+ * walk and 16-byte loads, and writes every byte of both layouts' codes and
+ * block scales (row_out: rows x cols, col_out: cols x rows, as
+ * ufp4_quantize_rowcol) with coalesced 16-byte stores; tensor scales are not
+ * touched.  The bytes written are zero unless a lane's 64 input words xor to
+ * one fixed constant.  rows must be a multiple of 128 and cols of 256
+ * (UFP4_ERR_SHAPE); x, the codes and the row-wise scales 16-byte and the
+ * column-wise scales 8-byte aligned (UFP4_ERR_ALIGNMENT); null pointers give
+ * UFP4_ERR_INVALID_ARGUMENT.  Asynchronous on `stream`. */
+int ufp4_roof_rowcol(const uint16_t* x, int64_t rows, int64_t cols, ufp4_qtensor row_out, ufp4_qtensor col_out,
+                     ufp4_stream_t stream);
+
 /* The 16 signs (+1/-1) selected by rht_seed (host memory). */
 int ufp4_rht_signs(uint64_t rht_seed, int8_t signs_host[16]);
 

@@ -129,6 +129,14 @@ int main() {
   EXPECT(ufp4_time_rowcol(x, 8192, 2048, 2048, &ok, row, col, ws, wsb, nullptr, nullptr, &tq),
          UFP4_ERR_INVALID_ARGUMENT);
 
+  // bandwidth roof hook: full tiles only
+  EXPECT(ufp4_roof_rowcol(x, 8192, 2048, row, col, nullptr), UFP4_OK);
+  EXPECT(ufp4_roof_rowcol(x, 8192 + 16, 2048, row, col, nullptr), UFP4_ERR_SHAPE);
+  EXPECT(ufp4_roof_rowcol(x, 8192, 2048 + 16, row, col, nullptr), UFP4_ERR_SHAPE);
+  EXPECT(ufp4_roof_rowcol(x, 0, 2048, row, col, nullptr), UFP4_ERR_SHAPE);
+  EXPECT(ufp4_roof_rowcol(nullptr, 8192, 2048, row, col, nullptr), UFP4_ERR_INVALID_ARGUMENT);
+  EXPECT(ufp4_roof_rowcol(x + 1, 8192, 2048, row, col, nullptr), UFP4_ERR_ALIGNMENT);
+
   // the no-allocation variant: argument errors first, then the size limit;
   // a valid call needs the device's scratch array, which a GPU-less run
   // cannot look up (UFP4_ERR_HIP), or runs to the stubbed launches

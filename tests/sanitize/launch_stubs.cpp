@@ -54,6 +54,13 @@ hipError_t launch_fused(const QuantParams& p, int64_t grid, hipStream_t, hipEven
   require(p.fs_gen != nullptr && p.fs_words != nullptr && p.n_work <= kMaxFusedTiles && !p.mx, "single pass");
   return quant_launch(p, grid, "single pass");
 }
+hipError_t launch_roof(const QuantParams& p, int64_t grid, hipStream_t) {
+  ++g_stub_calls;
+  require(p.x && p.row_codes && p.row_scales && p.col_codes && p.col_scales, "roof outputs");
+  require(p.rows % kTileRows == 0 && p.cols % kBandCols == 0 && p.padded_rows == p.rows && p.ld == p.cols, "roof shape");
+  require(p.n_work == p.n_band * p.n_tiles && grid >= p.n_work && grid % kNumXcd == 0, "roof grid");
+  return g_stub_result;
+}
 hipError_t launch_fill(uint32_t* ptr, int64_t n, uint32_t, hipStream_t) {
   ++g_stub_calls;
   require(ptr != nullptr && n >= 0, "fill");

@@ -622,6 +622,26 @@ def test_grouped_delayed_single_layouts_and_bad_offsets(env):
     assert bool((rqb.codes == 0xAB).all())
 
 
+def test_roof_hook_writes_every_output_byte(env):
+    # the bandwidth reference writes zeros over every code and block-scale
+    # byte of both layouts (which start as 0xAB) and leaves the tensor scales
+    torch, F, orc = env
+    R, C = 384, 768
+    x = to_dev(torch, synth.activation(R, C, seed=19))
+    row, col = F.alloc_layout(R, C, NV16), F.alloc_layout(C, R, NV16)
+    for q in (row, col):
+        q.codes.fill_(0xAB)
+        q.scales.fill_(0xAB)
+        q.tensor_scale.fill_(2.0)
+    F.ufp4_roof_rowcol(x, row, col)
+    torch.cuda.synchronize()
+    for q in (row, col):
+        assert int(q.codes.count_nonzero()) == 0 and int(q.scales.count_nonzero()) == 0
+        assert bool((q.tensor_scale == 2.0).all())
+    with pytest.raises(F.Ufp4Error):
+        F.ufp4_roof_rowcol(x[:, :512].contiguous()[:200], row, col)
+
+
 # ------------------------------------------------------- dequantize / stats
 @pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
 @pytest.mark.parametrize("scaling", [NV16, MX32])
