@@ -217,32 +217,53 @@ __device__ __forceinline__ uint32_t round_rtne(float y) {
 
 // Stochastic rounding: with lo <= |y| < hi adjacent grid magnitudes and
 // frac = (|y| - lo) / (hi - lo) (exact), round up iff r < ceil(frac * 2^32).
+//
+// Uniform grids (E1M2, E2M1C: step 1/2; INT4: step 1): t = |y| / step is
+// exact, lo = floor(t), frac = t - floor(t).  t is clamped to [0, top] by
+// one median (a NaN operand makes v_med3_f32 return the smallest of the
+// three, 0 here, so NaN gives index 0; +inf and everything at or above the
+// top give the top with frac 0).  A signaling NaN is quieted first (free
+// when y is the result of arithmetic), since the median treats it otherwise.
+// Returns the magnitude index.
+template <int GRID>
+__device__ __forceinline__ uint32_t sr_uniform_index(float y, uint32_t r) {
+  constexpr float kInvStep = GRID == kGridINT4 ? 1.0f : 2.0f;
+  const float t = __builtin_amdgcn_fmed3f(__builtin_canonicalizef(fabsf(y) * kInvStep), 0.0f,
+                                          (float)grid_top<GRID>());
+  const uint32_t lo = (uint32_t)t;
+  const uint32_t thr = (uint32_t)ceilf(__builtin_amdgcn_fractf(t) * 4294967296.0f);
+  return lo + (r < thr ? 1u : 0u);
+}
+
+// The same as a two's-complement integer carrying the sign of y (0 for a
+// zero index, whatever the sign), for the packing paths whose nibbles are
+// converted to sign-magnitude eight at a time.
+template <int GRID>
+__device__ __forceinline__ uint32_t sr_uniform_tc(float y, uint32_t r) {
+  const uint32_t k = sr_uniform_index<GRID>(y, r);
+  const uint32_t s = (uint32_t)((int32_t)__float_as_uint(y) >> 31);
+  return (k ^ s) - s;
+}
+
 template <int GRID>
 __device__ __forceinline__ uint32_t round_sr(float y, uint32_t r) {
-  const float a = fabsf(y);
-  if (!(a == a)) return 0u;
   uint32_t k;
-  if (a >= grid_qmax<GRID>()) {
-    k = grid_top<GRID>();
-  } else {
-    float lo_idx, frac;
-    if (GRID == kGridE1M2 || GRID == kGridE2M1C) {
-      const float t = a + a;
-      lo_idx = floorf(t);
-      frac = t - lo_idx;
-    } else if (GRID == kGridINT4) {
-      lo_idx = floorf(a);
-      frac = a - lo_idx;
+  if (GRID == kGridE2M1) {
+    const float a = fabsf(y);
+    if (!(a == a)) return 0u;
+    if (a >= grid_qmax<GRID>()) {
+      k = grid_top<GRID>();
     } else {
       const uint32_t i = (uint32_t)(a >= 0.5f) + (uint32_t)(a >= 1.0f) + (uint32_t)(a >= 1.5f) +
                          (uint32_t)(a >= 2.0f) + (uint32_t)(a >= 3.0f) + (uint32_t)(a >= 4.0f);
       const float lo = i < 4u ? 0.5f * (float)i : (i == 4u ? 2.0f : (i == 5u ? 3.0f : 4.0f));
       const float rw = i < 4u ? 2.0f : (i == 6u ? 0.5f : 1.0f);  // 1 / bucket width
-      lo_idx = (float)i;
-      frac = (a - lo) * rw;
+      const float frac = (a - lo) * rw;
+      const uint32_t thr = (uint32_t)ceilf(frac * 4294967296.0f);
+      k = i + (r < thr ? 1u : 0u);
     }
-    const uint32_t thr = (uint32_t)ceilf(frac * 4294967296.0f);
-    k = (uint32_t)lo_idx + (r < thr ? 1u : 0u);
+  } else {
+    k = sr_uniform_index<GRID>(y, r);
   }
   return k ? make_code<GRID>(k, y) : 0u;
 }

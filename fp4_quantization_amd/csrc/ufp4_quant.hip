@@ -290,6 +290,13 @@ __device__ __forceinline__ uint32_t push_nibble(uint32_t m, uint32_t acc) {
   return __builtin_amdgcn_alignbit(m, acc, 4u);
 }
 
+// t clamped to [-top, top], NaN to a zero: the median of |t|, 0 and top (a
+// NaN operand makes v_med3_f32 return the smallest of the three, 0 here; t
+// is the result of arithmetic, so never a signaling NaN), with t's sign.
+__device__ __forceinline__ float clamp_top(float t, float top) {
+  return __builtin_copysignf(__builtin_amdgcn_fmed3f(fabsf(t), 0.0f, top), t);
+}
+
 // fl(t + 1.5*2^23) has t rounded to the nearest integer (ties to even) in
 // its low mantissa bits, as a two's-complement value, for |t| < 2^22.
 constexpr float kMagic = 12582912.0f;
@@ -490,6 +497,7 @@ using ColStage = ColStageT<8>;
 template <int GRID, bool SR>
 struct GridTraits {
   static constexpr bool kFast = !SR && GRID != kGridE2M1;      // uniform grids
+  static constexpr bool kFastSR = SR && GRID != kGridE2M1;     // uniform grids, stochastic
   static constexpr float kMul = GRID == kGridINT4 ? 1.0f : 2.0f;  // grid step -> integer
   static constexpr float kTop = (float)grid_top<GRID>();          // clamp, in grid steps
 };
@@ -546,7 +554,7 @@ __device__ __forceinline__ float row_pass(const QuantParams& p, const TileInfo& 
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           float t = v[r][j] * mult;
-          if (MX || DELAYED) t = __builtin_amdgcn_fmed3f(t, -G::kTop, G::kTop);
+          if (MX || DELAYED) t = clamp_top(t, G::kTop);
           acc = push_nibble(__float_as_uint(t + kMagic), acc);
         }
         packed[r] = GRID == kGridINT4 ? acc : tc_to_signmag8(acc);
@@ -555,7 +563,16 @@ __device__ __forceinline__ float row_pass(const QuantParams& p, const TileInfo& 
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const int i = NR * g4 + r;
-        if (SR) {
+        if (G::kFastSR) {
+          const uint64_t base = (uint64_t)(T.seg_row0 + L.m_h0 + i) * (uint64_t)C + (uint64_t)L.c0;
+          const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
+          const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
+          const uint32_t rw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+          uint32_t acc = 0u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc = push_nibble(sr_uniform_tc<GRID>((v[r][j] * fin) * inv[r], rw[j]), acc);
+          packed[r] = GRID == kGridINT4 ? acc : tc_to_signmag8(acc);
+        } else if (SR) {
           const uint64_t base = (uint64_t)(T.seg_row0 + L.m_h0 + i) * (uint64_t)C + (uint64_t)L.c0;
           const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
           const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
@@ -633,8 +650,8 @@ __device__ __forceinline__ float col_pass(const QuantParams& p, const TileInfo& 
         for (int j = 0; j < 8; ++j) {
           float t0 = v[r][j] * mult, t1 = v[r][8 + j] * mult;
           if (MX || DELAYED) {
-            t0 = __builtin_amdgcn_fmed3f(t0, -G::kTop, G::kTop);
-            t1 = __builtin_amdgcn_fmed3f(t1, -G::kTop, G::kTop);
+            t0 = clamp_top(t0, G::kTop);
+            t1 = clamp_top(t1, G::kTop);
           }
           a0 = push_nibble(__float_as_uint(t0 + kMagic), a0);
           a1 = push_nibble(__float_as_uint(t1 + kMagic), a1);
@@ -645,7 +662,21 @@ __device__ __forceinline__ float col_pass(const QuantParams& p, const TileInfo& 
     } else {
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        if (SR) {
+        if (G::kFastSR) {
+          const int64_t cglob = L.c0 + 2 * g2 + r;
+          const uint64_t base = (uint64_t)cglob * (uint64_t)p.padded_rows + (uint64_t)(T.coff + L.m_h0);
+          uint32_t acc[2] = {0u, 0u};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const Ctr4 rr = sr_words4((base >> 2) + q, 1u, p.sr_k0, p.sr_k1);
+            const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[q >> 1] = push_nibble(sr_uniform_tc<GRID>((v[r][4 * q + j] * fin) * inv[r], rw[j]), acc[q >> 1]);
+          }
+          lo[r] = GRID == kGridINT4 ? acc[0] : tc_to_signmag8(acc[0]);
+          hi[r] = GRID == kGridINT4 ? acc[1] : tc_to_signmag8(acc[1]);
+        } else if (SR) {
           const int64_t cglob = L.c0 + 2 * g2 + r;
           const uint64_t base = (uint64_t)cglob * (uint64_t)p.padded_rows + (uint64_t)(T.coff + L.m_h0);
           uint32_t word[4];
@@ -740,7 +771,7 @@ __device__ __forceinline__ float2 quant_tile(const QuantParams& p, const TileInf
   }
   const RowLaneSigns rs = row_lane_signs<RHT>(p, L.lc & 1);
   if (p.do_row) {
-    tile_r = row_pass<GRID, SR, MX, RHT, DELAYED>(
+    tile_r = row_pass<GRID, SR, MX, RHT, DELAYED, SR ? 2 : 4>(
         p, T, L, tsr, lut[0], rs.fin, [&](int i, float(&v)[8]) __attribute__((always_inline)) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -1618,7 +1649,7 @@ __global__ __launch_bounds__(kThreads, 2) void ufp4_single_kernel(QuantParams p)
     int parity = L.lc & 1;
     asm volatile("" : "+v"(parity));
     const RowLaneSigns rs = row_lane_signs<RHT>(p, parity);
-    row_pass<GRID, SR, false, RHT, false>(
+    row_pass<GRID, SR, false, RHT, false, SR ? 2 : 4>(
         p, T, L, tsr, lut[0], rs.fin, [&](int i, float(&v)[8]) __attribute__((always_inline)) {
           const uint4 u = wl[i][threadIdx.x];
           v[0] = bf_lo(u.x);

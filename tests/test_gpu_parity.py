@@ -192,6 +192,39 @@ def test_edge_values(env):
                     assert_layout_equal(col, orc.quantize(xb, oc, COL), f"{name} col")
 
 
+def nonfinite_input(R, C, seed, inf=True):
+    """Normal values with about 1% NaN and (if inf) 1% each of +-inf, bf16."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((R, C)).astype(np.float32)
+    u = rng.random((R, C))
+    x[u < 0.01] = np.nan
+    if inf:
+        x[(u >= 0.01) & (u < 0.02)] = np.inf
+        x[(u >= 0.02) & (u < 0.03)] = -np.inf
+    return synth.f32_to_bf16(x)
+
+
+@pytest.mark.parametrize("rht", [0, 1])
+@pytest.mark.parametrize("sched", [TWO_PASS, SINGLE_PASS])
+def test_nonfinite_inputs(env, schedule, rht, sched):
+    # NaN codes to 0 and is left out of every maximum; +-inf saturates (and,
+    # through the transform, turns its block into NaN and inf values); with
+    # inf present the tensor scale is inf.  Both with and without inf.
+    torch, F, orc = env
+    schedule(sched)
+    R, C = 96, 160
+    for inf in (False, True):
+        xb = nonfinite_input(R, C, seed=31 + rht, inf=inf)
+        for grid in (E1M2, INT4, E2M1, E2M1C):
+            for scaling in (NV16, MX32):
+                for rounding in (RTNE, SR):
+                    say(f"[nonfinite] inf={inf} rht={rht} sched={sched} grid={grid} scl={scaling} rnd={rounding}")
+                    fc, oc = cfgs(F, orc, grid, rounding, scaling, rht, rht_seed=5, sr_seed=5)
+                    row, col = gpu_rowcol(env, xb, fc)
+                    assert_layout_equal(row, orc.quantize(xb, oc, ROW), "nonfinite row")
+                    assert_layout_equal(col, orc.quantize(xb, oc, COL), "nonfinite col")
+
+
 def test_empty_tensor(env):
     torch, F, orc = env
     fc, _ = cfgs(F, orc)
