@@ -33,7 +33,8 @@ Reported beside the headline, under "extra" (never as the value): a
 bandwidth reference on the same buffers (ufp4_roof_rowcol: the quantization
 kernels' loads and the call's output bytes with no arithmetic), the RHT-off
 call, the E2M1, INT4 and MX32 variants of the call, the other schedule,
-delayed scaling, the consumer GEMM, a streaming
+delayed scaling, the consumer GEMM (NV16 on the fp16 MFMA; MX32 on the scaled
+f8f6f4 MFMA), a streaming
 copy of 512 MiB on the same box, the weight workload's shrinkage sweep (SQNR,
 mean signed error in grid units and gain alpha per grid, RHT on and off),
 the output-gradient workload (stochastic rounding, row+col) and MoE workload
@@ -629,6 +630,21 @@ def main():
     gemm_steps = 20
     ms_gemm, _ = time_graph(torch, gemm_fns, gemm_steps, 3, stream)
     gemm_tflops = 2.0 * ROWS * ROWS * COLS / (ms_gemm * 1e-3) / 1e12
+    # the same product with MX32 operands on the scaled f8f6f4 MFMA: E2M1
+    # codes as FP4 (peak 10.1 PFLOP/s), E1M2 codes expanded to FP8 (5.0)
+    mx_gemm = {}
+    for gname, g, peak in (("e2m1_fp4", F.GRID_E2M1, 10100.0), ("e1m2_fp8", F.GRID_E1M2, 5000.0)):
+        cm = F.config(g, F.ROUND_RTNE, F.SCALE_MX32, rht=1, rht_seed=1)
+        xm = F.alloc_layout(ROWS, COLS, F.SCALE_MX32, device=dev)
+        wm = F.alloc_layout(ROWS, COLS, F.SCALE_MX32, device=dev)
+        F.ufp4_quantize(x0, cm, xm, sets[0][3])
+        F.ufp4_quantize(wx, cm, wm, sets[0][3])
+        ms_m, _ = time_graph(torch, [lambda: F.ufp4_gemm_nt(cm, xm, wm, ROWS, ROWS, COLS, gc, stream)],
+                             gemm_steps, 3, stream)
+        tf = 2.0 * ROWS * ROWS * COLS / (ms_m * 1e-3) / 1e12
+        mx_gemm[f"gemm_mx32_{gname}"] = {"ms": round(ms_m, 6), "tflops": round(tf, 1),
+                                         "frac_of_peak": round(tf / peak, 4)}
+        del xm, wm
     del gc
     # the other schedule on the same buffers, for comparison
     other = "two_pass" if single else "single_pass"
@@ -701,6 +717,7 @@ def main():
     line["extra"]["gemm_8192x8192x2048_ms"] = round(ms_gemm, 6)
     line["extra"]["gemm_tflops"] = round(gemm_tflops, 1)
     line["extra"]["gemm_frac_of_fp16_mfma_peak"] = round(gemm_tflops / 2500.0, 4)
+    line["extra"].update(mx_gemm)
     line["extra"]["delayed_scaling_ms"] = round(ms_delayed, 6)
     line["extra"]["delayed_scaling_gbps"] = round(nbytes / (ms_delayed * 1e-3) / 1e9, 2)
     if ms_warm is not None:

@@ -206,7 +206,6 @@ int ufp4_gemm_nt(const ufp4_config* cfg, int64_t M, int64_t N, int64_t K, ufp4_q
                  float* c, int64_t ldc, ufp4_stream_t stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
-  if (cfg->scaling != UFP4_SCALE_NV16) return UFP4_ERR_INVALID_ARGUMENT;
   if (M < 0 || N < 0 || K < 0 || ldc < N) return UFP4_ERR_INVALID_ARGUMENT;
   if (K % 32) return UFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return UFP4_OK;
@@ -230,6 +229,7 @@ int ufp4_gemm_nt(const ufp4_config* cfg, int64_t M, int64_t N, int64_t K, ufp4_q
   p.K = K;
   p.ldc = ldc;
   p.grid = cfg->grid;
+  p.mx = cfg->scaling == UFP4_SCALE_MX32;
   if (launch_gemm(p, (hipStream_t)stream) != hipSuccess) return UFP4_ERR_HIP;
   return UFP4_OK;
 }

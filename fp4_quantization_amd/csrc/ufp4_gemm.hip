@@ -244,8 +244,203 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
       }
 }
 
+// ------------------------------------------------------------------ MX32
+// MX32 operands multiply on the scaled f8f6f4 MFMA (32 x 32 x 64, fp32
+// accumulation), which takes one E8M0 scale per 32 elements along K per
+// operand row: exactly the MX32 block scale, so no dequantization happens
+// outside the matrix core.  Operand formats: E2M1 codes (and E2M1C codes,
+// whose magnitudes 0..2 are E2M1 values with the same encodings) are OCP
+// FP4 values as stored; E1M2 (k/2) and INT4 (k) values are exact in OCP FP8
+// E4M3 and are expanded to it byte by byte.  The products of the scaled
+// values are exact (a few significant bits times powers of two inside fp32's
+// range), so c differs from the exact sum only by the accumulation order.
+//
+// Lane layout of v_mfma_scale_f32_32x32x64_f8f6f4 (measured on gfx950 with
+// an in-bounds probe against a host model): lane l holds row (column of B)
+// l % 32 and 32 values of the 64-element K slice; FP4: K positions
+// 32 (l / 32) .. +31 in nibble order; FP8: 16 (l / 32) .. +15 in bytes 0..15
+// and 32 + 16 (l / 32) .. +15 in bytes 16..31; its scale register holds the
+// E8M0 byte of block l / 32 of the slice for that row.  The 32 x 32 result
+// is laid out as for the other 32 x 32 MFMAs.
+//
+// Tiles are 256 x 256 per workgroup of 8 waves (each 64 x 128 as 2 x 4 MFMA
+// tiles), K steps of 128 (two slices), double-buffered in LDS: each thread
+// stages one half (64 K values: two MX blocks) of one A row and one B row
+// per step, requested one step ahead.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+template <int GRID>
+struct MxFmt {
+  static constexpr bool kFp4 = GRID == kGridE2M1 || GRID == kGridE2M1C;
+  static constexpr int kFmt = kFp4 ? 4 : 0;      // cbsz / blgp: FP4 E2M1 or FP8 E4M3
+  static constexpr int kRowBytes = kFp4 ? 64 : 128;  // one K step of 128 values
+  static constexpr int kPitch = kRowBytes + 16;  // LDS row pitch (spreads fragment reads over banks)
+};
+constexpr int kMxK = 128;
+
+// Eight codes (element 2i in the low nibble of byte i) to eight E4M3 bytes
+// (element e in byte e of out[e / 4]) for E1M2 (k/2) or INT4 (k); the sign
+// bit of a code becomes the E4M3 sign (a negative zero stays zero).
+template <int GRID>
+__device__ __forceinline__ void expand8_e4m3(uint32_t word, uint32_t out[2]) {
+  if (GRID == kGridINT4) word = signmag8(word);
+  // E4M3 encodings of the magnitudes 0..7 (low word 0..3, high word 4..7)
+  const uint32_t lo = GRID == kGridINT4 ? 0x44403800u : 0x3C383000u;  // {0,1,2,3} / {0,.5,1,1.5}
+  const uint32_t hi = GRID == kGridINT4 ? 0x4E4C4A48u : 0x46444240u;  // {4..7} / {2,2.5,3,3.5}
+  const uint32_t he = (uint32_t)__builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(hi, lo, word & 0x07070707u),
+                                                             word << 4, 0x80808080u, 0xF8);
+  const uint32_t ho = (uint32_t)__builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(hi, lo, (word >> 4) & 0x07070707u),
+                                                             word, 0x80808080u, 0xF8);
+  out[0] = __builtin_amdgcn_perm(ho, he, 0x05010400u);  // elements 0..3
+  out[1] = __builtin_amdgcn_perm(ho, he, 0x07030602u);  // elements 4..7
+}
+
+template <int GRID>
+__global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p) {
+  using Fm = MxFmt<GRID>;
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][kGemmM][Fm::kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGemmN][Fm::kPitch];
+  __shared__ uint8_t Ss[2][2][kGemmM][4];  // [buffer][operand][row][block of the step]
+  const int64_t m0 = (int64_t)blockIdx.y * kGemmM, n0 = (int64_t)blockIdx.x * kGemmN;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
+  const int lr = t >> 1, h = t & 1;  // staged row, half of the K step
+  const int64_t am = m0 + lr, bn = n0 + lr;
+  const bool a_ok = am < p.M, b_ok = bn < p.N;
+  const int64_t kc = p.K / 2, ks = p.K / 32;
+  const uint8_t* ac = p.a_codes + (a_ok ? am : 0) * kc + 32 * h;
+  const uint8_t* as = p.a_scales + (a_ok ? am : 0) * ks + 2 * h;
+  const uint8_t* bc = p.b_codes + (b_ok ? bn : 0) * kc + 32 * h;
+  const uint8_t* bs = p.b_scales + (b_ok ? bn : 0) * ks + 2 * h;
+  const int64_t nsteps = (p.K + kMxK - 1) / kMxK;
+  // codes of the thread's two blocks (16 bytes each) and their scale bytes;
+  // a block past K (or a row past M / N) is zero with scale 2^0
+  struct Stage {
+    g32x4 a[2], b[2];
+    uint32_t sa, sb;
+  };
+  auto fetch = [&](int64_t st) {
+    Stage f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      // addresses stay inside the operands whether or not the load is used
+      const bool in = st * kMxK + 64 * h + 32 * q + 32 <= p.K;
+      const int64_t off = in ? st * (kMxK / 2) + 16 * q : 0;
+      f.a[q] = (in && a_ok) ? *reinterpret_cast<const g32x4*>(ac + off) : g32x4{0u, 0u, 0u, 0u};
+      f.b[q] = (in && b_ok) ? *reinterpret_cast<const g32x4*>(bc + off) : g32x4{0u, 0u, 0u, 0u};
+    }
+    const bool in0 = st * kMxK + 64 * h + 32 <= p.K, in1 = st * kMxK + 64 * h + 64 <= p.K;
+    const int64_t s0 = in0 ? st * (kMxK / 32) : 0, s1 = in1 ? st * (kMxK / 32) + 1 : 0;
+    f.sa = (in0 && a_ok ? (uint32_t)as[s0] : 127u) | ((in1 && a_ok ? (uint32_t)as[s1] : 127u) << 8);
+    f.sb = (in0 && b_ok ? (uint32_t)bs[s0] : 127u) | ((in1 && b_ok ? (uint32_t)bs[s1] : 127u) << 8);
+    return f;
+  };
+  auto put_row = [&](const g32x4 c[2], uint8_t* dst) {
+    if (Fm::kFp4) {
+      reinterpret_cast<g32x4*>(dst)[0] = c[0];
+      reinterpret_cast<g32x4*>(dst)[1] = c[1];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        uint32_t e[8];
+        expand8_e4m3<GRID>(c[q].x, e);
+        expand8_e4m3<GRID>(c[q].y, e + 2);
+        expand8_e4m3<GRID>(c[q].z, e + 4);
+        expand8_e4m3<GRID>(c[q].w, e + 6);
+        reinterpret_cast<g32x4*>(dst)[2 * q] = g32x4{e[0], e[1], e[2], e[3]};
+        reinterpret_cast<g32x4*>(dst)[2 * q + 1] = g32x4{e[4], e[5], e[6], e[7]};
+      }
+    }
+  };
+  auto put = [&](const Stage& f, int buf) {
+    constexpr int half_bytes = Fm::kRowBytes / 2;
+    put_row(f.a, &As[buf][lr][half_bytes * h]);
+    put_row(f.b, &Bs[buf][lr][half_bytes * h]);
+    *reinterpret_cast<uint16_t*>(&Ss[buf][0][lr][2 * h]) = (uint16_t)f.sa;
+    *reinterpret_cast<uint16_t*>(&Ss[buf][1][lr][2 * h]) = (uint16_t)f.sb;
+  };
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  if (nsteps > 0) put(fetch(0), 0);
+  Stage nxt = fetch(nsteps > 1 ? 1 : 0);
+  __syncthreads();
+  const int g = lane >> 5, r32 = lane & 31;
+  for (int64_t st = 0; st < nsteps; ++st) {
+    const int cur = (int)(st & 1);
+    // stage the next step into the other buffer (last read before the
+    // previous barrier) and request the one after; the staging registers
+    // are free again before the fragments of this step are read
+    if (st + 1 < nsteps) {
+      put(nxt, cur ^ 1);
+      if (st + 2 < nsteps) nxt = fetch(st + 2);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      i32x8 fa[2], fb[4];
+      int sa[2], sb[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm + 32 * i + r32;
+        if (Fm::kFp4) {
+          const g32x4 v = *reinterpret_cast<const g32x4*>(&As[cur][row][32 * kk + 16 * g]);
+          fa[i] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        } else {
+          const g32x4 v0 = *reinterpret_cast<const g32x4*>(&As[cur][row][64 * kk + 16 * g]);
+          const g32x4 v1 = *reinterpret_cast<const g32x4*>(&As[cur][row][64 * kk + 32 + 16 * g]);
+          fa[i] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        }
+        sa[i] = Ss[cur][0][row][2 * kk + g];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = wn + 32 * j + r32;
+        if (Fm::kFp4) {
+          const g32x4 v = *reinterpret_cast<const g32x4*>(&Bs[cur][row][32 * kk + 16 * g]);
+          fb[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        } else {
+          const g32x4 v0 = *reinterpret_cast<const g32x4*>(&Bs[cur][row][64 * kk + 16 * g]);
+          const g32x4 v1 = *reinterpret_cast<const g32x4*>(&Bs[cur][row][64 * kk + 32 + 16 * g]);
+          fb[j] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        }
+        sb[j] = Ss[cur][1][row][2 * kk + g];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], Fm::kFmt, Fm::kFmt,
+                                                                      0, sa[i], 0, sb[j]);
+    }
+    __syncthreads();
+  }
+  const float s = p.a_ts[0] * p.b_ts[0];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t col = n0 + wn + 32 * j + (lane & 31);
+        if (row < p.M && col < p.N) __builtin_nontemporal_store(acc[i][j][r] * s, &p.c[row * p.ldc + col]);
+      }
+}
+
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const dim3 grid((unsigned)((p.N + kGemmN - 1) / kGemmN), (unsigned)((p.M + kGemmM - 1) / kGemmM));
+  if (p.mx) {
+    switch (p.grid) {
+      case kGridE1M2: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridE1M2>, grid, dim3(kGemmThreads), 0, s, p); break;
+      case kGridINT4: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridINT4>, grid, dim3(kGemmThreads), 0, s, p); break;
+      case kGridE2M1: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridE2M1>, grid, dim3(kGemmThreads), 0, s, p); break;
+      case kGridE2M1C: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridE2M1C>, grid, dim3(kGemmThreads), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (p.grid) {
     case kGridE1M2: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridE1M2>, grid, dim3(kGemmThreads), 0, s, p); break;
     case kGridINT4: hipLaunchKernelGGL(ufp4_gemm_kernel<kGridINT4>, grid, dim3(kGemmThreads), 0, s, p); break;

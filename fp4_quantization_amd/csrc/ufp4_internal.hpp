@@ -136,6 +136,7 @@ struct GemmParams {
   float* c;
   int64_t M, N, K, ldc;
   int32_t grid;
+  int32_t mx;  // MX32 operands (E8M0 scales per 32), else NV16
 };
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 hipError_t launch_to_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s);

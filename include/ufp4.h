@@ -254,16 +254,21 @@ int ufp4_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int32_
 /* --- consumer GEMM -------------------------------------------------------- */
 
 /* c[m][n] = sum_k xa[m][k] * xb[n][k] (fp32, row-major with stride ldc), where
- * xa and xb are the dequantized values of a and b: NV16 row-wise layouts of
- * an M x K and an N x K matrix (codes [rows][K/2], scales [rows][K/16], one
- * tensor scale), blocks along K, the reduction dimension of the training
- * GEMMs ("Shrinkage Bias: The Hidden Geometric Trap in FP4 Training"
- * (zhichai.net), "Key points": the fix quantizes the operands of all three).
- * Operands quantized with the same RHT signs give the product of the
- * untransformed matrices (the transform is orthonormal).  Each dequantized
- * value is exact in fp16; the products are summed on the fp16 MFMA in fp32,
- * so c differs from the exact sum only by fp32 accumulation order.
- * cfg: grid of both operands; NV16 only.  K % 32 == 0 (UFP4_ERR_SHAPE);
+ * xa and xb are the dequantized values of a and b: row-wise layouts of an
+ * M x K and an N x K matrix (codes [rows][K/2]; NV16: scales [rows][K/16]
+ * and one tensor scale; MX32: E8M0 scales [rows][K/32], tensor scale 1),
+ * blocks along K, the reduction dimension of the training GEMMs ("Shrinkage
+ * Bias: The Hidden Geometric Trap in FP4 Training" (zhichai.net), "Key
+ * points": the fix quantizes the operands of all three).  Operands quantized
+ * with the same RHT signs give the product of the untransformed matrices
+ * (the transform is orthonormal).  NV16: each dequantized value is exact in
+ * fp16 and the products are summed on the fp16 MFMA in fp32.  MX32: the
+ * codes (as FP4 for E2M1 and E2M1C, expanded to FP8 E4M3 for E1M2 and INT4)
+ * and the E8M0 block scales feed the scaled f8f6f4 MFMA directly, fp32
+ * accumulation.  Either way the products are exact and c differs from the
+ * exact sum only by fp32 accumulation order (and, for MX32, by fp32 range:
+ * scaled products below fp32's smallest subnormal are lost).
+ * cfg: grid and scaling of both operands.  K % 32 == 0 (UFP4_ERR_SHAPE);
  * ldc >= N; codes 16-byte aligned.  M or N of 0 writes nothing; K of 0
  * writes zeros. */
 int ufp4_gemm_nt(const ufp4_config* cfg, int64_t M, int64_t N, int64_t K, ufp4_qtensor a, ufp4_qtensor b,

@@ -233,7 +233,8 @@ int main() {
   EXPECT(ufp4_f32_to_bf16(dev<float>((size_t)9 << 30), 4, dev<uint16_t>((size_t)10 << 30), nullptr), UFP4_OK);
   float* c = dev<float>((size_t)11 << 30);
   EXPECT(ufp4_gemm_nt(&ok, 256, 256, 48, row, row, c, 256, nullptr), UFP4_ERR_SHAPE);
-  EXPECT(ufp4_gemm_nt(&mx, 256, 256, 64, row, row, c, 256, nullptr), UFP4_ERR_INVALID_ARGUMENT);
+  EXPECT(ufp4_gemm_nt(&mx, 256, 256, 64, row, row, c, 256, nullptr), UFP4_OK);  // MX32: scaled-MFMA path
+  EXPECT(ufp4_gemm_nt(&mx, 256, 256, 48, row, row, c, 256, nullptr), UFP4_ERR_SHAPE);
   EXPECT(ufp4_gemm_nt(&ok, 256, 256, 64, row, row, c, 128, nullptr), UFP4_ERR_INVALID_ARGUMENT);
   EXPECT(ufp4_gemm_nt(&ok, (int64_t)0x10000 * 256, 256, 64, row, row, c, 256, nullptr), UFP4_ERR_SHAPE);
   EXPECT(ufp4_gemm_nt(&ok, 0, 256, 64, row, row, c, 256, nullptr), UFP4_OK);

@@ -84,7 +84,8 @@ hipError_t launch_round(const float* y, int64_t n, int32_t, int32_t, uint64_t, u
 }
 hipError_t launch_gemm(const GemmParams& p, hipStream_t) {
   ++g_stub_calls;
-  require(p.M > 0 && p.N > 0 && p.K >= 0 && p.ldc >= p.N && p.c, "gemm");
+  require(p.M > 0 && p.N > 0 && p.K >= 0 && p.K % 32 == 0 && p.ldc >= p.N && p.c, "gemm");
+  require(p.mx == 0 || p.mx == 1, "gemm scaling");
   return g_stub_result;
 }
 hipError_t launch_to_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t) {

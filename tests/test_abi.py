@@ -82,7 +82,7 @@ def test_gemm_arguments(F):
     q = F.ufp4_qtensor(ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(12288))
     c = ctypes.c_void_p(1 << 20)
     g = F.lib.ufp4_gemm_nt
-    assert g(ctypes.byref(mx), 16, 16, 32, q, q, c, 16, None) == 1    # MX32
+    assert g(ctypes.byref(mx), 16, 16, 48, q, q, c, 16, None) == 2    # MX32: K % 32 as well
     assert g(ctypes.byref(cfg), 16, 16, 48, q, q, c, 16, None) == 2   # K % 32
     assert g(ctypes.byref(cfg), 16, 16, 32, q, q, c, 8, None) == 1    # ldc < N
     assert g(ctypes.byref(cfg), -1, 16, 32, q, q, c, 16, None) == 1

@@ -350,28 +350,29 @@ def test_delayed_row_only_nonfinite_and_many_entries(env):
 
 
 # ------------------------------------------------------------ consumer GEMM
-def upload(torch, F, q, rows, cols):
+def upload(torch, F, q, rows, cols, scaling=NV16):
     """An oracle-quantized row-wise layout as a device QTensor."""
-    qt = F.alloc_layout(rows, cols, NV16)
+    qt = F.alloc_layout(rows, cols, scaling)
     qt.codes.copy_(torch.from_numpy(np.ascontiguousarray(q[0])))
     qt.scales.copy_(torch.from_numpy(np.ascontiguousarray(q[1])))
     qt.tensor_scale.copy_(torch.from_numpy(np.ascontiguousarray(q[2])))
     return qt
 
 
+@pytest.mark.parametrize("scaling", [NV16, MX32])
 @pytest.mark.parametrize("grid", [E1M2, INT4, E2M1, E2M1C])
-def test_gemm_matches_oracle_reference(env, grid):
+def test_gemm_matches_oracle_reference(env, grid, scaling):
     # operands quantized by the oracle; the GEMM against the float64 product
     # of the oracle's dequantized operands, within the fp32 accumulation bound
     torch, F, orc = env
-    for M, N, K in ((256, 384, 512), (130, 70, 96), (1, 1, 32), (300, 129, 2048)):
-        say(f"[gemm] grid={grid} {M}x{N}x{K}")
-        fc, oc = cfgs(F, orc, grid, RTNE, NV16, 1, 7, 7)
+    for M, N, K in ((256, 384, 512), (130, 70, 96), (1, 1, 32), (300, 129, 2048), (257, 513, 160)):
+        say(f"[gemm] grid={grid} scaling={scaling} {M}x{N}x{K}")
+        fc, oc = cfgs(F, orc, grid, RTNE, scaling, 1, 7, 7)
         a = orc.quantize(synth.activation(M, K, seed=M + K), oc, ROW)
         b = orc.quantize(synth.weight(N, K, seed=N + K), oc, ROW)
         ref, mag = orc.gemm_nt_reference(a, b, oc, M, N, K)
         c = torch.full((M, N + 3), np.nan, dtype=torch.float32, device="cuda")[:, :N]
-        F.ufp4_gemm_nt(fc, upload(torch, F, a, M, K), upload(torch, F, b, N, K), M, N, K, c)
+        F.ufp4_gemm_nt(fc, upload(torch, F, a, M, K, scaling), upload(torch, F, b, N, K, scaling), M, N, K, c)
         torch.cuda.synchronize()
         got = c.cpu().numpy().astype(np.float64)
         bound = (K + 4) * 2.0 ** -24 * mag + 1e-30
@@ -402,6 +403,33 @@ def test_gemm_exact_on_exactly_representable_products(env):
     np.testing.assert_array_equal(c.cpu().numpy().astype(np.float64), ka @ kb.T)
     ref, _ = orc.gemm_nt_reference(a, b, oc, M, N, K)
     np.testing.assert_array_equal(ref, ka @ kb.T)
+
+
+@pytest.mark.parametrize("grid", [INT4, E1M2, E2M1])
+def test_gemm_mx32_exact_on_representable_products(env, grid):
+    # MX32 operands with random codes and E8M0 scales 2^-2 .. 2^2: every
+    # product is a small integer times a power of two at least 2^-5 and every
+    # partial sum stays below 2^19 in magnitude, so the fp32 result is exact;
+    # covers the K positions and scales of every lane of the scaled MFMA
+    torch, F, orc = env
+    rng = np.random.default_rng(41 + grid)
+    M, N, K = 96, 160, 384
+    fc, oc = cfgs(F, orc, grid, RTNE, MX32, 0, 0, 0)
+    top = 4 if grid == E2M1C else 7
+
+    def layout(rows):
+        k = rng.integers(-top, top + 1, size=(rows, K))
+        nib = (np.where(k < 0, 8 | -k, k) if grid != INT4 else k & 15).astype(np.uint8)
+        codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+        scales = rng.integers(125, 130, size=(rows, K // 32)).astype(np.uint8)
+        q = (codes, scales, np.ones(1, np.float32))
+        return q, orc.dequantize(*q, rows, K, oc).astype(np.float64)
+
+    (a, xa), (b, xb) = layout(M), layout(N)
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    F.ufp4_gemm_nt(fc, upload(torch, F, a, M, K, MX32), upload(torch, F, b, N, K, MX32), M, N, K, c)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c.cpu().numpy().astype(np.float64), xa @ xb.T)
 
 
 def test_gemm_degenerate_shapes(env):
