@@ -16,7 +16,7 @@ namespace ufp4 {
 constexpr int kThreads = 256;
 constexpr int kBandCols = 256;
 constexpr int kTileRows = 128;
-constexpr int kMaxGroups = 256;
+constexpr int kMaxGroups = 1024;
 constexpr int kNumXcd = 8;
 
 struct QuantParams {

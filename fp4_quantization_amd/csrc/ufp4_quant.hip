@@ -45,6 +45,8 @@ struct GroupLds {
   int64_t off[kMaxGroups + 1];
   int64_t ppre[kMaxGroups + 1];  // prefix of padded rows
   int32_t tpre[kMaxGroups + 1];  // prefix of row tiles
+  int64_t runp[kThreads];        // scan of the threads' runs
+  int32_t runt[kThreads];
   int32_t bad;
   int32_t seg;
 };
@@ -103,21 +105,48 @@ __device__ __forceinline__ TileInfo tile_info(const QuantParams& p, GroupLds& g)
     if (g.off[0] != 0 || g.off[E] != p.rows) g.bad = 1;
   }
   __syncthreads();
-  for (int s = 1; s < E; s <<= 1) {
+  // inclusive scans of entries 1..E: each thread scans a run of `per`
+  // consecutive entries, the run totals are scanned across the threads
+  // (Hillis-Steele), and each run then adds the total of the runs before it
+  const int per = (E + kThreads - 1) / kThreads;
+  const int nrun = (E + per - 1) / per;
+  const int b0 = 1 + tid * per, b1 = min(E + 1, b0 + per);
+  {
+    int64_t sp = 0;
+    int32_t sq = 0;
+    for (int i = b0; i < b1; ++i) {
+      sp += g.ppre[i];
+      g.ppre[i] = sp;
+      sq += g.tpre[i];
+      g.tpre[i] = sq;
+    }
+    g.runp[tid] = sp;
+    g.runt[tid] = sq;
+  }
+  __syncthreads();
+  for (int s = 1; s < nrun; s <<= 1) {
     int64_t a = 0;
     int32_t b = 0;
-    const int i = tid + 1;
-    if (tid < E && tid >= s) {
-      a = g.ppre[i - s];
-      b = g.tpre[i - s];
+    if (tid >= s) {
+      a = g.runp[tid - s];
+      b = g.runt[tid - s];
     }
     __syncthreads();
-    if (tid < E && tid >= s) {
-      g.ppre[i] += a;
-      g.tpre[i] += b;
+    if (tid >= s) {
+      g.runp[tid] += a;
+      g.runt[tid] += b;
     }
     __syncthreads();
   }
+  if (tid > 0) {
+    const int64_t a = g.runp[tid - 1];
+    const int32_t b = g.runt[tid - 1];
+    for (int i = b0; i < b1; ++i) {
+      g.ppre[i] += a;
+      g.tpre[i] += b;
+    }
+  }
+  __syncthreads();
   if (tid == 0) {
     if (p.do_col && g.ppre[E] != p.padded_rows) g.bad = 1;
     if (g.tpre[E] > p.n_tiles) g.bad = 1;

@@ -207,8 +207,9 @@ int ufp4_quantize_rowcol_noalloc(const uint16_t* x, int64_t rows, int64_t cols, 
  * padded_rows (a host value) rather than as a device array of column offsets:
  * the offsets follow from offsets_dev and the block, and the device derives
  * them, so the two can never disagree.
- * offsets_dev: device array of num_groups+1 int64, offsets[0] = 0, non-
- * decreasing, offsets[E] = total_rows.  Each segment gets its own tensor scale
+ * offsets_dev: device array of num_groups+1 int64 (1 <= num_groups <= 1024,
+ * else UFP4_ERR_INVALID_ARGUMENT), offsets[0] = 0, non-decreasing,
+ * offsets[E] = total_rows.  Each segment gets its own tensor scale
  * per layout.  Column-wise blocks restart at each segment start; a segment's
  * last block is zero-padded to B rows and all of its outputs are stored.
  * padded_rows = sum over segments of roundup(M_e, B) (ufp4_grouped_col_offsets

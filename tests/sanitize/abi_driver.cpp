@@ -154,7 +154,7 @@ int main() {
   const size_t gwsb = ufp4_workspace_size(65536, 4096, 64);
   EXPECT(ufp4_quantize_grouped(x, 65536, 4096, off, 0, 65536, &ok, row, col, ws, gwsb, nullptr),
          UFP4_ERR_INVALID_ARGUMENT);
-  EXPECT(ufp4_quantize_grouped(x, 65536, 4096, off, 257, 65536, &ok, row, col, ws, gwsb, nullptr),
+  EXPECT(ufp4_quantize_grouped(x, 65536, 4096, off, 1025, 65536, &ok, row, col, ws, gwsb, nullptr),
          UFP4_ERR_INVALID_ARGUMENT);
   EXPECT(ufp4_quantize_grouped(x, 65536, 4096, nullptr, 64, 65536, &ok, row, col, ws, gwsb, nullptr),
          UFP4_ERR_INVALID_ARGUMENT);

@@ -150,7 +150,7 @@ def test_rowcol_and_grouped_argument_errors(F):
                                            padded if padded is not None else 128, ctypes.byref(cfg),
                                            row or q(F), col or q(F), ctypes.c_void_p(FAKE), 1 << 30, None)
     assert grouped(E=0) == 1
-    assert grouped(E=257) == 1
+    assert grouped(E=1025) == 1
     assert grouped(offsets=0) == 1
     assert grouped(offsets=FAKE + 4) == 3
     assert grouped(padded=96) == 2          # fewer than total rows

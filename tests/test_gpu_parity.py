@@ -245,6 +245,58 @@ def test_deterministic_repeat(env):
         assert torch.equal(qa.codes, qb.codes) and torch.equal(qa.scales, qb.scales)
 
 
+def test_identical_bytes_across_schedules_and_work_distributions(env, schedule):
+    # the kernels' tile size is fixed by the lane geometry, so the launch
+    # variants are the schedules and the assignment of tiles to workgroups:
+    # two passes, one pass, one pass with tiles left to other workgroups
+    # (strides 2, 3, 7), the no-allocation entry point, delayed scaling under
+    # the tensor's own maxima, and a grouped call with one segment all give
+    # the same bytes, each repeated, with stochastic rounding (whose words
+    # are tied to output positions) and the transform on
+    torch, F, orc = env
+    R, C = 640, 1280
+    xb = synth.output_grad(R, C, seed=61)
+    fc, _ = cfgs(F, orc, E1M2, SR, NV16, 1, 9, 9)
+    x = to_dev(torch, xb)
+
+    def outs():
+        return F.alloc_layout(R, C, NV16), F.alloc_layout(C, R, NV16)
+
+    def grab(pair):
+        torch.cuda.synchronize()
+        return [t.clone() for q in pair for t in (q.codes, q.scales, q.tensor_scale)]
+
+    results = {}
+    ws = F.Workspace(R, C)
+    for name, mode, stride in (("two_pass", TWO_PASS, 0), ("single", SINGLE_PASS, 0), ("left2", SINGLE_PASS, 2),
+                               ("left3", SINGLE_PASS, 3), ("left7", SINGLE_PASS, 7)):
+        schedule(mode, stride)
+        for rep in range(2):
+            pair = outs()
+            F.ufp4_quantize_rowcol(x, fc, *pair, ws)
+            results[f"{name}.{rep}"] = grab(pair)
+    schedule(AUTO, 0)
+    for rep in range(2):
+        pair = outs()
+        F.ufp4_quantize_rowcol_noalloc(x, fc, *pair)
+        results[f"noalloc.{rep}"] = grab(pair)
+    n = F.ufp4_amax_tiles(R, C)
+    a1 = torch.zeros((n, 2), dtype=torch.float32, device="cuda")
+    a2 = torch.zeros((n, 2), dtype=torch.float32, device="cuda")
+    F.ufp4_quantize_delayed(x, fc, torch.ones((1, 2), dtype=torch.float32, device="cuda"), a1, *outs())
+    pair = outs()
+    F.ufp4_quantize_delayed(x, fc, a1, a2, *pair)
+    results["delayed_own"] = grab(pair)
+    pair = outs()
+    F.ufp4_quantize_grouped(x, torch.tensor([0, R], dtype=torch.int64, device="cuda"), R, fc, *pair,
+                            F.Workspace(R, C, 1))
+    results["grouped_one_segment"] = grab(pair)
+    ref = results.pop("two_pass.0")
+    for name, got in results.items():
+        for i, (u, v) in enumerate(zip(ref, got)):
+            assert torch.equal(u, v), f"{name}: output {i} differs from the two-pass call"
+
+
 @pytest.mark.parametrize("sched", [TWO_PASS, SINGLE_PASS])
 def test_timing_hook_matches_plain_call(env, schedule, sched):
     torch, F, orc = env
@@ -592,6 +644,23 @@ def test_grouped_small(env, scaling, rounding):
     np.testing.assert_array_equal(coff, ocoff)
     assert_layout_equal(rq, (rc, rs, rts), "grouped row")
     assert_layout_equal(cq, (cc, cs, cts), "grouped col")
+
+
+def test_grouped_many_segments(env):
+    # 1000 ragged segments (many empty or of one row), near the limit of 1024
+    torch, F, orc = env
+    rng = np.random.default_rng(14)
+    counts = rng.integers(0, 6, size=1000) * rng.integers(0, 2, size=1000)
+    counts[rng.integers(0, 1000, size=20)] = rng.integers(17, 300, size=20)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    xb = synth.activation(int(offsets[-1]), 256, seed=15)
+    say(f"[grouped] E=1000 rows={offsets[-1]}")
+    fc, oc = cfgs(F, orc, E1M2, SR, NV16, 1, rht_seed=8, sr_seed=8)
+    rq, cq, coff = gpu_grouped(env, xb, offsets, fc)
+    (rc, rs, rts), (cc, cs, cts), ocoff = orc.quantize_grouped(xb, offsets, oc)
+    np.testing.assert_array_equal(coff, ocoff)
+    assert_layout_equal(rq, (rc, rs, rts), "grouped row, 1000 segments")
+    assert_layout_equal(cq, (cc, cs, cts), "grouped col, 1000 segments")
 
 
 def test_grouped_single_outputs_and_bad_offsets(env):
