@@ -123,6 +123,7 @@ bool single_pass(bool grouped, bool mx, bool both, int64_t n_work) {
 // Start and end events of the two kernels of one call.
 struct KernelTimer {
   hipEvent_t ev[4];
+  bool single = false;  // the call ran as one kernel (events 2 and 3 only)
 };
 
 int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream, KernelTimer* tm = nullptr) {
@@ -152,11 +153,7 @@ int run_quant(QuantParams& p, void* ws, size_t ws_bytes, hipStream_t stream, Ker
       p.fs_gen = reinterpret_cast<uint32_t*>(base + kWsGenOffset);
       p.fs_words = reinterpret_cast<uint64_t*>(base + kWsHeader);
       p.fs_orphan_stride = mode == UFP4_SCHEDULE_SINGLE_PASS ? g_left_stride.load(std::memory_order_relaxed) : 0;
-      if (tm) {
-        // no separate maxima kernel: its interval is empty
-        if (hipEventRecord(tm->ev[0], stream) != hipSuccess || hipEventRecord(tm->ev[1], stream) != hipSuccess)
-          return UFP4_ERR_HIP;
-      }
+      if (tm) tm->single = true;  // no separate maxima kernel
       if (launch_fused(p, grid, stream, tm ? tm->ev[2] : nullptr, tm ? tm->ev[3] : nullptr) != hipSuccess)
         return UFP4_ERR_HIP;
       return UFP4_OK;
@@ -416,8 +413,9 @@ int ufp4_time_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, 
     }
   if (rc == UFP4_OK) rc = rowcol_impl(x, rows, cols, ld, cfg, row_out, col_out, ws, ws_bytes, stream, &tm);
   if (rc == UFP4_OK) {
+    *ms_amax_host = 0.0f;
     if (hipEventSynchronize(tm.ev[3]) != hipSuccess ||
-        hipEventElapsedTime(ms_amax_host, tm.ev[0], tm.ev[1]) != hipSuccess ||
+        (!tm.single && hipEventElapsedTime(ms_amax_host, tm.ev[0], tm.ev[1]) != hipSuccess) ||
         hipEventElapsedTime(ms_quant_host, tm.ev[2], tm.ev[3]) != hipSuccess)
       rc = UFP4_ERR_HIP;
   }

@@ -306,8 +306,8 @@ def test_timing_hook_matches_plain_call(env, schedule, sched):
     x = to_dev(torch, xb)
     row, col = F.alloc_layout(384, 512, NV16), F.alloc_layout(512, 384, NV16)
     ms_a, ms_q = F.ufp4_time_rowcol(x, fc, row, col, F.Workspace(384, 512))
-    # the single pass has no separate maxima kernel (an empty interval)
-    assert ms_q > 0.0 and (ms_a > 0.0 if sched == TWO_PASS else ms_a >= 0.0)
+    # the single pass has no separate maxima kernel: its time is reported as 0
+    assert ms_q > 0.0 and (ms_a > 0.0 if sched == TWO_PASS else ms_a == 0.0)
     for name, qt, layout in (("row", row, ROW), ("col", col, COL)):
         c, s_, t = orc.quantize(xb, oc, layout)
         assert np.array_equal(qt.codes.cpu().numpy(), c), name
