@@ -273,10 +273,12 @@ template <int GRID>
 struct MxFmt {
   static constexpr bool kFp4 = GRID == kGridE2M1 || GRID == kGridE2M1C;
   static constexpr int kFmt = kFp4 ? 4 : 0;      // cbsz / blgp: FP4 E2M1 or FP8 E4M3
-  static constexpr int kRowBytes = kFp4 ? 64 : 128;  // one K step of 128 values
+  static constexpr int kK = kFp4 ? 256 : 128;    // K values per step (per barrier)
+  static constexpr int kSlices = kK / 64;        // MFMA K slices per step
+  static constexpr int kBlocks = kK / 64;        // MX blocks each thread stages per operand row half
+  static constexpr int kRowBytes = kFp4 ? kK / 2 : kK;  // one step of one row in LDS
   static constexpr int kPitch = kRowBytes + 16;  // LDS row pitch (spreads fragment reads over banks)
 };
-constexpr int kMxK = 128;
 
 // Eight codes (element 2i in the low nibble of byte i) to eight E4M3 bytes
 // (element e in byte e of out[e / 4]) for E1M2 (k/2) or INT4 (k); the sign
@@ -300,7 +302,8 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
   using Fm = MxFmt<GRID>;
   __shared__ __attribute__((aligned(16))) uint8_t As[2][kGemmM][Fm::kPitch];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGemmN][Fm::kPitch];
-  __shared__ uint8_t Ss[2][2][kGemmM][4];  // [buffer][operand][row][block of the step]
+  __shared__ uint8_t Ss[2][2][kGemmM][Fm::kK / 32];  // [buffer][operand][row][block of the step]
+  constexpr int NB = Fm::kBlocks;   // MX blocks per thread and operand per step
   const int64_t m0 = (int64_t)blockIdx.y * kGemmM, n0 = (int64_t)blockIdx.x * kGemmN;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
@@ -308,40 +311,38 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
   const int64_t am = m0 + lr, bn = n0 + lr;
   const bool a_ok = am < p.M, b_ok = bn < p.N;
   const int64_t kc = p.K / 2, ks = p.K / 32;
-  const uint8_t* ac = p.a_codes + (a_ok ? am : 0) * kc + 32 * h;
-  const uint8_t* as = p.a_scales + (a_ok ? am : 0) * ks + 2 * h;
-  const uint8_t* bc = p.b_codes + (b_ok ? bn : 0) * kc + 32 * h;
-  const uint8_t* bs = p.b_scales + (b_ok ? bn : 0) * ks + 2 * h;
-  const int64_t nsteps = (p.K + kMxK - 1) / kMxK;
-  // codes of the thread's two blocks (16 bytes each) and their scale bytes;
+  const uint8_t* ac = p.a_codes + (a_ok ? am : 0) * kc + 16 * NB * h;
+  const uint8_t* as = p.a_scales + (a_ok ? am : 0) * ks + NB * h;
+  const uint8_t* bc = p.b_codes + (b_ok ? bn : 0) * kc + 16 * NB * h;
+  const uint8_t* bs = p.b_scales + (b_ok ? bn : 0) * ks + NB * h;
+  const int64_t nsteps = (p.K + Fm::kK - 1) / Fm::kK;
+  // codes of the thread's NB blocks (16 bytes each) and their scale bytes;
   // a block past K (or a row past M / N) is zero with scale 2^0
   struct Stage {
-    g32x4 a[2], b[2];
-    uint32_t sa, sb;
+    g32x4 a[NB], b[NB];
+    uint8_t sa[NB], sb[NB];
   };
   auto fetch = [&](int64_t st) {
     Stage f;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < NB; ++q) {
       // addresses stay inside the operands whether or not the load is used
-      const bool in = st * kMxK + 64 * h + 32 * q + 32 <= p.K;
-      const int64_t off = in ? st * (kMxK / 2) + 16 * q : 0;
+      const bool in = st * Fm::kK + 32 * NB * h + 32 * q + 32 <= p.K;
+      const int64_t off = in ? st * (Fm::kK / 2) + 16 * q : 0;
+      const int64_t so = in ? st * (Fm::kK / 32) + q : 0;
       f.a[q] = (in && a_ok) ? *reinterpret_cast<const g32x4*>(ac + off) : g32x4{0u, 0u, 0u, 0u};
       f.b[q] = (in && b_ok) ? *reinterpret_cast<const g32x4*>(bc + off) : g32x4{0u, 0u, 0u, 0u};
+      f.sa[q] = (in && a_ok) ? as[so] : (uint8_t)127;
+      f.sb[q] = (in && b_ok) ? bs[so] : (uint8_t)127;
     }
-    const bool in0 = st * kMxK + 64 * h + 32 <= p.K, in1 = st * kMxK + 64 * h + 64 <= p.K;
-    const int64_t s0 = in0 ? st * (kMxK / 32) : 0, s1 = in1 ? st * (kMxK / 32) + 1 : 0;
-    f.sa = (in0 && a_ok ? (uint32_t)as[s0] : 127u) | ((in1 && a_ok ? (uint32_t)as[s1] : 127u) << 8);
-    f.sb = (in0 && b_ok ? (uint32_t)bs[s0] : 127u) | ((in1 && b_ok ? (uint32_t)bs[s1] : 127u) << 8);
     return f;
   };
-  auto put_row = [&](const g32x4 c[2], uint8_t* dst) {
-    if (Fm::kFp4) {
-      reinterpret_cast<g32x4*>(dst)[0] = c[0];
-      reinterpret_cast<g32x4*>(dst)[1] = c[1];
-    } else {
+  auto put_row = [&](const g32x4 (&c)[NB], uint8_t* dst) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < NB; ++q) {
+      if (Fm::kFp4) {
+        reinterpret_cast<g32x4*>(dst)[q] = c[q];
+      } else {
         uint32_t e[8];
         expand8_e4m3<GRID>(c[q].x, e);
         expand8_e4m3<GRID>(c[q].y, e + 2);
@@ -356,8 +357,11 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
     constexpr int half_bytes = Fm::kRowBytes / 2;
     put_row(f.a, &As[buf][lr][half_bytes * h]);
     put_row(f.b, &Bs[buf][lr][half_bytes * h]);
-    *reinterpret_cast<uint16_t*>(&Ss[buf][0][lr][2 * h]) = (uint16_t)f.sa;
-    *reinterpret_cast<uint16_t*>(&Ss[buf][1][lr][2 * h]) = (uint16_t)f.sb;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      Ss[buf][0][lr][NB * h + q] = f.sa[q];
+      Ss[buf][1][lr][NB * h + q] = f.sb[q];
+    }
   };
   f32x16 acc[2][4];
 #pragma unroll
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
       if (st + 2 < nsteps) nxt = fetch(st + 2);
     }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < Fm::kSlices; ++kk) {
       i32x8 fa[2], fb[4];
       int sa[2], sb[4];
 #pragma unroll
