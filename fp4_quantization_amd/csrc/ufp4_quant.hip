@@ -836,7 +836,7 @@ __device__ __forceinline__ float2 quant_tile(const QuantParams& p, const TileInf
 }
 
 template <int GRID, bool SR, bool MX, bool RHT>
-__global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void ufp4_quant_kernel(QuantParams p) {
   __shared__ GroupLds g;
   __shared__ float lut[2][128];
   __shared__ float red[2][kThreads / 64];
@@ -923,7 +923,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_quant_kernel(QuantParams p) {
     __syncthreads();
   }
   load_rows<4, 16, true>(p, T, L, w);
-  quant_tile<GRID, SR, MX, RHT>(p, T, L, w, tsr, tsc, lut, cst);
+  quant_tile<GRID, SR, MX, RHT, false>(p, T, L, w, tsr, tsc, lut, cst);
 }
 
 // ------------------------------------------------------------ delayed
@@ -947,7 +947,7 @@ __device__ __forceinline__ TensorScale given_tensor_scale(float a, float qmax) {
 }
 
 template <int GRID, bool SR, bool RHT>
-__global__ __launch_bounds__(kThreads) void ufp4_delayed_kernel(QuantParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void ufp4_delayed_kernel(QuantParams p) {
   __shared__ float lut[2][128];
   __shared__ float red[2][kThreads / 64];
   __shared__ ColStage cst;
@@ -991,7 +991,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_delayed_kernel(QuantParams p) {
   }
   __syncthreads();  // also: every thread has read red
   load_rows<4, 16, true>(p, T, L, w);
-  float2 m = quant_tile<GRID, SR, false, RHT, true, true>(p, T, L, w, tsr, tsc, lut, cst);
+  float2 m = quant_tile<GRID, SR, false, RHT, false, true>(p, T, L, w, tsr, tsc, lut, cst);
   m.x = wave_max(m.x);
   m.y = wave_max(m.y);
   if ((threadIdx.x & 63) == 0) {
@@ -1020,7 +1020,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_delayed_kernel(QuantParams p) {
 // the host beforehand) with an atomic max on the bit patterns, which order
 // like the non-negative values; the updates are not waited for.
 template <int GRID, bool SR, bool RHT>
-__global__ __launch_bounds__(kThreads) void ufp4_grouped_delayed_kernel(QuantParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void ufp4_grouped_delayed_kernel(QuantParams p) {
   __shared__ GroupLds g;
   __shared__ float lut[2][128];
   __shared__ float red[2][kThreads / 64];
@@ -1057,7 +1057,7 @@ __global__ __launch_bounds__(kThreads) void ufp4_grouped_delayed_kernel(QuantPar
   }
   __syncthreads();
   load_rows<4, 16, true>(p, T, L, w);
-  float2 m = quant_tile<GRID, SR, false, RHT, true, true>(p, T, L, w, tsr, tsc, lut, cst);
+  float2 m = quant_tile<GRID, SR, false, RHT, false, true>(p, T, L, w, tsr, tsc, lut, cst);
   m.x = wave_max(m.x);
   m.y = wave_max(m.y);
   if ((threadIdx.x & 63) == 0) {
