@@ -97,9 +97,10 @@ QUANT_KERNEL = "ufp4_quant_kernel<0, false, false, true>"
 ROOF_KERNEL = "ufp4_roof_kernel"
 
 
-def _counter_means(csv_dir, counter):
+def _counter_means(csv_dir, counter, counts=None):
     """Mean counter value (KiB) per dispatch, by kernel name, from a rocprofv3
-    --pmc CSV directory; also the largest-grid copyBuffer dispatches'."""
+    --pmc CSV directory; also the largest-grid copyBuffer dispatches'.  The
+    number of dispatches per kernel goes to `counts` if given."""
     import csv
     import glob
 
@@ -118,6 +119,8 @@ def _counter_means(csv_dir, counter):
                 else:
                     sums.setdefault(name, []).append(v)
     means = {k: sum(v) / len(v) for k, v in sums.items()}
+    if counts is not None:
+        counts.update({k: len(v) for k, v in sums.items()})
     copy_mean = None
     if copies:
         big = copies[max(copies)]
@@ -130,13 +133,18 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
     single-pass kernel, of the two-pass quantization kernel and per two-pass
     call, each counter scaled by what it reads for a plain 512 MiB device
     copy."""
-    fetch, _ = _counter_means(fetch_dir, "FETCH_SIZE")
+    ncall = {}
+    fetch, _ = _counter_means(fetch_dir, "FETCH_SIZE", ncall)
     write, _ = _counter_means(write_dir, "WRITE_SIZE")
     _, copy_fetch = _counter_means(copy_fetch_dir, "FETCH_SIZE")
     _, copy_write = _counter_means(copy_write_dir, "WRITE_SIZE")
     copy_kib = 512 * 1024
     ff, wf = copy_kib / copy_fetch, copy_kib / copy_write
     if workload:
+        # the kernels every call launches (at least half as often as the
+        # most frequent one); set-up kernels run once or twice per process
+        most = max(ncall.values())
+        fetch = {k: v for k, v in fetch.items() if 2 * ncall[k] >= most}
         summarize_workload_counters(workload, fetch, write,
                                     {"copy_bytes": copy_kib * 1024, "fetch_kib_raw": copy_fetch,
                                      "write_kib_raw": copy_write, "fetch_factor": ff, "write_factor": wf},
@@ -203,7 +211,7 @@ def summarize_workload_counters(name, fetch, write, copy_cal, ff, wf, commands):
            "fetch_kib_raw": fetch, "write_kib_raw": write, "copy_calibration": copy_cal,
            "kernel_source_sha256": kernel_source_sha(), "commands": commands,
            "note": "KiB per dispatch, mean over dispatches; bytes = (fetch * fetch_factor + write * write_factor) "
-                   "* 1024; every kernel of the run is one per call"}
+                   "* 1024; the kernels each call launches (set-up kernels that run once are left out)"}
     path = os.path.join(ROOT, "profiles", f"counters_{name}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
