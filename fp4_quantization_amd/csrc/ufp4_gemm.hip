@@ -302,7 +302,9 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
   using Fm = MxFmt<GRID>;
   __shared__ __attribute__((aligned(16))) uint8_t As[2][kGemmM][Fm::kPitch];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGemmN][Fm::kPitch];
-  __shared__ uint8_t Ss[2][2][kGemmM][Fm::kK / 32];  // [buffer][operand][row][block of the step]
+  // [buffer][operand][row][block of the step], read back one row at a time
+  __shared__ __attribute__((aligned(8))) uint8_t Ss[2][2][kGemmM][Fm::kK / 32];
+  constexpr int SW = Fm::kK / 128;  // 32-bit words of scale bytes per row and step
   constexpr int NB = Fm::kBlocks;   // MX blocks per thread and operand per step
   const int64_t m0 = (int64_t)blockIdx.y * kGemmM, n0 = (int64_t)blockIdx.x * kGemmN;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
@@ -381,10 +383,23 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
       put(nxt, cur ^ 1);
       if (st + 2 < nsteps) nxt = fetch(st + 2);
     }
+    // the step's scale bytes of the lane's rows, shifted so that the byte of
+    // slice kk's block for this lane's half (block 2 kk + g) sits at byte
+    // 2 (kk % 2) of word kk / 2, which the MFMA's scale byte select takes
+    uint32_t swa[2][SW], swb[4][SW];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < SW; ++q)
+        swa[i][q] = reinterpret_cast<const uint32_t*>(&Ss[cur][0][wm + 32 * i + r32][0])[q] >> (8 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < SW; ++q)
+        swb[j][q] = reinterpret_cast<const uint32_t*>(&Ss[cur][1][wn + 32 * j + r32][0])[q] >> (8 * g);
 #pragma unroll
     for (int kk = 0; kk < Fm::kSlices; ++kk) {
       i32x8 fa[2], fb[4];
-      int sa[2], sb[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = wm + 32 * i + r32;
@@ -396,7 +411,6 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
           const g32x4 v1 = *reinterpret_cast<const g32x4*>(&As[cur][row][64 * kk + 32 + 16 * g]);
           fa[i] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
         }
-        sa[i] = Ss[cur][0][row][2 * kk + g];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -409,14 +423,17 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
           const g32x4 v1 = *reinterpret_cast<const g32x4*>(&Bs[cur][row][64 * kk + 32 + 16 * g]);
           fb[j] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
         }
-        sb[j] = Ss[cur][1][row][2 * kk + g];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], Fm::kFmt, Fm::kFmt,
-                                                                      0, sa[i], 0, sb[j]);
+          if (kk & 1)  // (the byte select must be a constant: kk is unrolled)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], Fm::kFmt, Fm::kFmt,
+                                                                        2, (int)swa[i][kk >> 1], 2, (int)swb[j][kk >> 1]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], Fm::kFmt, Fm::kFmt,
+                                                                        0, (int)swa[i][kk >> 1], 0, (int)swb[j][kk >> 1]);
     }
     __syncthreads();
   }
