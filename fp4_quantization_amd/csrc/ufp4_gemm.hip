@@ -17,9 +17,8 @@
 // from an exact sum only by the fp32 accumulation order.
 //
 // Tiles are 256 x 256 per workgroup of 8 waves, K steps of 64, with two LDS
-// buffers: a step multiplies from one while the next step's codes (requested
-// two steps ahead) are expanded in registers between the multiplies and
-// stored into the other, and ends in one barrier.
+// buffers: each step first expands the next step's codes into the other
+// buffer, then multiplies from its own, and ends in one barrier.
 //
 // The expansion is byte arithmetic: every grid value's fp16 encoding has a
 // zero low byte, so one byte permute looks the high bytes of four codes up in
@@ -103,16 +102,15 @@ __device__ __forceinline__ void store16(const uint32_t o[8], _Float16* dst) {
 
 // Grid: (ceil(N/256), ceil(M/256)); 512 threads (8 waves).  Wave w computes
 // the 64 x 128 sub-tile at rows 64 (w / 2), columns 128 (w % 2), as 2 x 4
-// MFMA tiles of 32 x 32.  Per K step of 64 each thread expands two adjacent
+// MFMA tiles of 32 x 32.  Per K step of 64 each thread stages two adjacent
 // blocks of A (row t / 2, blocks 2 (t % 2) and 2 (t % 2) + 1 of the step: 16
 // code bytes, one load) and two of B.  At the 144-byte row pitch both the
 // fragment reads (consecutive rows) and these stores (two threads per row)
-// fall on distinct LDS banks.  The expanded tiles are double-buffered: a
-// step multiplies from one buffer while the next step's codes (requested
-// kPrefetch steps ahead) are expanded in registers between its multiplies
-// and stored into the other, so each step ends in one barrier.
+// fall on distinct LDS banks.  The expanded tiles are double-buffered: at
+// the start of a step the next step's codes (requested one step earlier)
+// are expanded and stored into the other buffer, the step after that is
+// requested, then this step multiplies, and the step ends in one barrier.
 constexpr int kGemmThreads = 512;
-constexpr int kPrefetch = 2;  // steps between a code request and its use (even: buffer = step parity)
 
 template <int GRID>
 __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
@@ -121,114 +119,70 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
   const int64_t m0 = (int64_t)blockIdx.y * kGemmM, n0 = (int64_t)blockIdx.x * kGemmN;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
-  const int lr = t >> 1, lb = 2 * (t & 1);  // row, first of the thread's two blocks
+  const int lr = t >> 1, lb = 2 * (t & 1);
   const int64_t am = m0 + lr, bn = n0 + lr;
   const bool a_ok = am < p.M, b_ok = bn < p.N;
   const int64_t kc = p.K / 2, ks = p.K / 16;
-  // rows outside the matrices read row 0 and are zeroed below
   const uint8_t* ac = p.a_codes + (a_ok ? am : 0) * kc + 8 * lb;
   const uint8_t* as = p.a_scales + (a_ok ? am : 0) * ks + lb;
   const uint8_t* bc = p.b_codes + (b_ok ? bn : 0) * kc + 8 * lb;
   const uint8_t* bs = p.b_scales + (b_ok ? bn : 0) * ks + lb;
+  const int64_t nsteps = (p.K + kGemmK - 1) / kGemmK;
+  struct Stage {
+    g32x4 a, b;
+    uint32_t sa, sb;
+  };
+  auto fetch = [&](int64_t st) {
+    Stage f;
+    const bool in = st * kGemmK + 16 * lb + 32 <= p.K;
+    const int64_t off = in ? st * (kGemmK / 2) : 0, so = in ? st * (kGemmK / 16) : 0;
+    f.a = (in && a_ok) ? *reinterpret_cast<const g32x4*>(ac + off) : g32x4{0u, 0u, 0u, 0u};
+    f.b = (in && b_ok) ? *reinterpret_cast<const g32x4*>(bc + off) : g32x4{0u, 0u, 0u, 0u};
+    f.sa = (in && a_ok) ? ((uint32_t)as[so] | ((uint32_t)as[so + 1] << 8)) : 0u;
+    f.sb = (in && b_ok) ? ((uint32_t)bs[so] | ((uint32_t)bs[so + 1] << 8)) : 0u;
+    return f;
+  };
+  auto put = [&](const Stage& f, int buf) {
+    uint32_t e[8];
+    expand16<GRID>(g32x2{f.a.x, f.a.y}, f.sa & 0xFFu, e);
+    store16(e, &As[buf][lr][16 * lb]);
+    expand16<GRID>(g32x2{f.a.z, f.a.w}, f.sa >> 8, e);
+    store16(e, &As[buf][lr][16 * lb + 16]);
+    expand16<GRID>(g32x2{f.b.x, f.b.y}, f.sb & 0xFFu, e);
+    store16(e, &Bs[buf][lr][16 * lb]);
+    expand16<GRID>(g32x2{f.b.z, f.b.w}, f.sb >> 8, e);
+    store16(e, &Bs[buf][lr][16 * lb + 16]);
+  };
   f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  // Codes and scales of step k + kPrefetch are requested at step k.  The
-  // ring index is static: the loop runs kPrefetch steps per iteration.
-  g32x4 ra[kPrefetch], rb[kPrefetch];
-  uint32_t rsa[kPrefetch], rsb[kPrefetch];  // two scale bytes each
-  // K is a multiple of 32: a last step of 32 leaves blocks 2 and 3 empty
-  const int64_t nsteps = (p.K + kGemmK - 1) / kGemmK;
-  auto scale2 = [](const uint8_t* q) -> uint32_t { return (uint32_t)q[0] | ((uint32_t)q[1] << 8); };
-  auto has = [&](int64_t st) { return st * kGemmK + 16 * lb + 32 <= p.K; };  // the thread's blocks exist
-#pragma unroll
-  for (int u = 0; u < kPrefetch; ++u) {
-    ra[u] = rb[u] = g32x4{0u, 0u, 0u, 0u};
-    rsa[u] = rsb[u] = 0u;
-    if (u < nsteps && has(u)) {
-      ra[u] = *reinterpret_cast<const g32x4*>(ac + (int64_t)u * (kGemmK / 2));
-      rb[u] = *reinterpret_cast<const g32x4*>(bc + (int64_t)u * (kGemmK / 2));
-      rsa[u] = scale2(as + u * (kGemmK / 16));
-      rsb[u] = scale2(bs + u * (kGemmK / 16));
-    }
-  }
-  // expand and store the two blocks of one operand row
-  auto put = [&](bool ok, g32x4 c, uint32_t sc, _Float16* dst) {
-    uint32_t e0[8], e1[8];
-    expand16<GRID>(ok ? g32x2{c.x, c.y} : g32x2{0u, 0u}, sc & 0xFFu, e0);
-    expand16<GRID>(ok ? g32x2{c.z, c.w} : g32x2{0u, 0u}, sc >> 8, e1);
-    store16(e0, dst);
-    store16(e1, dst + 16);
-  };
-  if (nsteps > 0) {
-    put(a_ok, ra[0], rsa[0], &As[0][lr][16 * lb]);
-    put(b_ok, rb[0], rsb[0], &Bs[0][lr][16 * lb]);
-  }
+  if (nsteps > 0) put(fetch(0), 0);
+  Stage nxt = fetch(nsteps > 1 ? 1 : 0);
   __syncthreads();
-  for (int64_t s0 = 0; s0 < nsteps; s0 += kPrefetch) {
-#pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) {
-      const int64_t st = s0 + u;  // this step; its tiles are in buffer u & 1
-      if (st < nsteps) {
-        const int cur = u & 1;
-        // slot u held this step's codes (already expanded); refill it with
-        // step st + kPrefetch's
-        if (st + kPrefetch < nsteps) {
-          const int64_t k1 = (st + kPrefetch) * kGemmK;
-          const bool h = has(st + kPrefetch);
-          ra[u] = h ? *reinterpret_cast<const g32x4*>(ac + k1 / 2) : g32x4{0u, 0u, 0u, 0u};
-          rb[u] = h ? *reinterpret_cast<const g32x4*>(bc + k1 / 2) : g32x4{0u, 0u, 0u, 0u};
-          rsa[u] = h ? scale2(as + k1 / 16) : 0u;
-          rsb[u] = h ? scale2(bs + k1 / 16) : 0u;
-        }
-        // the next step's codes sit in slot (u + 1) % kPrefetch; they are
-        // expanded in registers while the multiplies run (after the last
-        // step the slot is stale and its expansion goes unread)
-        const int v = (u + 1) % kPrefetch;
-        uint32_t ea[2][8], eb[2][8];
-        expand16<GRID>(a_ok ? g32x2{ra[v].x, ra[v].y} : g32x2{0u, 0u}, rsa[v] & 0xFFu, ea[0]);
-        expand16<GRID>(a_ok ? g32x2{ra[v].z, ra[v].w} : g32x2{0u, 0u}, rsa[v] >> 8, ea[1]);
-        expand16<GRID>(b_ok ? g32x2{rb[v].x, rb[v].y} : g32x2{0u, 0u}, rsb[v] & 0xFFu, eb[0]);
-        expand16<GRID>(b_ok ? g32x2{rb[v].z, rb[v].w} : g32x2{0u, 0u}, rsb[v] >> 8, eb[1]);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          f16x8 fa[2][2], fb[2][4];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int kk = 2 * half + q;
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-              fa[q][i] = *reinterpret_cast<const f16x8*>(&As[cur][wm + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              fb[q][j] = *reinterpret_cast<const f16x8*>(&Bs[cur][wn + 32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
-          }
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[q][i], fb[q][j], acc[i][j], 0, 0, 0);
-          // issue order: the fragment reads, then each multiply followed by
-          // a share of the expansion's arithmetic
-          __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
-#pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU (best of 2..8 measured)
-          }
-        }
-        // the other buffer was last read before the previous step's barrier
-        store16(ea[0], &As[cur ^ 1][lr][16 * lb]);
-        store16(ea[1], &As[cur ^ 1][lr][16 * lb + 16]);
-        store16(eb[0], &Bs[cur ^ 1][lr][16 * lb]);
-        store16(eb[1], &Bs[cur ^ 1][lr][16 * lb + 16]);
-        __syncthreads();
-      }
+  for (int64_t st = 0; st < nsteps; ++st) {
+    const int cur = (int)(st & 1);
+    if (st + 1 < nsteps) {
+      put(nxt, cur ^ 1);
+      if (st + 2 < nsteps) nxt = fetch(st + 2);
     }
+#pragma unroll
+    for (int kk = 0; kk < kGemmK / 16; ++kk) {
+      f16x8 fa[2], fb[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = *reinterpret_cast<const f16x8*>(&As[cur][wm + 32 * i + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const f16x8*>(&Bs[cur][wn + 32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
   }
   const float s = p.a_ts[0] * p.b_ts[0];
 #pragma unroll
@@ -239,7 +193,6 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int64_t col = n0 + wn + 32 * j + (lane & 31);
-        // written once, never read here: a non-temporal store
         if (row < p.M && col < p.N) __builtin_nontemporal_store(acc[i][j][r] * s, &p.c[row * p.ldc + col]);
       }
 }
