@@ -746,6 +746,7 @@ __device__ __forceinline__ float col_pass(const QuantParams& p, const TileInfo& 
   const int64_t rows_here = T.P - T.m0;
   const int nch = rows_here >= kTileRows ? 8 : (int)(rows_here / 16);  // chunks that exist
   uint8_t* cc = p.col_codes + band_c0 * (Rp / 2) + (T.coff + T.m0) / 2;
+  const bool run_aligned = ((T.coff + T.m0) & 127) == 0;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
     const int q = threadIdx.x + j * kThreads;
@@ -754,7 +755,15 @@ __device__ __forceinline__ float col_pass(const QuantParams& p, const TileInfo& 
     if (col < ncols && chq < nch) {
       const uint2 cw = cst.codes[chq][sc];
       const u32x2 cv2 = {cw.x, cw.y};
-      __builtin_nontemporal_store(cv2, reinterpret_cast<u32x2*>(cc + (int64_t)col * (Rp / 2) + 8 * chq));
+      u32x2* dst = reinterpret_cast<u32x2*>(cc + (int64_t)col * (Rp / 2) + 8 * chq);
+      // A tile's 64-byte run fills a line half when it starts on one (dense
+      // tensors): written once, non-temporal.  Segment starts fall on any 16
+      // rows, and then the run shares its lines with the neighbouring tiles'
+      // runs: cached stores let the L2 merge them before they are written.
+      if (run_aligned)
+        __builtin_nontemporal_store(cv2, dst);
+      else
+        *dst = cv2;
     }
   }
   uint8_t* cs = p.col_scales + band_c0 * (Rp / B) + (T.coff + T.m0) / B;
