@@ -2,8 +2,9 @@
 workspace entry point it varies (ufp4_quantize_rowcol), through the C ABI:
 bit-identical codes, scales and tensor scales on calls in a row, each later
 call on a smaller tensor than the one before (the shared scratch array keeps
-the earlier call's contents), under each schedule; and the size limit,
-rejected before anything is enqueued."""
+the earlier call's contents), under each schedule; the call captured in a
+HIP graph and replayed; and the size limit, rejected before anything is
+enqueued."""
 import ctypes
 import sys
 
@@ -68,6 +69,45 @@ def test_noalloc_matches_workspace_call(env, sched):
         oc = orc.config(INT4, RTNE, MX32, 1, 4, 4)
         c, s, t = orc.quantize(xb, oc, 0)
         assert np.array_equal(rb.codes.cpu().numpy(), c) and np.array_equal(rb.scales.cpu().numpy(), s)
+    finally:
+        F.ufp4_set_schedule(AUTO, 0)
+
+
+@pytest.mark.parametrize("sched", [AUTO, TWO_PASS])
+def test_noalloc_in_a_captured_graph(env, sched):
+    # the callers this entry point is for capture it in a HIP graph: the
+    # call is captured once and replayed three times, with eager calls on
+    # another tensor in between (which leave their own contents in the
+    # scratch array); every replay matches the workspace call's output
+    torch, F, _ = env
+    F.ufp4_set_schedule(sched, 0)
+    try:
+        R, C = 1024, 1536
+        xb = synth.output_grad(R, C, seed=7)
+        x = torch.from_numpy(xb.view(np.int16)).cuda()
+        fc = F.config(E1M2, SR, NV16, 1, 7, 7)
+        ra, ca = F.alloc_layout(R, C, NV16), F.alloc_layout(C, R, NV16)
+        F.ufp4_quantize_rowcol(x, fc, ra, ca, F.Workspace(R, C))
+        rb, cb = F.alloc_layout(R, C, NV16), F.alloc_layout(C, R, NV16)
+        other = torch.from_numpy(synth.activation(512, 512, seed=8).view(np.int16)).cuda()
+        ro, co = F.alloc_layout(512, 512, NV16), F.alloc_layout(512, 512, NV16)
+        F.ufp4_quantize_rowcol_noalloc(x, fc, rb, cb)  # first use on the device happens eagerly
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            F.ufp4_quantize_rowcol_noalloc(x, fc, rb, cb)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            say(f"[noalloc graph] sched={sched} replay {rep}")
+            rb.codes.fill_(0x5A)
+            cb.codes.fill_(0x5A)
+            F.ufp4_quantize_rowcol_noalloc(other, fc, ro, co)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            same(torch, ra, rb, f"row, replay {rep}")
+            same(torch, ca, cb, f"col, replay {rep}")
     finally:
         F.ufp4_set_schedule(AUTO, 0)
 
