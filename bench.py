@@ -703,7 +703,12 @@ def main():
                      "kernel": ("ufp4_single_kernel<E1M2, RTNE, RHT> (single pass, the whole call)" if single
                                 else "ufp4_quant_kernel<E1M2, RTNE, NV16, RHT>"),
                      "bytes_per_launch": nbytes,
-                     "kernel_ms_mean": round(float(k_quant.mean()), 6)},
+                     "kernel_ms_mean": round(float(k_quant.mean()), 6),
+                     # the measured rate of the same loads and output bytes
+                     # with no arithmetic (ufp4_roof_rowcol), and the
+                     # kernel's fraction of it
+                     "attainable_gbps": round(nbytes / (ms_roof * 1e-3) / 1e9, 1),
+                     "frac_of_attainable": round(quant_gbps / (nbytes / (ms_roof * 1e-3) / 1e9), 4)},
         "extra": {"elements_per_s": round(ROWS * COLS / (ms * 1e-3), 1),
                   "call_frac_of_peak": round(gbps / PEAK_GBPS, 4),
                   "call_hbm_bytes_counted": traffic_call,
