@@ -1096,7 +1096,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 // The memory traffic of a dense NV16 row+col call with no arithmetic: the
 // same tile walk (XCD-aware order) and 16-byte non-temporal loads of the
 // lane sub-tiles as the quantization kernels, and the call's output bytes
-// (both layouts' codes and block scales) as coalesced non-temporal stores.
+// (both layouts' codes and block scales) as coalesced stores (cached: the
+// output's 8- to 128-byte pieces of lines are merged in the L2, which
+// measured faster than non-temporal stores for this pattern).
 // The stored value is the loaded words folded to one word and compared with
 // a constant, so every load is live; it is zero unless a lane's 64 words
 // xor to that constant.  Full tiles only (rows a multiple of 128, columns of
@@ -1117,18 +1119,17 @@ __global__ __launch_bounds__(kThreads) void ufp4_roof_kernel(QuantParams p) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {  // row-wise codes: 128 rows x 128 bytes
     const int i = t + kThreads * j, r = i >> 3, k = i & 7;
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p.row_codes + (T.m0 + r) * (p.cols / 2) + c0 / 2 + 16 * k));
+    *reinterpret_cast<u32x4*>(p.row_codes + (T.m0 + r) * (p.cols / 2) + c0 / 2 + 16 * k) = o;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {  // column-wise codes: 256 columns x 64 bytes
     const int i = t + kThreads * j, c = i >> 2, k = i & 3;
-    __builtin_nontemporal_store(
-        o, reinterpret_cast<u32x4*>(p.col_codes + (c0 + c) * (p.padded_rows / 2) + T.m0 / 2 + 16 * k));
+    *reinterpret_cast<u32x4*>(p.col_codes + (c0 + c) * (p.padded_rows / 2) + T.m0 / 2 + 16 * k) = o;
   }
   if (t < kTileRows)  // row-wise scales: 16 bytes per row
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p.row_scales + (T.m0 + t) * (p.cols / 16) + c0 / 16));
+    *reinterpret_cast<u32x4*>(p.row_scales + (T.m0 + t) * (p.cols / 16) + c0 / 16) = o;
   const u32x2 o2 = {z, z};  // column-wise scales: 8 bytes per column
-  __builtin_nontemporal_store(o2, reinterpret_cast<u32x2*>(p.col_scales + (c0 + t) * (p.padded_rows / 16) + T.m0 / 16));
+  *reinterpret_cast<u32x2*>(p.col_scales + (c0 + t) * (p.padded_rows / 16) + T.m0 / 16) = o2;
 }
 
 // ------------------------------------------------------- single pass

@@ -441,7 +441,8 @@ int ufp4_time_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
  * rows x cols bf16 tensor x (ld = cols) with the quantization kernels' tile
  * walk and 16-byte loads, and writes every byte of both layouts' codes and
  * block scales (row_out: rows x cols, col_out: cols x rows, as
- * ufp4_quantize_rowcol) with coalesced 16-byte stores; tensor scales are not
+ * ufp4_quantize_rowcol) with coalesced 16-byte stores (column-wise scales:
+ * 8-byte); tensor scales are not
  * touched.  The bytes written are zero unless a lane's 64 input words xor to
  * one fixed constant.  rows must be a multiple of 128 and cols of 256
  * (UFP4_ERR_SHAPE); x, the codes and the row-wise scales 16-byte and the
