@@ -216,11 +216,14 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_kernel(GemmParams p) {
 // E8M0 byte of block l / 32 of the slice for that row.  The 32 x 32 result
 // is laid out as for the other 32 x 32 MFMAs.
 //
-// Tiles are 256 x 256 per workgroup of 8 waves (each 64 x 128 as 2 x 4 MFMA
-// tiles), K steps of 128 (two slices), double-buffered in LDS: each thread
-// stages one half (64 K values: two MX blocks) of one A row and one B row
-// per step, requested one step ahead.
+// Tiles are 256 x 256 per workgroup of 16 waves (each 64 x 64 as 2 x 2 MFMA
+// tiles: 64 accumulator registers, so four waves fit per SIMD), K steps of
+// 256 (FP4) or 128 (FP8) values, double-buffered in LDS: each thread stages
+// one half of one A row (threads 0..511) or one B row (512..1023) per step,
+// requested one step ahead.
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kMxThreads = 1024;  // 16 waves: 4 x 4 wave tiles of 64 x 64
 
 template <int GRID>
 struct MxFmt {
@@ -251,7 +254,7 @@ __device__ __forceinline__ void expand8_e4m3(uint32_t word, uint32_t out[2]) {
 }
 
 template <int GRID>
-__global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p) {
+__global__ __launch_bounds__(kMxThreads) void ufp4_gemm_mx_kernel(GemmParams p) {
   using Fm = MxFmt<GRID>;
   __shared__ __attribute__((aligned(16))) uint8_t As[2][kGemmM][Fm::kPitch];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGemmN][Fm::kPitch];
@@ -261,22 +264,27 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
   constexpr int NB = Fm::kBlocks;   // MX blocks per thread and operand per step
   const int64_t m0 = (int64_t)blockIdx.y * kGemmM, n0 = (int64_t)blockIdx.x * kGemmN;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
-  const int lr = t >> 1, h = t & 1;  // staged row, half of the K step
+  const int wm = (wave >> 2) * 64, wn = (wave & 3) * 64;
+  const int op = t >> 9;                   // operand this thread stages: 0 A, 1 B
+  const int lr = (t & 511) >> 1, h = t & 1;  // staged row, half of the K step
   const int64_t am = m0 + lr, bn = n0 + lr;
-  const bool a_ok = am < p.M, b_ok = bn < p.N;
+  const bool a_ok = am < p.M && op == 0, b_ok = bn < p.N && op == 1;
   const int64_t kc = p.K / 2, ks = p.K / 32;
   const uint8_t* ac = p.a_codes + (a_ok ? am : 0) * kc + 16 * NB * h;
   const uint8_t* as = p.a_scales + (a_ok ? am : 0) * ks + NB * h;
   const uint8_t* bc = p.b_codes + (b_ok ? bn : 0) * kc + 16 * NB * h;
   const uint8_t* bs = p.b_scales + (b_ok ? bn : 0) * ks + NB * h;
   const int64_t nsteps = (p.K + Fm::kK - 1) / Fm::kK;
-  // codes of the thread's NB blocks (16 bytes each) and their scale bytes;
-  // a block past K (or a row past M / N) is zero with scale 2^0
+  // codes of the thread's NB blocks (16 bytes each) of its operand row and
+  // their scale bytes; a block past K (or a row past M / N) is zero with
+  // scale 2^0
   struct Stage {
-    g32x4 a[NB], b[NB];
-    uint8_t sa[NB], sb[NB];
+    g32x4 c[NB];
+    uint8_t sc[NB];
   };
+  const uint8_t* src = op == 0 ? ac : bc;
+  const uint8_t* ss = op == 0 ? as : bs;
+  const bool ok = op == 0 ? a_ok : b_ok;
   auto fetch = [&](int64_t st) {
     Stage f;
 #pragma unroll
@@ -285,10 +293,8 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
       const bool in = st * Fm::kK + 32 * NB * h + 32 * q + 32 <= p.K;
       const int64_t off = in ? st * (Fm::kK / 2) + 16 * q : 0;
       const int64_t so = in ? st * (Fm::kK / 32) + q : 0;
-      f.a[q] = (in && a_ok) ? *reinterpret_cast<const g32x4*>(ac + off) : g32x4{0u, 0u, 0u, 0u};
-      f.b[q] = (in && b_ok) ? *reinterpret_cast<const g32x4*>(bc + off) : g32x4{0u, 0u, 0u, 0u};
-      f.sa[q] = (in && a_ok) ? as[so] : (uint8_t)127;
-      f.sb[q] = (in && b_ok) ? bs[so] : (uint8_t)127;
+      f.c[q] = (in && ok) ? *reinterpret_cast<const g32x4*>(src + off) : g32x4{0u, 0u, 0u, 0u};
+      f.sc[q] = (in && ok) ? ss[so] : (uint8_t)127;
     }
     return f;
   };
@@ -310,19 +316,15 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
   };
   auto put = [&](const Stage& f, int buf) {
     constexpr int half_bytes = Fm::kRowBytes / 2;
-    put_row(f.a, &As[buf][lr][half_bytes * h]);
-    put_row(f.b, &Bs[buf][lr][half_bytes * h]);
+    put_row(f.c, op == 0 ? &As[buf][lr][half_bytes * h] : &Bs[buf][lr][half_bytes * h]);
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      Ss[buf][0][lr][NB * h + q] = f.sa[q];
-      Ss[buf][1][lr][NB * h + q] = f.sb[q];
-    }
+    for (int q = 0; q < NB; ++q) Ss[buf][op][lr][NB * h + q] = f.sc[q];
   };
-  f32x16 acc[2][4];
+  f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   if (nsteps > 0) put(fetch(0), 0);
   Stage nxt = fetch(nsteps > 1 ? 1 : 0);
   __syncthreads();
@@ -339,20 +341,20 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
     // the step's scale bytes of the lane's rows, shifted so that the byte of
     // slice kk's block for this lane's half (block 2 kk + g) sits at byte
     // 2 (kk % 2) of word kk / 2, which the MFMA's scale byte select takes
-    uint32_t swa[2][SW], swb[4][SW];
+    uint32_t swa[2][SW], swb[2][SW];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int q = 0; q < SW; ++q)
         swa[i][q] = reinterpret_cast<const uint32_t*>(&Ss[cur][0][wm + 32 * i + r32][0])[q] >> (8 * g);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < SW; ++q)
         swb[j][q] = reinterpret_cast<const uint32_t*>(&Ss[cur][1][wn + 32 * j + r32][0])[q] >> (8 * g);
 #pragma unroll
     for (int kk = 0; kk < Fm::kSlices; ++kk) {
-      i32x8 fa[2], fb[4];
+      i32x8 fa[2], fb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = wm + 32 * i + r32;
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const int row = wn + 32 * j + r32;
         if (Fm::kFp4) {
           const g32x4 v = *reinterpret_cast<const g32x4*>(&Bs[cur][row][32 * kk + 16 * g]);
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           if (kk & 1)  // (the byte select must be a constant: kk is unrolled)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], Fm::kFmt, Fm::kFmt,
                                                                         2, (int)swa[i][kk >> 1], 2, (int)swb[j][kk >> 1]);
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(kGemmThreads) void ufp4_gemm_mx_kernel(GemmParams p
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -407,10 +409,10 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const dim3 grid((unsigned)((p.N + kGemmN - 1) / kGemmN), (unsigned)((p.M + kGemmM - 1) / kGemmM));
   if (p.mx) {
     switch (p.grid) {
-      case kGridE1M2: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridE1M2>, grid, dim3(kGemmThreads), 0, s, p); break;
-      case kGridINT4: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridINT4>, grid, dim3(kGemmThreads), 0, s, p); break;
-      case kGridE2M1: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridE2M1>, grid, dim3(kGemmThreads), 0, s, p); break;
-      case kGridE2M1C: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridE2M1C>, grid, dim3(kGemmThreads), 0, s, p); break;
+      case kGridE1M2: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridE1M2>, grid, dim3(kMxThreads), 0, s, p); break;
+      case kGridINT4: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridINT4>, grid, dim3(kMxThreads), 0, s, p); break;
+      case kGridE2M1: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridE2M1>, grid, dim3(kMxThreads), 0, s, p); break;
+      case kGridE2M1C: hipLaunchKernelGGL(ufp4_gemm_mx_kernel<kGridE2M1C>, grid, dim3(kMxThreads), 0, s, p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
