@@ -41,9 +41,12 @@ __device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t m) {
   return r;
 }
 
-__device__ __forceinline__ Ctr4 philox10(Ctr4 c, uint32_t k0, uint32_t k1) {
+// N rounds of Philox4x32 from counter c under key (k0, k1) (the key of the
+// first of these rounds).
+template <int N>
+__device__ __forceinline__ Ctr4 philox_rounds(Ctr4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
+  for (int r = 0; r < N; ++r) {
     const uint64_t p0 = mul_wide(c.x, 0xD2511F53u), p1 = mul_wide(c.z, 0xCD9E8D57u);
     const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
     const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
@@ -56,10 +59,19 @@ __device__ __forceinline__ Ctr4 philox10(Ctr4 c, uint32_t k0, uint32_t k1) {
   return c;
 }
 
+__device__ __forceinline__ Ctr4 philox10(Ctr4 c, uint32_t k0, uint32_t k1) { return philox_rounds<10>(c, k0, k1); }
+
 // Four consecutive stochastic-rounding words for flat output indices
-// 4q .. 4q+3 of output stream `stream`.
+// 4q .. 4q+3 of output stream `stream`: Philox4x32-10 of the counter
+// (lo(q), hi(q), stream, 0).  The first round is written out: its product of
+// the stream word is a constant at every call site (a plain product, which
+// the compiler folds), and the zero fourth word drops out of its xor.
 __device__ __forceinline__ Ctr4 sr_words4(uint64_t q, uint32_t stream, uint32_t k0, uint32_t k1) {
-  return philox10(Ctr4{(uint32_t)q, (uint32_t)(q >> 32), stream, 0u}, k0, k1);
+  const uint64_t p0 = mul_wide((uint32_t)q, 0xD2511F53u);
+  const uint64_t p1 = (uint64_t)stream * 0xCD9E8D57u;
+  const Ctr4 c{(uint32_t)__builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), (uint32_t)(q >> 32), k0, 0x96),
+               (uint32_t)p1, (uint32_t)(p0 >> 32) ^ k1, (uint32_t)p0};
+  return philox_rounds<9>(c, k0 + 0x9E3779B9u, k1 + 0xBB67AE85u);
 }
 
 // ---------------------------------------------------------------- FWHT
@@ -225,24 +237,20 @@ __device__ __forceinline__ uint32_t round_rtne(float y) {
 // top give the top with frac 0).  A signaling NaN is quieted first (free
 // when y is the result of arithmetic), since the median treats it otherwise.
 // Returns the magnitude index.
+// sr_steps takes s = y / step (any sign) instead of y, and s must not be a
+// signaling NaN (the result of arithmetic never is).
 template <int GRID>
-__device__ __forceinline__ uint32_t sr_uniform_index(float y, uint32_t r) {
-  constexpr float kInvStep = GRID == kGridINT4 ? 1.0f : 2.0f;
-  const float t = __builtin_amdgcn_fmed3f(__builtin_canonicalizef(fabsf(y) * kInvStep), 0.0f,
-                                          (float)grid_top<GRID>());
+__device__ __forceinline__ uint32_t sr_steps(float s, uint32_t r) {
+  const float t = __builtin_amdgcn_fmed3f(fabsf(s), 0.0f, (float)grid_top<GRID>());
   const uint32_t lo = (uint32_t)t;
   const uint32_t thr = (uint32_t)ceilf(__builtin_amdgcn_fractf(t) * 4294967296.0f);
   return lo + (r < thr ? 1u : 0u);
 }
 
-// The same as a two's-complement integer carrying the sign of y (0 for a
-// zero index, whatever the sign), for the packing paths whose nibbles are
-// converted to sign-magnitude eight at a time.
 template <int GRID>
-__device__ __forceinline__ uint32_t sr_uniform_tc(float y, uint32_t r) {
-  const uint32_t k = sr_uniform_index<GRID>(y, r);
-  const uint32_t s = (uint32_t)((int32_t)__float_as_uint(y) >> 31);
-  return (k ^ s) - s;
+__device__ __forceinline__ uint32_t sr_uniform_index(float y, uint32_t r) {
+  constexpr float kInvStep = GRID == kGridINT4 ? 1.0f : 2.0f;
+  return sr_steps<GRID>(__builtin_canonicalizef(y * kInvStep), r);
 }
 
 template <int GRID>

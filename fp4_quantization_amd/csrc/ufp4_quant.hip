@@ -319,6 +319,73 @@ __device__ __forceinline__ uint32_t push_nibble(uint32_t m, uint32_t acc) {
   return __builtin_amdgcn_alignbit(m, acc, 4u);
 }
 
+// Shift the magnitude index k (< 8) in at the top of acc as a sign-magnitude
+// nibble with the sign of s: bit 31 of s is the new nibble's bit 3.
+__device__ __forceinline__ uint32_t push_signmag(uint32_t k, float s, uint32_t acc) {
+  // (a & ~m) | (b & m) with m the sign bit: one three-input op (table 0xD8)
+  return (uint32_t)__builtin_amdgcn_bitop3_b32(__builtin_amdgcn_alignbit(k, acc, 4u), __float_as_uint(s),
+                                               0x80000000u, 0xD8);
+}
+
+// Eight sign-magnitude nibbles: a zero magnitude loses its sign bit (bit 3
+// of m + 7 is set iff the magnitude m <= 7 is nonzero; no carry leaves the
+// nibble).
+__device__ __forceinline__ uint32_t clear_neg_zero8(uint32_t P) {
+  const uint32_t nz = (P & 0x77777777u) + 0x77777777u;
+  return (uint32_t)__builtin_amdgcn_bitop3_b32(P, nz, 0x77777777u, 0xE0);  // P & (nz | 0x77777777)
+}
+
+// Stochastic rounding of eight values, given in grid steps, onto a uniform
+// grid, packed as eight nibbles (value j in nibble j): sign-magnitude codes,
+// or two's-complement ones for INT4.
+template <int GRID>
+__device__ __forceinline__ uint32_t sr_pack8(const float* s, const uint32_t* rw) {
+  uint32_t acc = 0u;
+  if (GRID == kGridINT4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t k = sr_steps<GRID>(s[j], rw[j]);
+      const uint32_t sg = (uint32_t)((int32_t)__float_as_uint(s[j]) >> 31);
+      acc = push_nibble((k ^ sg) - sg, acc);
+    }
+    return acc;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = push_signmag(sr_steps<GRID>(s[j], rw[j]), s[j], acc);
+  return clear_neg_zero8(acc);
+}
+
+// The values of NB blocks in grid steps for stochastic rounding, in place:
+// s = ((v fin) inv_b) kMul, where fin is the lane's multiplier (1/4 with the
+// folded sign, or 1) and kMul = 1 / (grid step).  When M = fin inv_b kMul
+// has |M| >= 2^-15 (or inv_b is 0) in every block of the wavefront, s is the
+// one product v M, which gives the same index and sign: M is then exact;
+// v fin is exact (a nonzero v is a multiple of 2^-133, a sum of bf16
+// values); at normal magnitudes the power-of-two factors commute with
+// rounding; and a product in the subnormal range, in either form, is a
+// nonzero value below 2^-124 (|v fin inv_b| >= 2^-149), so index 0 with
+// threshold 1.
+template <int GRID, int NB, int N>
+__device__ __forceinline__ void sr_steps_inplace(float (&v)[NB][N], const float inv[NB], float fin) {
+  constexpr float kMul = GRID == kGridINT4 ? 1.0f : 2.0f;
+  bool fold = true;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) fold &= (inv[b] == 0.0f) | (fabsf(fin * inv[b] * kMul) >= 0x1p-15f);
+  if (__all(fold)) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float m = fin * inv[b] * kMul;
+#pragma unroll
+      for (int j = 0; j < N; ++j) v[b][j] *= m;
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < N; ++j) v[b][j] = ((v[b][j] * fin) * inv[b]) * kMul;
+  }
+}
+
 // t clamped to [-top, top], NaN to a zero: the median of |t|, 0 and top (a
 // NaN operand makes v_med3_f32 return the smallest of the three, 0 here; t
 // is the result of arithmetic, so never a signaling NaN), with t's sign.
@@ -589,6 +656,7 @@ __device__ __forceinline__ float row_pass(const QuantParams& p, const TileInfo& 
         packed[r] = GRID == kGridINT4 ? acc : tc_to_signmag8(acc);
       }
     } else {
+      if (G::kFastSR) sr_steps_inplace<GRID>(v, inv, fin);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const int i = NR * g4 + r;
@@ -597,10 +665,7 @@ __device__ __forceinline__ float row_pass(const QuantParams& p, const TileInfo& 
           const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
           const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
           const uint32_t rw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-          uint32_t acc = 0u;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc = push_nibble(sr_uniform_tc<GRID>((v[r][j] * fin) * inv[r], rw[j]), acc);
-          packed[r] = GRID == kGridINT4 ? acc : tc_to_signmag8(acc);
+          packed[r] = sr_pack8<GRID>(v[r], rw);
         } else if (SR) {
           const uint64_t base = (uint64_t)(T.seg_row0 + L.m_h0 + i) * (uint64_t)C + (uint64_t)L.c0;
           const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
@@ -689,22 +754,19 @@ __device__ __forceinline__ float col_pass(const QuantParams& p, const TileInfo& 
         hi[r] = GRID == kGridINT4 ? a1 : tc_to_signmag8(a1);
       }
     } else {
+      if (G::kFastSR) sr_steps_inplace<GRID>(v, inv, fin);
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         if (G::kFastSR) {
           const int64_t cglob = L.c0 + 2 * g2 + r;
           const uint64_t base = (uint64_t)cglob * (uint64_t)p.padded_rows + (uint64_t)(T.coff + L.m_h0);
-          uint32_t acc[2] = {0u, 0u};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const Ctr4 rr = sr_words4((base >> 2) + q, 1u, p.sr_k0, p.sr_k1);
-            const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[q >> 1] = push_nibble(sr_uniform_tc<GRID>((v[r][4 * q + j] * fin) * inv[r], rw[j]), acc[q >> 1]);
+          for (int h = 0; h < 2; ++h) {
+            const Ctr4 r0 = sr_words4((base >> 2) + 2 * h, 1u, p.sr_k0, p.sr_k1);
+            const Ctr4 r1 = sr_words4((base >> 2) + 2 * h + 1, 1u, p.sr_k0, p.sr_k1);
+            const uint32_t rw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+            (h ? hi[r] : lo[r]) = sr_pack8<GRID>(&v[r][8 * h], rw);
           }
-          lo[r] = GRID == kGridINT4 ? acc[0] : tc_to_signmag8(acc[0]);
-          hi[r] = GRID == kGridINT4 ? acc[1] : tc_to_signmag8(acc[1]);
         } else if (SR) {
           const int64_t cglob = L.c0 + 2 * g2 + r;
           const uint64_t base = (uint64_t)cglob * (uint64_t)p.padded_rows + (uint64_t)(T.coff + L.m_h0);
