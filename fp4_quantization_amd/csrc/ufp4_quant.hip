@@ -393,6 +393,26 @@ __device__ __forceinline__ float clamp_top(float t, float top) {
   return __builtin_copysignf(__builtin_amdgcn_fmed3f(fabsf(t), 0.0f, top), t);
 }
 
+// Eight values rounded to E2M1 (nearest, ties to even, saturating at +-6)
+// by the hardware conversion, two per instruction into byte k of the word
+// (value j in nibble j), as sign-magnitude codes; a zero result loses the
+// sign the conversion keeps.  Each value is first clamped to [-6, 6] with
+// NaN mapped to a zero (clamp_top), the code the oracle gives a NaN; the
+// conversion saturates at +-6 itself, so the clamp changes nothing else.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* y) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = clamp_top(y[2 * k], 6.0f), b = clamp_top(y[2 * k + 1], 6.0f);
+    // the byte select must be a constant: k is unrolled
+    if (k == 0) w = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 0);
+    if (k == 1) w = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 1);
+    if (k == 2) w = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 2);
+    if (k == 3) w = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 3);
+  }
+  return clear_neg_zero8(w);
+}
+
 // fl(t + 1.5*2^23) has t rounded to the nearest integer (ties to even) in
 // its low mantissa bits, as a two's-complement value, for |t| < 2^22.
 constexpr float kMagic = 12582912.0f;
@@ -655,6 +675,14 @@ __device__ __forceinline__ float row_pass(const QuantParams& p, const TileInfo& 
         }
         packed[r] = GRID == kGridINT4 ? acc : tc_to_signmag8(acc);
       }
+    } else if (GRID == kGridE2M1 && !SR && ok) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = (v[r][j] * fin) * inv[r];
+        packed[r] = e2m1_pack8(y);
+      }
     } else {
       if (G::kFastSR) sr_steps_inplace<GRID>(v, inv, fin);
 #pragma unroll
@@ -752,6 +780,15 @@ __device__ __forceinline__ float col_pass(const QuantParams& p, const TileInfo& 
         }
         lo[r] = GRID == kGridINT4 ? a0 : tc_to_signmag8(a0);
         hi[r] = GRID == kGridINT4 ? a1 : tc_to_signmag8(a1);
+      }
+    } else if (GRID == kGridE2M1 && !SR && ok) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        float y[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y[j] = (v[r][j] * fin) * inv[r];
+        lo[r] = e2m1_pack8(y);
+        hi[r] = e2m1_pack8(y + 8);
       }
     } else {
       if (G::kFastSR) sr_steps_inplace<GRID>(v, inv, fin);
