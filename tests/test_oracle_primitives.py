@@ -172,6 +172,24 @@ def test_rht_rounding_within_bound(orc):
         assert np.all(np.abs(v - exact) <= bound + 1e-45)
 
 
+def test_rht_outputs_are_multiples_of_the_bf16_quantum(orc):
+    # Every input is a multiple of 2^-133 (the smallest bf16 step), so every
+    # fp32 sum and difference of the butterfly is one too (rounding never
+    # goes below the operands' common step), and the transform's outputs,
+    # after the final 1/4, are multiples of 2^-135.  The quantizer's
+    # single-product scaling relies on this: the 1/4 is exact and a nonzero
+    # value never falls below 2^-135.  Inputs mix bf16 subnormals with values
+    # up to 2^100, random signs.
+    rng = np.random.default_rng(13)
+    s = orc.rht_signs(3)
+    for _ in range(400):
+        mag = rng.integers(0, 0x7180, 16)  # bf16 magnitude patterns: 0, subnormals .. 2^100
+        mag[rng.random(16) < 0.3] = rng.integers(1, 0x80, 1)[0]  # some subnormals in most blocks
+        x = synth.bf16_to_f32((mag | (rng.integers(0, 2, 16) << 15)).astype(np.uint16))
+        q = orc.rht16(x, s).astype(np.float64) * 2.0 ** 135
+        assert np.all(np.isfinite(q)) and np.all(q == np.round(q))
+
+
 # -------------------------------------------------------------------- E4M3
 def _e4m3_values():
     vals = []
