@@ -192,6 +192,34 @@ def test_edge_values(env):
                     assert_layout_equal(col, orc.quantize(xb, oc, COL), f"{name} col")
 
 
+def test_e2m1_ties_through_the_packed_conversion(env, schedule):
+    # Without the transform, a tensor maximum of 6 * 448 makes the NV16
+    # tensor scale 1 and a 6.0 at the start of every 16-long row and column
+    # block makes those blocks' scales 1 (the MX32 scale of a 6.0 block is
+    # 2^0 as well), so the scaled values are the inputs themselves: exact
+    # E2M1 ties (0.25, 0.75, ..., 5) and grid values, rounded to nearest
+    # even by the packed hardware conversion.  Both schedules, both layouts.
+    torch, F, orc = env
+    R, C = 64, 96
+    rng = np.random.default_rng(41)
+    vals = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 3.0, 4.0, 6.0, 0.0], np.float32)
+    x = rng.choice(vals, (R, C)) * rng.choice(np.array([-1.0, 1.0], np.float32), (R, C))
+    x[:, ::16] = 6.0
+    x[::16, :] = -6.0
+    x[0, 0] = 6.0 * 448.0
+    xb = synth.f32_to_bf16(x.astype(np.float32))
+    assert np.array_equal(synth.bf16_to_f32(xb), x.astype(np.float32))
+    for sched in (TWO_PASS, SINGLE_PASS):
+        schedule(sched)
+        for grid in (E2M1, E1M2):
+            for scaling in (NV16, MX32):
+                say(f"[e2m1 ties] sched={sched} grid={grid} scl={scaling}")
+                fc, oc = cfgs(F, orc, grid, RTNE, scaling, 0, rht_seed=1, sr_seed=1)
+                row, col = gpu_rowcol(env, xb, fc)
+                assert_layout_equal(row, orc.quantize(xb, oc, ROW), "ties row")
+                assert_layout_equal(col, orc.quantize(xb, oc, COL), "ties col")
+
+
 def nonfinite_input(R, C, seed, inf=True):
     """Normal values with about 1% NaN and (if inf) 1% each of +-inf, bf16."""
     rng = np.random.default_rng(seed)
