@@ -253,6 +253,21 @@ __device__ __forceinline__ uint32_t sr_uniform_index(float y, uint32_t r) {
   return sr_steps<GRID>(__builtin_canonicalizef(y * kInvStep), r);
 }
 
+// E2M1, the same rule: the magnitudes 0, 1/2, 1, 3/2 | 2, 3 | 4, 6 are
+// uniform within [0, 2) (step 1/2), [2, 4) (step 1) and [4, 6] (step 2), so
+// a = |y| clamped to [0, 6] (NaN to 0) gives s = 2a, a - 2 or a/2 - 2 (each
+// exact) and the index is the range's first index + floor(s), plus one iff
+// r < ceil(fract(s) * 2^32), with fract(s) the bucket fraction (a - lo) /
+// (hi - lo).  y must not be a signaling NaN.
+__device__ __forceinline__ uint32_t sr_e2m1_index(float y, uint32_t r) {
+  const float a = __builtin_amdgcn_fmed3f(fabsf(y), 0.0f, 6.0f);
+  const bool r0 = a < 2.0f, r1 = a < 4.0f;
+  const float s = r0 ? a + a : (r1 ? a - 2.0f : fmaf(a, 0.5f, -2.0f));
+  const uint32_t base = r0 ? 0u : (r1 ? 4u : 6u);
+  const uint32_t thr = (uint32_t)ceilf(__builtin_amdgcn_fractf(s) * 4294967296.0f);
+  return base + (uint32_t)s + (r < thr ? 1u : 0u);
+}
+
 template <int GRID>
 __device__ __forceinline__ uint32_t round_sr(float y, uint32_t r) {
   uint32_t k;

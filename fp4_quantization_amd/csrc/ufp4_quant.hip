@@ -335,9 +335,9 @@ __device__ __forceinline__ uint32_t clear_neg_zero8(uint32_t P) {
   return (uint32_t)__builtin_amdgcn_bitop3_b32(P, nz, 0x77777777u, 0xE0);  // P & (nz | 0x77777777)
 }
 
-// Stochastic rounding of eight values, given in grid steps, onto a uniform
-// grid, packed as eight nibbles (value j in nibble j): sign-magnitude codes,
-// or two's-complement ones for INT4.
+// Stochastic rounding of eight values, given in grid steps for the uniform
+// grids and as they are for E2M1, packed as eight nibbles (value j in nibble
+// j): sign-magnitude codes, or two's-complement ones for INT4.
 template <int GRID>
 __device__ __forceinline__ uint32_t sr_pack8(const float* s, const uint32_t* rw) {
   uint32_t acc = 0u;
@@ -351,13 +351,17 @@ __device__ __forceinline__ uint32_t sr_pack8(const float* s, const uint32_t* rw)
     return acc;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc = push_signmag(sr_steps<GRID>(s[j], rw[j]), s[j], acc);
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t k = GRID == kGridE2M1 ? sr_e2m1_index(s[j], rw[j]) : sr_steps<GRID>(s[j], rw[j]);
+    acc = push_signmag(k, s[j], acc);
+  }
   return clear_neg_zero8(acc);
 }
 
 // The values of NB blocks in grid steps for stochastic rounding, in place:
 // s = ((v fin) inv_b) kMul, where fin is the lane's multiplier (1/4 with the
-// folded sign, or 1) and kMul = 1 / (grid step).  When M = fin inv_b kMul
+// folded sign, or 1) and kMul = 1 / (grid step) (1 for E2M1, whose steps
+// differ: its values stay as they are).  When M = fin inv_b kMul
 // has |M| >= 2^-15 (or inv_b is 0) in every block of the wavefront, s is the
 // one product v M, which gives the same index and sign: M is then exact;
 // v fin is exact (a nonzero v is a multiple of 2^-133, a sum of bf16
@@ -367,7 +371,7 @@ __device__ __forceinline__ uint32_t sr_pack8(const float* s, const uint32_t* rw)
 // threshold 1.
 template <int GRID, int NB, int N>
 __device__ __forceinline__ void sr_steps_inplace(float (&v)[NB][N], const float inv[NB], float fin) {
-  constexpr float kMul = GRID == kGridINT4 ? 1.0f : 2.0f;
+  constexpr float kMul = GRID == kGridINT4 || GRID == kGridE2M1 ? 1.0f : 2.0f;
   bool fold = true;
 #pragma unroll
   for (int b = 0; b < NB; ++b) fold &= (inv[b] == 0.0f) | (fabsf(fin * inv[b] * kMul) >= 0x1p-15f);
@@ -613,7 +617,6 @@ using ColStage = ColStageT<8>;
 template <int GRID, bool SR>
 struct GridTraits {
   static constexpr bool kFast = !SR && GRID != kGridE2M1;      // uniform grids
-  static constexpr bool kFastSR = SR && GRID != kGridE2M1;     // uniform grids, stochastic
   static constexpr float kMul = GRID == kGridINT4 ? 1.0f : 2.0f;  // grid step -> integer
   static constexpr float kTop = (float)grid_top<GRID>();          // clamp, in grid steps
 };
@@ -684,28 +687,16 @@ __device__ __forceinline__ float row_pass(const QuantParams& p, const TileInfo& 
         packed[r] = e2m1_pack8(y);
       }
     } else {
-      if (G::kFastSR) sr_steps_inplace<GRID>(v, inv, fin);
+      if (SR) sr_steps_inplace<GRID>(v, inv, fin);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const int i = NR * g4 + r;
-        if (G::kFastSR) {
+        if (SR) {
           const uint64_t base = (uint64_t)(T.seg_row0 + L.m_h0 + i) * (uint64_t)C + (uint64_t)L.c0;
           const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
           const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
           const uint32_t rw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
           packed[r] = sr_pack8<GRID>(v[r], rw);
-        } else if (SR) {
-          const uint64_t base = (uint64_t)(T.seg_row0 + L.m_h0 + i) * (uint64_t)C + (uint64_t)L.c0;
-          const Ctr4 r0 = sr_words4(base >> 2, 0u, p.sr_k0, p.sr_k1);
-          const Ctr4 r1 = sr_words4((base >> 2) + 1, 0u, p.sr_k0, p.sr_k1);
-          packed[r] = quantize_code<GRID, SR>((v[r][0] * fin) * inv[r], r0.x) |
-                      (quantize_code<GRID, SR>((v[r][1] * fin) * inv[r], r0.y) << 4) |
-                      (quantize_code<GRID, SR>((v[r][2] * fin) * inv[r], r0.z) << 8) |
-                      (quantize_code<GRID, SR>((v[r][3] * fin) * inv[r], r0.w) << 12) |
-                      (quantize_code<GRID, SR>((v[r][4] * fin) * inv[r], r1.x) << 16) |
-                      (quantize_code<GRID, SR>((v[r][5] * fin) * inv[r], r1.y) << 20) |
-                      (quantize_code<GRID, SR>((v[r][6] * fin) * inv[r], r1.z) << 24) |
-                      (quantize_code<GRID, SR>((v[r][7] * fin) * inv[r], r1.w) << 28);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
@@ -791,10 +782,10 @@ __device__ __forceinline__ float col_pass(const QuantParams& p, const TileInfo& 
         hi[r] = e2m1_pack8(y + 8);
       }
     } else {
-      if (G::kFastSR) sr_steps_inplace<GRID>(v, inv, fin);
+      if (SR) sr_steps_inplace<GRID>(v, inv, fin);
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        if (G::kFastSR) {
+        if (SR) {
           const int64_t cglob = L.c0 + 2 * g2 + r;
           const uint64_t base = (uint64_t)cglob * (uint64_t)p.padded_rows + (uint64_t)(T.coff + L.m_h0);
 #pragma unroll
@@ -804,20 +795,6 @@ __device__ __forceinline__ float col_pass(const QuantParams& p, const TileInfo& 
             const uint32_t rw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
             (h ? hi[r] : lo[r]) = sr_pack8<GRID>(&v[r][8 * h], rw);
           }
-        } else if (SR) {
-          const int64_t cglob = L.c0 + 2 * g2 + r;
-          const uint64_t base = (uint64_t)cglob * (uint64_t)p.padded_rows + (uint64_t)(T.coff + L.m_h0);
-          uint32_t word[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const Ctr4 rr = sr_words4((base >> 2) + q, 1u, p.sr_k0, p.sr_k1);
-            word[q] = quantize_code<GRID, SR>((v[r][4 * q + 0] * fin) * inv[r], rr.x) |
-                      (quantize_code<GRID, SR>((v[r][4 * q + 1] * fin) * inv[r], rr.y) << 4) |
-                      (quantize_code<GRID, SR>((v[r][4 * q + 2] * fin) * inv[r], rr.z) << 8) |
-                      (quantize_code<GRID, SR>((v[r][4 * q + 3] * fin) * inv[r], rr.w) << 12);
-          }
-          lo[r] = word[0] | (word[1] << 16);
-          hi[r] = word[2] | (word[3] << 16);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
