@@ -234,11 +234,10 @@ __device__ __forceinline__ uint32_t round_rtne(float y) {
 // exact, lo = floor(t), frac = t - floor(t).  t is clamped to [0, top] by
 // one median (a NaN operand makes v_med3_f32 return the smallest of the
 // three, 0 here, so NaN gives index 0; +inf and everything at or above the
-// top give the top with frac 0).  A signaling NaN is quieted first (free
-// when y is the result of arithmetic), since the median treats it otherwise.
-// Returns the magnitude index.
-// sr_steps takes s = y / step (any sign) instead of y, and s must not be a
-// signaling NaN (the result of arithmetic never is).
+// top give the top with frac 0).  Both return the magnitude index.
+//
+// sr_steps takes s = y / step (any sign), which must not be a signaling NaN
+// (the median treats one otherwise; the result of arithmetic never is one).
 template <int GRID>
 __device__ __forceinline__ uint32_t sr_steps(float s, uint32_t r) {
   const float t = __builtin_amdgcn_fmed3f(fabsf(s), 0.0f, (float)grid_top<GRID>());
@@ -247,6 +246,8 @@ __device__ __forceinline__ uint32_t sr_steps(float s, uint32_t r) {
   return lo + (r < thr ? 1u : 0u);
 }
 
+// sr_uniform_index takes y itself and quiets a signaling NaN first (free
+// when y is the result of arithmetic).
 template <int GRID>
 __device__ __forceinline__ uint32_t sr_uniform_index(float y, uint32_t r) {
   constexpr float kInvStep = GRID == kGridINT4 ? 1.0f : 2.0f;
