@@ -85,6 +85,24 @@ def test_activation_rowcol_8192x2048(env):
     assert torch.equal(a1, a2) and bool((a1 >= 0).all())
 
 
+@pytest.mark.parametrize("grid,rounding,scaling", [(E2M1, RTNE, NV16), (E2M1, SR, NV16), (E2M1, RTNE, MX32),
+                                                    (E2M1, SR, MX32), (INT4, RTNE, NV16), (E1M2, RTNE, MX32)])
+def test_activation_variants_rowcol_8192x2048(env, grid, rounding, scaling):
+    # the grid, rounding and scaling variants of the headline call, as the
+    # benchmark's variant legs launch them (one row+column call)
+    torch, F, orc = env
+    say(f"[full] activation 8192x2048 RHT grid={grid} rnd={rounding} scl={scaling} row+col")
+    xb = synth.activation(8192, 2048, seed=1)
+    fc = F.config(grid, rounding, scaling, 1, 1, 1)
+    oc = orc.config(grid, rounding, scaling, 1, 1, 1)
+    x = to_dev(torch, xb)
+    row, col = F.alloc_layout(8192, 2048, scaling), F.alloc_layout(2048, 8192, scaling)
+    F.ufp4_quantize_rowcol(x, fc, row, col, F.Workspace(8192, 2048))
+    torch.cuda.synchronize()
+    check_layout("row", row, orc.quantize(xb, oc, ROW))
+    check_layout("col", col, orc.quantize(xb, oc, COL))
+
+
 def test_weight_grid_sweep_2048x8192(env):
     torch, F, orc = env
     xb = synth.weight(2048, 8192, seed=2)
